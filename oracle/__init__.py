@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for the MRU prefix-scan path (test infrastructure only).
+
+Imported by tests, the smoke check and the benchmark's CPU-baseline leg; never
+by the product path.  See ``mru_oracle`` for the definitions and citations.
+"""
+from .mru_oracle import (  # noqa: F401
+    FP32_DOMAIN_LIMIT,
+    build_ref,
+    bwd_ref,
+    flatten_ref,
+    loss_ref,
+    rel_fro_err,
+    representable,
+    scan_ref,
+)

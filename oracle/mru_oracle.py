@@ -1,0 +1,165 @@
+"""Plain fp64 CPU oracle for the MRU prefix-scan path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports, calls or links it, and it
+shares no code with that path: it is written from the definitions on the MRU
+pages, slowly and obviously, in numpy float64.
+
+Sources (page titles as printed; section names are the pages' own):
+
+* "MRU Update: An independent developer's alternative to Attention is now
+  running successfully" (openai-hub.net, English version of the openai-hub.com
+  article), section "What MRU Actually Does": each token's vector becomes an
+  input state matrix, the matrices are multiplied one after another along the
+  sequence to give the output state matrix, and that matrix is turned back
+  into a vector.  Each step multiplies the current state matrix by the new
+  input matrix (state on the left, input on the right), and associativity of
+  the matrix product is what allows a parallel scan.
+* "Improving Matrix Recurrent Units as an Attention Alternative"
+  (setupai.cc), Key Points: the input state matrix is built by LDU factor
+  filling with a determinant-correcting scalar.
+
+Readings taken where the pages are silent:
+
+* The n*n entries of a token vector, viewed row-major as X, fill the strictly
+  lower part of a unit lower-triangular L, the strictly upper part of a unit
+  upper-triangular U, and log of a positive diagonal D (D_ii = exp X_ii).
+* The determinant-correcting scalar is c = |det(L D U)|^(-1/n), so that
+  det(M) = 1 for M = c L D U.
+* The scan is inclusive with P_0 = I and right multiplication,
+  P_t = P_{t-1} M_t.
+* Flattening is the row-major reshape of P_t to an n*n vector, per head.
+* The backward pass is the vector-Jacobian product of L = sum_t <R_t, P_t>_F
+  with respect to every M_t (the pages describe training through the product
+  but give no formula; the chain rule fixes it).
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+against closed forms, library routines, brute force, finite differences and
+an independent autograd library; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "build_ref", "scan_ref", "bwd_ref", "flatten_ref", "loss_ref",
+    "rel_fro_err", "representable", "FP32_DOMAIN_LIMIT",
+]
+
+# Largest |entry| of an exact P_t that the parity comparison grades; fp32
+# overflows at 2^128, and 2^125 leaves room for association-order differences.
+FP32_DOMAIN_LIMIT = 2.0 ** 125
+
+
+def _as_matrices(x: np.ndarray, n: int) -> np.ndarray:
+    x = np.asarray(x)
+    if x.shape[-1] != n * n:
+        raise ValueError(f"last axis must be n*n = {n * n}, got {x.shape[-1]}")
+    return x.astype(np.float64).reshape(*x.shape[:-1], n, n)
+
+
+def build_ref(x: np.ndarray, n: int) -> np.ndarray:
+    """Input state matrices from raw token vectors (LDU fill + det correction).
+
+    ``x``: ``[..., n*n]`` (any real dtype, promoted to float64).
+    Returns ``M``: ``[..., n, n]`` float64 with ``M = c * L @ D @ U``.
+
+    Follows "Improving Matrix Recurrent Units as an Attention Alternative",
+    Key Points (LDU factor filling, determinant-correcting scalar), with the
+    row-major fill described in the module docstring.  The determinant is
+    taken with the library routine, not with any closed form, so that the
+    det(M) = 1 pin checks the construction rather than restating it.
+    """
+    X = _as_matrices(x, n)
+    eye = np.eye(n)
+    L = np.tril(X, -1) + eye
+    U = np.triu(X, 1) + eye
+    D = np.diagonal(X, axis1=-2, axis2=-1)
+    LDU = (L * np.exp(D)[..., None, :]) @ U          # L @ diag(exp(X_ii)) @ U
+    det = np.linalg.det(LDU)
+    c = np.abs(det) ** (-1.0 / n)
+    return c[..., None, None] * LDU
+
+
+def scan_ref(M: np.ndarray) -> np.ndarray:
+    """All prefix products P_t = M_1 M_2 ... M_t, serial, left to right.
+
+    ``M``: ``[..., T, n, n]``; returns float64 of the same shape.
+
+    Follows "MRU Update: ..." (openai-hub.net), section "What MRU Actually
+    Does": cumulative multiplication along the sequence, each step being the
+    current state matrix times the new input matrix.  No blocking and no
+    reassociation: one matrix product per token, in token order.
+    """
+    M = np.asarray(M, dtype=np.float64)
+    T, n = M.shape[-3], M.shape[-1]
+    batch = M.shape[:-3]
+    P = np.empty(M.shape, dtype=np.float64)
+    state = np.broadcast_to(np.eye(n), batch + (n, n)).copy()    # P_0 = I
+    for t in range(T):
+        state = state @ M[..., t, :, :]
+        P[..., t, :, :] = state
+    return P
+
+
+def flatten_ref(P: np.ndarray) -> np.ndarray:
+    """Output state matrix back to a vector: the row-major reshape ``[..., n*n]``
+    ("What MRU Actually Does", dimension reduction step)."""
+    P = np.asarray(P)
+    return P.reshape(*P.shape[:-2], P.shape[-1] * P.shape[-2])
+
+
+def loss_ref(P: np.ndarray, R: np.ndarray) -> float:
+    """L = sum over (b, h, t) of the Frobenius inner product <R_t, P_t>."""
+    return float(np.sum(np.asarray(P, np.float64) * np.asarray(R, np.float64)))
+
+
+def bwd_ref(M: np.ndarray, R: np.ndarray) -> np.ndarray:
+    """Gradient dL/dM_t of L = sum_t <R_t, P_t> with P_t = P_{t-1} M_t.
+
+    ``M``, ``R``: ``[..., T, n, n]``; returns float64 ``dM`` of the same shape.
+
+    Reverse-mode chain rule, serial from the last token to the first: with
+    Q_t the total adjoint of P_t (R_t plus what flows back from P_{t+1} =
+    P_t M_{t+1}), Q_T = R_T, Q_t = R_t + Q_{t+1} M_{t+1}^T, and since P_t
+    depends on M_t only through P_{t-1} M_t, dL/dM_t = P_{t-1}^T Q_t with
+    P_0 = I.  The prefixes come from this module's own fp64 forward.
+    """
+    M = np.asarray(M, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    if M.shape != R.shape:
+        raise ValueError("M and R must have the same shape")
+    T, n = M.shape[-3], M.shape[-1]
+    batch = M.shape[:-3]
+    P = scan_ref(M)
+    eye = np.broadcast_to(np.eye(n), batch + (n, n))
+    dM = np.empty(M.shape, dtype=np.float64)
+    Q = np.zeros(batch + (n, n))
+    for t in range(T - 1, -1, -1):
+        if t + 1 < T:
+            Q = R[..., t, :, :] + Q @ np.swapaxes(M[..., t + 1, :, :], -1, -2)
+        else:
+            Q = R[..., t, :, :].copy()
+        P_prev = P[..., t - 1, :, :] if t > 0 else eye
+        dM[..., t, :, :] = np.swapaxes(P_prev, -1, -2) @ Q
+    return dM
+
+
+def rel_fro_err(test: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-matrix relative Frobenius error ||test - ref||_F / ||ref||_F in float64.
+
+    Reduces the last two axes.  A zero reference norm gives inf (or nan for
+    0/0), which every tolerance check treats as a failure.
+    """
+    test = np.asarray(test, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.sqrt(np.sum((test - ref) ** 2, axis=(-2, -1)))
+    den = np.sqrt(np.sum(ref ** 2, axis=(-2, -1)))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return num / den
+
+
+def representable(P_ref: np.ndarray, limit: float = FP32_DOMAIN_LIMIT) -> np.ndarray:
+    """Mask of matrices whose exact entries all stay within ``limit`` (fp32 parity domain)."""
+    return np.max(np.abs(np.asarray(P_ref)), axis=(-2, -1)) <= limit
