@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the MRU hot path on one MI355X (gfx950).
+
+One step = the whole path over one batch of seeded synthetic input already
+resident in HBM: LDU build (x -> M), forward prefix scan (M -> P) and backward
+scan (M, P, dL/dP -> dL/dM).  Prints ONE JSON line:
+
+  value         tokens/s of the whole step (a token = one position of one batch
+                row, all heads included), timed with HIP events over exactly
+                --steps steps after --warmup untimed ones
+  roofline      the dominant kernel's algorithmic bytes per launch / its average
+                launch time (HIP events on the launch stream), against the
+                8 TB/s HBM peak; `traffic` is the measured HBM bytes per launch
+                from profiles/hbm_traffic.json when that record was taken on the
+                current kernel sources, else null
+  kernels       the same figures for every kernel of the step
+  n16, n32      forward-scan throughput on the n=16 and n=32 workloads
+  cpu_baseline  the fp64 oracle (oracle/) timed on the host on a bounded sample
+                of the same workload
+
+Only one GPU is used: --gpus N with N > 1 exits with an explanation.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+FP64_PEAK_TFLOPS = 78.6
+METRIC = "MRU prefix-scan tokens/s + achieved HBM GB/s (frac of peak), n=8 and n=16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "matrix_prefix_product_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(kind: str, S: int, T: int, n: int) -> int:
+    per = {"build": 8, "fwd": 8, "bwd": 16}[kind]  # bytes per matrix entry per token-head
+    return per * n * n * S * T
+
+
+def algorithmic_flops(kind: str, S: int, T: int, n: int) -> int:
+    # serial-product flops: forward n^3 mult-adds per token-head, backward 2 n^3
+    return {"build": n ** 3 // 3 * 2, "fwd": 2 * n ** 3, "bwd": 4 * n ** 3}[kind] * S * T
+
+
+def load_traffic(workload: str, kernel: str):
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    if not k:
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def time_cpu_baseline(w, budget_s: float):
+    """The oracle's build + forward + backward on a bounded sample, 1 thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import build_ref, bwd_ref, scan_ref
+    from workloads import gen_R, gen_x
+
+    def run(b_rows, h_rows, T):
+        x = gen_x(w.B, w.H, T, w.n, w.sigma_off, w.sigma_diag, w.seed, b_idx=b_rows, h_idx=h_rows)
+        R = gen_R(w.B, w.H, T, w.n, w.seed, b_idx=b_rows, h_idx=h_rows)
+        t0 = time.perf_counter()
+        M = build_ref(x, w.n)
+        scan_ref(M)
+        bwd_ref(M, R)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=1):
+        T = min(w.T, 4096)
+        b_rows, h_rows = [0], [0]
+        dt = run(b_rows, h_rows, T)
+        # grow the sample (more sequences) toward the time budget
+        seqs = max(1, min(w.B * w.H, int(budget_s / max(dt, 1e-4) * 0.8)))
+        nb = max(1, min(w.B, seqs // w.H)) if seqs >= w.H else 1
+        nh = w.H if seqs >= w.H else seqs
+        b_rows, h_rows = list(range(nb)), list(range(nh))
+        dt = run(b_rows, h_rows, T)
+    head_tokens = nb * nh * T
+    tokens = head_tokens / w.H
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{nb} batch rows x {nh} heads x {T} tokens of {w.name} (fp64 numpy build_ref + "
+                  f"scan_ref + bwd_ref, {dt:.1f} s, BLAS limited to 1 thread)",
+        "head_tokens_per_s": head_tokens / dt,
+    }
+
+
+def kernel_record(kind, avg_ms, S, T, n, workload):
+    b = algorithmic_bytes(kind, S, T, n)
+    gbs = b / (avg_ms * 1e-3) / 1e9
+    return {
+        "avg_us": round(avg_ms * 1e3, 2),
+        "algorithmic_bytes": b,
+        "achieved_GBs": round(gbs, 1),
+        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "traffic": load_traffic(workload, kind),
+    }
+
+
+def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
+    """Forward scan alone on a large workload; inputs generated on the GPU from a seed."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    scale = torch.full((n, n), so, device="cuda")
+    scale.fill_diagonal_(sd)
+    x = (torch.randn((B, H, T, n, n), generator=g, device="cuda") * scale).reshape(B, H, T, n * n)
+    M = mpp.build_inputs(x.contiguous(), n)
+    del x
+    P = torch.empty_like(M)
+    ws = torch.empty(max(mpp.workspace_bytes(B, H, T, n), 256), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        mpp.scan_fwd(M, out=P, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        mpp.scan_fwd(M, out=P, workspace=ws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    med = times[len(times) // 2]
+    S = B * H
+    b = algorithmic_bytes("fwd", S, T, n)
+    K, nch, Z, _ = mpp.scan_plan(B, H, T, n)
+    # implementation MFMA/VALU work: one n^3 product per token, two for tokens in
+    # chunks that need a carry (all but the first chunk of a sequence)
+    prod = S * T * (2.0 if nch > 1 else 1.0) - (S * K if nch > 1 else 0)
+    impl_flops = prod * 2 * n ** 3
+    peak = FP64_PEAK_TFLOPS if n == 16 else FP32_PEAK_TFLOPS
+    del M, P, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{name}: B={B},H={H},T={T},n={n}, forward scan only",
+        "median_us": round(med * 1e3, 1),
+        "tokens_per_s": B * T / (med * 1e-3),
+        "achieved_GBs": round(b / (med * 1e-3) / 1e9, 1),
+        "frac_hbm": round(b / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "plan": {"chunk": K, "chunks_per_seq": nch, "super": Z},
+        "matrix_tflops": round(impl_flops / (med * 1e-3) / 1e12, 2),
+        "matrix_peak_tflops": peak,
+        "matrix_util": round(impl_flops / (med * 1e-3) / 1e12 / peak, 4),
+        "data": "synthetic, seeded on the GPU (torch.Generator), same scales as the workload",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2l")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the n=16 / n=32 forward figures")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the MRU scan shards over independent "
+              "sequences with no communication, so this build measures one GPU's share; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import matrix_prefix_product_amd as mpp
+    from workloads import WORKLOADS, gen_R, gen_x
+
+    w = WORKLOADS[args.workload]
+    B, H, T, n = w.B, w.H, w.T, w.n
+    S = B * H
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = torch.from_numpy(gen_x(B, H, T, n, w.sigma_off, w.sigma_diag, w.seed)).to(dev)
+    R = torch.from_numpy(gen_R(B, H, T, n, w.seed)).to(dev)
+    M = torch.empty((B, H, T, n, n), device=dev)
+    P = torch.empty_like(M)
+    dM = torch.empty_like(M)
+    ws_f = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_FWD), 256), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_BWD), 256), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mpp.build_inputs(x, n, out=M)
+        if ev is not None:
+            ev[1].record()
+        mpp.scan_fwd(M, out=P, workspace=ws_f)
+        if ev is not None:
+            ev[2].record()
+        mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per = {k: [] for k in ("build", "fwd", "bwd")}
+    for e in evs:
+        per["build"].append(e[0].elapsed_time(e[1]))
+        per["fwd"].append(e[1].elapsed_time(e[2]))
+        per["bwd"].append(e[2].elapsed_time(e[3]))
+    kernels = {k: kernel_record(k, float(np.mean(v)), S, T, n, w.name) for k, v in per.items()}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    dk = kernels[dom]
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64" if n == 16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: char-LM-shaped MRU layer, B={B}, H={H} heads, T={T}, n={n} "
+                        "(d_model 512 as 8 heads of 8x8); one step = LDU build + forward scan + "
+                        "backward scan",
+            "B": B, "H": H, "T": T, "n": n,
+            "fwd_plan": dict(zip(("chunk", "chunks_per_seq", "super", "ws_bytes"),
+                                 mpp.scan_plan(B, H, T, n, mpp.DIR_FWD))),
+            "bwd_plan": dict(zip(("chunk", "chunks_per_seq", "super", "ws_bytes"),
+                                 mpp.scan_plan(B, H, T, n, mpp.DIR_BWD))),
+        },
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": dk["achieved_GBs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dk["frac_hbm"],
+            "traffic": dk["traffic"],
+            "algorithmic_bytes_per_launch": dk["algorithmic_bytes"],
+        },
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 4),
+    }
+    del x, R, M, P, dM, ws_f, ws_b
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        c3, c4 = WORKLOADS["c3"], WORKLOADS["c4"]
+        out["n16"] = fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3)
+        out["n32"] = fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = time_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

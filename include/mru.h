@@ -1,0 +1,162 @@
+/*
+ * mru.h -- C ABI of the MRU prefix-scan library (libmru.so, gfx950 / MI355X).
+ *
+ * Matrix Recurrent Units turn every token's vector into an n-by-n "input state
+ * matrix", multiply those matrices one after another along the sequence (the
+ * running product is the "output state matrix"), and turn each running product
+ * back into a vector.  Matrix multiplication is associative, which is what lets
+ * the running product be computed as a parallel scan instead of a serial loop.
+ *   Source: "MRU Update: An independent developer's alternative to Attention is
+ *   now running successfully", section "What MRU Actually Does".
+ * The input state matrix is built by LDU factor filling with a
+ * determinant-correcting scalar.
+ *   Source: "Improving Matrix Recurrent Units as an Attention Alternative",
+ *   Key Points.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Shapes      B (batch), H (heads), T (tokens) >= 0; n in {4, 8, 16, 32}.
+ *             S = B*H independent sequences.
+ * Layout      dense, contiguous, row-major fp32 device arrays [B][H][T][n][n];
+ *             a raw token vector x is the same bytes viewed as [B][H][T][n*n]
+ *             and an output vector is P viewed as [B][H][T][n*n] (row-major
+ *             flatten, heads kept separate).  Every pointer must be 16-byte
+ *             aligned.
+ * Ownership   the caller allocates and frees every buffer, including the
+ *             workspace (size from mru_scan_workspace_bytes).  The library
+ *             allocates no device memory and keeps no mutable global state;
+ *             calls are re-entrant.  Two calls that run at the same time need
+ *             distinct workspaces.
+ * Streams     all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *             default stream) and the call returns without synchronising.
+ *             Device-side faults surface at the caller's next synchronisation.
+ * Errors      every argument is validated on the host before anything is
+ *             enqueued; a non-OK status means nothing was launched.  An empty
+ *             problem (B*H*T == 0) returns MRU_OK without launching.  The
+ *             library never prints, aborts or exits.
+ * Arithmetic  inputs and outputs are IEEE fp32.  The running product is kept
+ *             in fp32 for n = 4, 8, 32 and in fp64 for n = 16.  Values beyond
+ *             the fp32 range become +-inf / nan exactly as IEEE arithmetic
+ *             gives them: nothing is clamped or renormalised.
+ */
+#ifndef MRU_H
+#define MRU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MRU_ABI_VERSION 1
+
+typedef enum mru_status {
+    MRU_OK = 0,
+    MRU_ERR_NULL = 1,       /* a required pointer is NULL                         */
+    MRU_ERR_SHAPE = 2,      /* B, H or T negative, n not in {4,8,16,32}, overflow */
+    MRU_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                   */
+    MRU_ERR_ALIAS = 4,      /* an output overlaps an input or another output      */
+    MRU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required            */
+    MRU_ERR_CHUNK = 6,      /* chunk < 0                                          */
+    MRU_ERR_HIP = 7         /* the HIP runtime reported an error at launch        */
+} mru_status;
+
+/* Scan direction for the workspace / chunk queries. */
+#define MRU_DIR_FWD 0
+#define MRU_DIR_BWD 1
+
+/* MRU_ABI_VERSION of the loaded library. */
+int32_t mru_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* mru_status_string(int32_t status);
+
+/*
+ * Input state matrices from raw token vectors (LDU fill + determinant
+ * correction).  Source: "Improving Matrix Recurrent Units as an Attention
+ * Alternative", Key Points.
+ *
+ * x  [B][H][T][n*n] fp32, read.  Viewed row-major as X (n-by-n): the strictly
+ *    lower part fills a unit lower-triangular L, the strictly upper part a unit
+ *    upper-triangular U, and the diagonal is log D (D_ii = exp X_ii).
+ * M  [B][H][T][n][n] fp32, written: M = c L D U with c = |det(L D U)|^(-1/n),
+ *    so det(M) = 1.  Computed as L diag(exp(X_ii - mean_j X_jj)) U, which is
+ *    the same matrix because det L = det U = 1.
+ * x and M must not overlap.
+ */
+mru_status mru_build_inputs(const float* x, float* M, int64_t B, int64_t H, int64_t T,
+                            int32_t n, void* stream);
+
+/*
+ * Chunk length (tokens per scan chunk) that chunk = 0 resolves to for this
+ * shape and direction; a pure function of its arguments.  Returns 0 for an
+ * invalid shape.
+ */
+int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction);
+
+/*
+ * The scan plan for this shape, direction and chunk (0 = automatic), as
+ * out4[0] = chunk length K, out4[1] = chunks per sequence (the token chunks,
+ * rounded up with empty chunks to a multiple of the chains a wave runs),
+ * out4[2] = chunks per super (the unit of the carry chain), out4[3] = workspace
+ * bytes.  A plan with one chunk per sequence needs no workspace.  Returns
+ * MRU_OK, MRU_ERR_NULL (out4 NULL), MRU_ERR_SHAPE or MRU_ERR_CHUNK.
+ */
+int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
+                      int32_t chunk, int64_t* out4);
+
+/*
+ * Workspace bytes that mru_scan_fwd (direction MRU_DIR_FWD) or mru_scan_bwd
+ * (MRU_DIR_BWD) needs for this shape and chunk (0 = automatic).  May be 0, in
+ * which case ws may be NULL.  Returns 0 for an invalid shape as well; callers
+ * validate through the scan call itself.
+ */
+size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
+                                int32_t chunk);
+
+/*
+ * Forward scan: every running product of the input state matrices.
+ * Source: "MRU Update: ...", section "What MRU Actually Does" (cumulative
+ * multiplication, state matrix times new input matrix; associativity allows a
+ * parallel scan).
+ *
+ * M      [B][H][T][n][n] fp32, read.
+ * P      [B][H][T][n][n] fp32, written: P_t = M_1 M_2 ... M_t for every sequence,
+ *        inclusive, with P_0 = I (right multiplication, P_t = P_{t-1} M_t).
+ *        P viewed as [B][H][T][n*n] is the flattened output vector.
+ * chunk  tokens per scan chunk; 0 = automatic (mru_scan_chunk).  Any positive
+ *        value gives the same result up to rounding order.
+ * ws     device workspace of at least mru_scan_workspace_bytes(..., MRU_DIR_FWD,
+ *        chunk) bytes (16-byte aligned), or NULL when that size is 0.  Its
+ *        contents on entry are ignored; on exit it holds scratch state only.
+ * M and P must not overlap; P must not overlap ws.
+ */
+mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
+                        int32_t chunk, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward scan: vector-Jacobian product of the forward scan.
+ * Given dP = dL/dP_t for every t, writes dM = dL/dM_t, where (chain rule on
+ * P_t = P_{t-1} M_t) with Q_T = dP_T and Q_t = dP_t + Q_{t+1} M_{t+1}^T,
+ * dM_t = P_{t-1}^T Q_t and P_0 = I.  The pages describe training through the
+ * product ("MRU Update: ...", section "The Two Fatal Issues From a Year Ago":
+ * unbounded states make gradients blow up) but give no formula; this is the
+ * exact gradient.
+ *
+ * M   [B][H][T][n][n] fp32, read (the forward inputs).
+ * P   [B][H][T][n][n] fp32, read (the forward outputs of mru_scan_fwd on M).
+ * dP  [B][H][T][n][n] fp32, read.
+ * dM  [B][H][T][n][n] fp32, written.
+ * chunk, ws, ws_bytes as for mru_scan_fwd with direction MRU_DIR_BWD.
+ * dM must not overlap M, P, dP or ws.
+ */
+mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
+                        int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MRU_H */

@@ -1,0 +1,239 @@
+"""MRU prefix scan on MI355X (gfx950): Python binding of libmru.so.
+
+Matrix Recurrent Units build an n-by-n input state matrix per token (LDU fill
+with a determinant-correcting scalar), multiply the matrices along the
+sequence, and flatten each running product back to a vector.  Every step of
+that runs in the HIP kernels of libmru.so; this module only checks tensor
+arguments, allocates outputs and workspaces through torch, and passes device
+pointers and the current stream to the C ABI declared in include/mru.h.
+
+Functions (tensors are contiguous fp32 on a ROCm device):
+    build_inputs(x, n)        x [B,H,T,n*n] -> M [B,H,T,n,n]
+    scan_fwd(M, chunk=0)      M -> P, P_t = M_1 ... M_t
+    scan_bwd(M, P, dP)        -> dM, gradient of sum_t <dP_t, P_t>
+    flatten(P)                P [B,H,T,n,n] -> [B,H,T,n*n] (a view)
+    mru_scan(M)               scan_fwd with autograd (backward = scan_bwd)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "build_inputs", "scan_fwd", "scan_bwd", "flatten", "mru_scan", "MRUScan",
+    "scan_plan", "scan_chunk", "workspace_bytes", "library_path", "load_library",
+    "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N",
+]
+
+DIR_FWD = 0
+DIR_BWD = 1
+SUPPORTED_N = (4, 8, 16, 32)
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmru.so")
+_LIB = None
+
+_STATUS = {
+    0: "MRU_OK", 1: "MRU_ERR_NULL", 2: "MRU_ERR_SHAPE", 3: "MRU_ERR_ALIGN", 4: "MRU_ERR_ALIAS",
+    5: "MRU_ERR_WORKSPACE", 6: "MRU_ERR_CHUNK", 7: "MRU_ERR_HIP",
+}
+
+
+class MRUError(RuntimeError):
+    """A non-OK status from libmru.so."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({_status_string(status)})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmru.so (built in-tree).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m matrix_prefix_product_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.mru_abi_version.restype = i32
+    lib.mru_abi_version.argtypes = []
+    lib.mru_status_string.restype = ctypes.c_char_p
+    lib.mru_status_string.argtypes = [i32]
+    lib.mru_build_inputs.restype = i32
+    lib.mru_build_inputs.argtypes = [vp, vp, i64, i64, i64, i32, vp]
+    lib.mru_scan_chunk.restype = i32
+    lib.mru_scan_chunk.argtypes = [i64, i64, i64, i32, i32]
+    lib.mru_scan_plan.restype = i32
+    lib.mru_scan_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
+    lib.mru_scan_workspace_bytes.restype = sz
+    lib.mru_scan_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.mru_scan_fwd.restype = i32
+    lib.mru_scan_fwd.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_bwd.restype = i32
+    lib.mru_scan_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    _LIB = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().mru_status_string(int(status)).decode()
+    except Exception:  # library missing: fall back to the code name
+        return _STATUS.get(status, str(status))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MRUError(status, what)
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _require(t: torch.Tensor, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm GPU device, got {t.device}")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mshape(M: torch.Tensor, name: str = "M"):
+    _require(M, name, 5)
+    B, H, T, n, n2 = M.shape
+    if n != n2 or n not in SUPPORTED_N:
+        raise ValueError(f"{name} must be [B,H,T,n,n] with n in {SUPPORTED_N}, got {tuple(M.shape)}")
+    return B, H, T, n
+
+
+def scan_chunk(B: int, H: int, T: int, n: int, direction: int = DIR_FWD) -> int:
+    """Chunk length the automatic plan uses for this shape."""
+    return int(load_library().mru_scan_chunk(B, H, T, n, direction))
+
+
+def scan_plan(B: int, H: int, T: int, n: int, direction: int = DIR_FWD, chunk: int = 0):
+    """(K, chunks per sequence, chunks per super, workspace bytes) of a scan."""
+    out = (ctypes.c_int64 * 4)()
+    _check(load_library().mru_scan_plan(B, H, T, n, direction, chunk, out), "mru_scan_plan")
+    return tuple(int(v) for v in out)
+
+
+def workspace_bytes(B: int, H: int, T: int, n: int, direction: int = DIR_FWD, chunk: int = 0) -> int:
+    return int(load_library().mru_scan_workspace_bytes(B, H, T, n, direction, chunk))
+
+
+def _workspace(shape, n, direction, chunk, device, workspace):
+    need = workspace_bytes(*shape, n, direction, chunk)
+    if workspace is not None:
+        if workspace.device != device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+        return workspace, workspace.numel()
+    if need == 0:
+        return None, 0
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
+def build_inputs(x: torch.Tensor, n: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[B,H,T,n*n] raw token vectors -> [B,H,T,n,n] input state matrices."""
+    _require(x, "x", 4)
+    B, H, T, nn = x.shape
+    if n not in SUPPORTED_N or nn != n * n:
+        raise ValueError(f"x must be [B,H,T,n*n] with n in {SUPPORTED_N}, got {tuple(x.shape)}, n={n}")
+    if out is None:
+        M = torch.empty((B, H, T, n, n), dtype=torch.float32, device=x.device)
+    else:
+        _require(out, "out", 5)
+        if tuple(out.shape) != (B, H, T, n, n) or out.device != x.device:
+            raise ValueError("out must be [B,H,T,n,n] on x's device")
+        M = out
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.mru_build_inputs(_ptr(x), _ptr(M), B, H, T, n, _stream_handle(x.device))
+    _check(st, "mru_build_inputs")
+    return M
+
+
+def scan_fwd(M: torch.Tensor, chunk: int = 0, out: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """All prefix products P_t = M_1 ... M_t (P_0 = I), [B,H,T,n,n]."""
+    B, H, T, n = _mshape(M)
+    if out is None:
+        out = torch.empty_like(M)
+    else:
+        _require(out, "out", 5)
+        if out.shape != M.shape or out.device != M.device:
+            raise ValueError("out must match M")
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_FWD, chunk, M.device, workspace)
+    lib = load_library()
+    with torch.cuda.device(M.device):
+        st = lib.mru_scan_fwd(_ptr(M), _ptr(out), B, H, T, n, chunk, _ptr(ws), ws_bytes,
+                              _stream_handle(M.device))
+    _check(st, "mru_scan_fwd")
+    return out
+
+
+def scan_bwd(M: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient dM of sum_t <dP_t, P_t> where P = scan_fwd(M), [B,H,T,n,n]."""
+    B, H, T, n = _mshape(M)
+    for name, t in (("P", P), ("dP", dP)):
+        _require(t, name, 5)
+        if t.shape != M.shape or t.device != M.device:
+            raise ValueError(f"{name} must have M's shape and device")
+    if out is None:
+        out = torch.empty_like(M)
+    else:
+        _require(out, "out", 5)
+        if out.shape != M.shape or out.device != M.device:
+            raise ValueError("out must match M")
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_BWD, chunk, M.device, workspace)
+    lib = load_library()
+    with torch.cuda.device(M.device):
+        st = lib.mru_scan_bwd(_ptr(M), _ptr(P), _ptr(dP), _ptr(out), B, H, T, n, chunk, _ptr(ws),
+                              ws_bytes, _stream_handle(M.device))
+    _check(st, "mru_scan_bwd")
+    return out
+
+
+def flatten(P: torch.Tensor) -> torch.Tensor:
+    """Row-major flatten of each output state matrix: [B,H,T,n,n] -> [B,H,T,n*n] view."""
+    return P.view(*P.shape[:-2], P.shape[-2] * P.shape[-1])
+
+
+class MRUScan(torch.autograd.Function):
+    """P = scan_fwd(M) with the exact VJP from scan_bwd."""
+
+    @staticmethod
+    def forward(ctx, M: torch.Tensor, chunk: int = 0):
+        M = M.contiguous()
+        P = scan_fwd(M, chunk)
+        ctx.save_for_backward(M, P)
+        ctx.chunk = chunk
+        return P
+
+    @staticmethod
+    def backward(ctx, dP: torch.Tensor):
+        M, P = ctx.saved_tensors
+        return scan_bwd(M, P, dP.contiguous(), ctx.chunk), None
+
+
+def mru_scan(M: torch.Tensor, chunk: int = 0) -> torch.Tensor:
+    return MRUScan.apply(M, chunk)

@@ -1,0 +1,251 @@
+// C ABI of libmru.so: argument validation, scan planning, launches.
+// The contract of every entry point is documented in include/mru.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "mru.h"
+#include "mru_device.h"
+#include "mru_kernels.h"
+
+namespace mru {
+
+__global__ void ws_reset_kernel(uint32_t* words, int64_t nwords) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nwords;
+         i += int64_t(gridDim.x) * blockDim.x)
+        words[i] = 0u;
+}
+
+namespace {
+
+constexpr int64_t kMaxT = int64_t(1) << 30;
+
+bool valid_n(int32_t n) { return n == 4 || n == 8 || n == 16 || n == 32; }
+
+int acc_bytes(int n) { return n == 16 ? 8 : 4; }
+
+int chains_per_wave(int n, int dir) { return n <= 8 ? valu_chains_per_wave(n, dir) : 1; }
+
+// Shape check shared by every entry point; fills S and the element count.
+bool shape_ok(int64_t B, int64_t H, int64_t T, int32_t n, int64_t* S, int64_t* elems) {
+    if (!valid_n(n) || B < 0 || H < 0 || T < 0 || T > kMaxT) return false;
+    const int64_t lim = INT64_MAX / 64;
+    if (B > 0 && H > lim / B) return false;
+    const int64_t s = B * H;
+    if (s > 0 && T > lim / s) return false;
+    const int64_t st = s * T;
+    if (st > lim / (int64_t(n) * n)) return false;
+    *S = s;
+    *elems = st * n * n;
+    return true;
+}
+
+struct Plan {
+    int64_t K = 0;        // tokens per chunk
+    int64_t nch = 0;      // chunks per sequence (incl. padding)
+    int64_t Z = 1;        // chunks per super
+    int64_t nchunks = 0;  // S * nch
+    size_t ws = 0;        // workspace bytes
+    size_t reset_words = 0;
+    bool multi = false;
+};
+
+// Chunk length used when the caller passes chunk = 0.  Single-chunk scans need
+// no carries at all (one product per token); they are chosen when the
+// sequences alone give the GPU enough independent chains.
+int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir) {
+    if (T <= 0) return 0;
+    int64_t target;
+    if (n <= 8) {
+        const int64_t lanes_per_chain = 64 / chains_per_wave(n, dir);
+        if (S * lanes_per_chain >= 32768) return T;  // >= 512 waves
+        target = 16384;                              // 1024 waves of chains
+    } else {
+        if (S >= 2048) return T;  // one wave per chain
+        target = 2048;
+    }
+    const int64_t nch = (target + S - 1) / S;
+    int64_t K = (T + nch - 1) / nch;
+    if (K < 16) K = 16;
+    return K < T ? K : T;
+}
+
+Plan make_plan(int64_t S, int64_t T, int n, int dir, int64_t chunk) {
+    Plan p;
+    if (S <= 0 || T <= 0) return p;
+    p.K = chunk > 0 ? (chunk < T ? chunk : T) : auto_chunk_len(S, T, n, dir);
+    p.nch = (T + p.K - 1) / p.K;
+    if (p.nch <= 1) {
+        p.nch = 1;
+        p.nchunks = S;
+        return p;
+    }
+    p.multi = true;
+    const int G = chains_per_wave(n, dir);
+    if (G > 1) {
+        p.nch = (p.nch + G - 1) / G * G;  // a wave never spans two sequences
+        int64_t z = llround(sqrt(double(p.nch / G)));
+        z = z < 1 ? 1 : (z > 4 ? 4 : z);
+        p.Z = G * z;                      // a wave never spans two supers
+    } else {
+        int64_t z = llround(sqrt(double(p.nch)));
+        p.Z = z < 1 ? 1 : (z > 64 ? 64 : z);
+    }
+    p.nchunks = S * p.nch;
+    const WsLayout L = ws_layout(p.nchunks, n, acc_bytes(n), dir == MRU_DIR_FWD ? 2 : 3);
+    p.ws = L.total;
+    p.reset_words = (L.flags_off + size_t(p.nchunks) * 4 + 3) / 4;
+    return p;
+}
+
+// Blocks of 64 lanes the scan kernel launches; the dispatch grid must stay
+// below 2^32 work-items.
+bool grid_ok(const Plan& p, int n, int dir) {
+    const int64_t G = chains_per_wave(n, dir);
+    const int64_t blocks = (p.nchunks + G - 1) / G;
+    return blocks * 64 <= int64_t(UINT32_MAX);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+mru_status launched(hipError_t e) { return e == hipSuccess ? MRU_OK : MRU_ERR_HIP; }
+
+mru_status reset_ws(void* ws, const Plan& p, hipStream_t stream) {
+    const int64_t words = int64_t(p.reset_words);
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(ws_reset_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), words);
+    return launched(hipGetLastError());
+}
+
+}  // namespace
+}  // namespace mru
+
+using namespace mru;
+
+extern "C" {
+
+int32_t mru_abi_version(void) { return MRU_ABI_VERSION; }
+
+const char* mru_status_string(int32_t status) {
+    switch (status) {
+        case MRU_OK: return "MRU_OK";
+        case MRU_ERR_NULL: return "MRU_ERR_NULL: a required pointer is NULL";
+        case MRU_ERR_SHAPE: return "MRU_ERR_SHAPE: bad B/H/T or n not in {4,8,16,32}";
+        case MRU_ERR_ALIGN: return "MRU_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case MRU_ERR_ALIAS: return "MRU_ERR_ALIAS: an output overlaps an input";
+        case MRU_ERR_WORKSPACE: return "MRU_ERR_WORKSPACE: workspace missing or too small";
+        case MRU_ERR_CHUNK: return "MRU_ERR_CHUNK: chunk must be >= 0";
+        case MRU_ERR_HIP: return "MRU_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "unknown mru_status";
+    }
+}
+
+mru_status mru_build_inputs(const float* x, float* M, int64_t B, int64_t H, int64_t T, int32_t n,
+                            void* stream) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (elems == 0) return MRU_OK;
+    if (!x || !M) return MRU_ERR_NULL;
+    if (!aligned16(x) || !aligned16(M)) return MRU_ERR_ALIGN;
+    const size_t bytes = size_t(elems) * sizeof(float);
+    if (overlap(x, bytes, M, bytes)) return MRU_ERR_ALIAS;
+    (void)hipGetLastError();
+    return launched(launch_build(x, M, S * T, n, static_cast<hipStream_t>(stream)));
+}
+
+int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems) || elems == 0) return 0;
+    return int32_t(auto_chunk_len(S, T, n, direction == MRU_DIR_BWD ? 1 : 0));
+}
+
+size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
+                                int32_t chunk) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems) || elems == 0 || chunk < 0) return 0;
+    return make_plan(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, chunk).ws;
+}
+
+int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
+                      int32_t chunk, int64_t* out4) {
+    int64_t S, elems;
+    if (!out4) return MRU_ERR_NULL;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (chunk < 0) return MRU_ERR_CHUNK;
+    const Plan p = make_plan(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, chunk);
+    out4[0] = p.K;
+    out4[1] = p.nch;
+    out4[2] = p.Z;
+    out4[3] = int64_t(p.ws);
+    return MRU_OK;
+}
+
+mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
+                        int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (chunk < 0) return MRU_ERR_CHUNK;
+    if (elems == 0) return MRU_OK;
+    if (!M || !P) return MRU_ERR_NULL;
+    if (!aligned16(M) || !aligned16(P)) return MRU_ERR_ALIGN;
+    const Plan p = make_plan(S, T, n, 0, chunk);
+    if (!grid_ok(p, n, 0)) return MRU_ERR_SHAPE;
+    const size_t bytes = size_t(elems) * sizeof(float);
+    if (overlap(M, bytes, P, bytes)) return MRU_ERR_ALIAS;
+    if (p.ws > 0) {
+        if (!ws) return MRU_ERR_WORKSPACE;
+        if (!aligned16(ws)) return MRU_ERR_ALIGN;
+        if (ws_bytes < p.ws) return MRU_ERR_WORKSPACE;
+        if (overlap(ws, p.ws, P, bytes) || overlap(ws, p.ws, M, bytes)) return MRU_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (p.multi) {
+        const mru_status st = reset_ws(ws, p, s);
+        if (st != MRU_OK) return st;
+    }
+    if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s));
+    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s));
+}
+
+mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
+                        int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                        size_t ws_bytes, void* stream) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (chunk < 0) return MRU_ERR_CHUNK;
+    if (elems == 0) return MRU_OK;
+    if (!M || !P || !dP || !dM) return MRU_ERR_NULL;
+    if (!aligned16(M) || !aligned16(P) || !aligned16(dP) || !aligned16(dM)) return MRU_ERR_ALIGN;
+    const Plan p = make_plan(S, T, n, 1, chunk);
+    if (!grid_ok(p, n, 1)) return MRU_ERR_SHAPE;
+    const size_t bytes = size_t(elems) * sizeof(float);
+    if (overlap(dM, bytes, M, bytes) || overlap(dM, bytes, P, bytes) ||
+        overlap(dM, bytes, dP, bytes))
+        return MRU_ERR_ALIAS;
+    if (p.ws > 0) {
+        if (!ws) return MRU_ERR_WORKSPACE;
+        if (!aligned16(ws)) return MRU_ERR_ALIGN;
+        if (ws_bytes < p.ws) return MRU_ERR_WORKSPACE;
+        if (overlap(ws, p.ws, dM, bytes) || overlap(ws, p.ws, M, bytes) ||
+            overlap(ws, p.ws, P, bytes) || overlap(ws, p.ws, dP, bytes))
+            return MRU_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (p.multi) {
+        const mru_status st = reset_ws(ws, p, s);
+        if (st != MRU_OK) return st;
+    }
+    if (n <= 8) return launched(launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s));
+    return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s));
+}
+
+}  // extern "C"

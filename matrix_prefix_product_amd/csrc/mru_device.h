@@ -1,0 +1,130 @@
+// Device-side helpers shared by the MRU scan kernels (gfx950, wave64).
+//
+// Multi-chunk scans run in one launch.  A sequence of T tokens is cut into
+// chunks of K tokens, and consecutive chunks are grouped into "supers" of Z
+// chunks.  Each chunk is owned by one chain (a group of lanes, or a whole wave
+// for the matrix-core kernels), which
+//   1. computes its chunk aggregate (the product of its matrices, or the affine
+//      map of the backward recurrence) and publishes it with flag AGG;
+//   2. composes the aggregates of the earlier chunks of its super, in a fixed
+//      left-to-right order, waiting for their AGG flags;
+//   3. if the super is not its sequence's first, waits for the PREFIX flag of
+//      the previous super's last chunk and applies that prefix; the super's
+//      last chunk then publishes its own inclusive prefix with flag PREFIX;
+//   4. re-runs its chunk from the resulting carry and writes the outputs.
+// Every product is taken in an order fixed by (K, Z) alone, so results are
+// bitwise reproducible run to run; a chunk waits on at most Z-1 aggregates
+// and the serial part is one hop per super.  Chains take their chunk from a
+// ticket counter (not blockIdx), so a chain only waits on chunks whose owners
+// are already running, and every wait ends.  Associativity of the matrix
+// product is what makes the regrouping legal ("MRU Update: ...", section
+// "What MRU Actually Does").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mru {
+
+constexpr uint32_t kFlagEmpty = 0;
+constexpr uint32_t kFlagAgg = 1;
+constexpr uint32_t kFlagPrefix = 2;
+
+// Status bits left in the workspace header by a kernel.
+constexpr uint32_t kStatusSpinTimeout = 1;
+
+// Upper bound on polls of one flag.  With ticket ordering every poll loop ends;
+// the bound only turns a logic error into a recorded status instead of a hang.
+constexpr uint32_t kSpinLimit = 1u << 21;
+
+// Workspace layout (all offsets 256-byte aligned):
+//   [0, 256)          header: ticket counter, status word
+//   flags             uint32[nchunks]
+//   slot 0 .. slot k  nchunks * n * n elements of the chain's accumulator type
+struct WsHeader {
+    uint32_t ticket;
+    uint32_t status;
+    uint32_t pad[62];
+};
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+    size_t flags_off;
+    size_t slot_off[3];
+    size_t total;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int64_t nchunks, int n, int elem_bytes, int nslots) {
+    WsLayout L{};
+    size_t off = align256(sizeof(WsHeader));
+    L.flags_off = off;
+    off = align256(off + size_t(nchunks) * sizeof(uint32_t));
+    for (int i = 0; i < 3; ++i) {
+        L.slot_off[i] = off;
+        if (i < nslots) off = align256(off + size_t(nchunks) * size_t(n) * n * elem_bytes);
+    }
+    L.total = off;
+    return L;
+}
+
+__device__ inline uint32_t load_flag(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void store_flag(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Device-scope fences.  Publishing is: plain stores of the matrix, release
+// fence, relaxed flag store.  Reading is: relaxed flag loads, acquire fence,
+// plain loads of the matrix.  Agent scope covers every XCD of the device.
+__device__ inline void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ inline void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// One ticket per wave, taken by lane 0 and broadcast.
+__device__ inline uint32_t wave_ticket(uint32_t* counter) {
+    uint32_t t = 0;
+    if ((threadIdx.x & 63) == 0) t = atomicAdd(counter, 1u);
+    return __builtin_amdgcn_readfirstlane(t);
+}
+
+// Wave-uniform wait until *flag == want.  Must be reached by the whole wave.
+// Records a timeout in the header instead of hanging.
+__device__ inline void wait_flag_eq(const uint32_t* flag, uint32_t want, WsHeader* hdr) {
+    uint32_t polls = 0;
+    for (;;) {
+        const uint32_t f = __builtin_amdgcn_readfirstlane(load_flag(flag));
+        if (f == want) return;
+        if (++polls >= kSpinLimit) {
+            if ((threadIdx.x & 63) == 0) atomicOr(&hdr->status, kStatusSpinTimeout);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// Wave-cooperative wait until every flag in [lo, hi) is non-empty; lane i polls
+// flags lo+i, lo+i+64, ...  Must be reached by the whole wave.
+__device__ inline void wait_range_nonempty(const uint32_t* flags, int64_t lo, int64_t hi,
+                                           WsHeader* hdr) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t base = lo; base < hi; base += 64) {
+        const int64_t j = base + lane;
+        uint32_t polls = 0;
+        for (;;) {
+            const bool ok = j >= hi || load_flag(&flags[j]) != kFlagEmpty;
+            if (__all(ok)) break;
+            if (++polls >= kSpinLimit) {
+                if (lane == 0) atomicOr(&hdr->status, kStatusSpinTimeout);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+}
+
+// Kernel that clears the workspace header and flags before a multi-chunk scan.
+__global__ void ws_reset_kernel(uint32_t* words, int64_t nwords);
+
+}  // namespace mru

@@ -1,0 +1,31 @@
+// Host-side launch functions of the MRU kernels (internal to libmru.so).
+// Shapes are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mru {
+
+// LDU fill + determinant correction for ntok = B*H*T token matrices.
+hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream);
+
+// Chunked scans over S sequences of T tokens: chunk length K, nch chunks per
+// sequence (possibly padded with empty chunks), supers of Z chunks.  nch == 1
+// runs without workspace; nch > 1 needs a cleared workspace header and flags.
+hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream);
+hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, float* dM, int64_t S,
+                           int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
+                           hipStream_t stream);
+hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream);
+hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, float* dM, int64_t S,
+                           int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
+                           hipStream_t stream);
+
+// Chains per wave of the vector-ALU kernels (n = 4, 8) for direction dir.
+int valu_chains_per_wave(int n, int dir);
+
+}  // namespace mru

@@ -1,0 +1,558 @@
+// Chunked look-back scans for small matrices (n = 4, 8) on the vector ALUs.
+//
+// Right multiplication acts on each row of the running state separately:
+// row_i(P_{t-1} M_t) = row_i(P_{t-1}) M_t.  So a chain is a group of n/R lanes,
+// each owning R rows of the n-by-n state, and no lane ever needs another lane's
+// state to advance; each needs the whole input matrix of the step, which the
+// wave stages through LDS from fully coalesced global loads (one 1 KiB wave
+// load per instruction) and then reads back as a broadcast.  A wave runs
+// 64*R/n chains side by side, each on its own chunk.
+//
+// Forward ("MRU Update: ...", section "What MRU Actually Does"): the chain
+// state is R rows of P_t = P_{t-1} M_t.
+// Backward (gradient of sum_t <dP_t, P_t>): the chain state is R rows of
+// Q_t = dP_t + Q_{t+1} M_{t+1}^T, swept from the last token to the first, and
+// dM_t = P_{t-1}^T Q_t needs all rows of Q_t, exchanged through LDS.
+#include "mru_device.h"
+#include "mru_kernels.h"
+
+namespace mru {
+namespace {
+
+struct ChainInfo {
+    int64_t base;  // token index (s*T + t0) of the chunk's first token
+    int32_t len;   // tokens in the chunk (0 for an idle chain)
+    int32_t t0;    // position of the chunk's first token in its sequence
+};
+
+template <int N, int R, int TB>
+struct Valu {
+    static constexpr int NN = N * N;
+    static constexpr int LPC = N / R;             // lanes per chain
+    static constexpr int G = 64 / LPC;            // chains per wave
+    static constexpr int F4_TOK = NN / 4;         // float4 per matrix
+    static constexpr int F4_BLK = TB * F4_TOK;    // float4 per chain per staged block
+    static constexpr int LD = (G * F4_BLK) / 64;  // float4 loads per lane per staged array
+    static constexpr int CH_STRIDE = TB * NN + 4; // floats per chain in LDS (16 B skew)
+    static_assert((G * F4_BLK) % 64 == 0, "staging must tile the wave");
+    static_assert(N % R == 0 && 64 % LPC == 0, "bad row split");
+};
+
+__device__ inline ChainInfo make_chain(int64_t c, int64_t nchunks, int64_t nch, int64_t K,
+                                       int64_t T, bool reverse) {
+    ChainInfo ci{0, 0, 0};
+    if (c < nchunks) {
+        const int64_t s = c / nch;
+        const int64_t r = c - s * nch;
+        const int64_t k = reverse ? nch - 1 - r : r;
+        const int64_t t0 = k * K;
+        const int64_t t1 = min(T, t0 + K);
+        ci.base = s * T + t0;
+        ci.len = int32_t(t1 > t0 ? t1 - t0 : 0);  // chunks past T (padding) are empty
+        ci.t0 = int32_t(t0);
+    }
+    return ci;
+}
+
+template <int N, int R>
+__device__ inline void set_identity_rows(float (&st)[R][N], int r0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] = (r0 + r == j) ? 1.f : 0.f;
+}
+
+template <int N, int R>
+__device__ inline void set_zero_rows(float (&st)[R][N]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] = 0.f;
+}
+
+template <int N>
+__device__ inline void load_matrix(float (&m)[N * N], const float* src) {
+#pragma unroll
+    for (int q = 0; q < N * N / 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(src)[q];
+        m[4 * q + 0] = v.x;
+        m[4 * q + 1] = v.y;
+        m[4 * q + 2] = v.z;
+        m[4 * q + 3] = v.w;
+    }
+}
+
+// st <- st * m   (m row-major n-by-n in registers)
+template <int N, int R>
+__device__ inline void rows_times(float (&st)[R][N], const float (&m)[N * N]) {
+    float o[R][N];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) o[r][j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < N; ++j) o[r][j] = fmaf(st[r][k], m[k * N + j], o[r][j]);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] = o[r][j];
+}
+
+// st <- st * m^T   (m row-major n-by-n in registers)
+template <int N, int R>
+__device__ inline void rows_times_t(float (&st)[R][N], const float (&m)[N * N]) {
+    float o[R][N];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) o[r][j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < N; ++j) o[r][j] = fmaf(st[r][k], m[j * N + k], o[r][j]);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] = o[r][j];
+}
+
+template <int N, int R>
+__device__ inline void store_rows(float* dst, const float (&st)[R][N]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q)
+            reinterpret_cast<float4*>(dst + r * N)[q] =
+                make_float4(st[r][4 * q], st[r][4 * q + 1], st[r][4 * q + 2], st[r][4 * q + 3]);
+}
+
+template <int N, int R>
+__device__ inline void load_rows(float (&st)[R][N], const float* src) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            const float4 v = reinterpret_cast<const float4*>(src + r * N)[q];
+            st[r][4 * q] = v.x;
+            st[r][4 * q + 1] = v.y;
+            st[r][4 * q + 2] = v.z;
+            st[r][4 * q + 3] = v.w;
+        }
+}
+
+template <int N, int R>
+__device__ inline void add_rows(float (&st)[R][N], const float* src) {
+    float t[R][N];
+    load_rows<N, R>(t, src);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] += t[r][j];
+}
+
+// Staging of one block of TB tokens for every chain of the wave.  Token slot
+// tau of chain ch holds global token  base + pos(tau) + shift, where
+// pos(tau) = blk + tau going forward and len-1-(blk+tau) going backward; it is
+// loaded only when that token lies inside the chunk (pos < len, pos >= 0) and
+// inside the sequence (0 <= t0 + pos + shift < T); other slots are zero.
+template <int N, int R, int TB, bool REV>
+__device__ inline void stage_load(float4* reg, const float* src,
+                                  const ChainInfo* info, int blk, int shift, int64_t T) {
+    using V = Valu<N, R, TB>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < V::LD; ++i) {
+        const int f = i * 64 + lane;
+        const int ch = f / V::F4_BLK;
+        const int off = f % V::F4_BLK;
+        const int tau = off / V::F4_TOK;
+        const int q = off % V::F4_TOK;
+        const ChainInfo ci = info[ch];
+        const int pos = REV ? ci.len - 1 - (blk + tau) : blk + tau;
+        const int64_t tseq = int64_t(ci.t0) + pos + shift;
+        const bool ok = pos >= 0 && pos < ci.len && tseq >= 0 && tseq < T;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ok) v = reinterpret_cast<const float4*>(src + (ci.base + pos + shift) * V::NN)[q];
+        reg[i] = v;
+    }
+}
+
+template <int N, int R, int TB>
+__device__ inline void stage_store(float* lds, const float4* reg) {
+    using V = Valu<N, R, TB>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < V::LD; ++i) {
+        const int f = i * 64 + lane;
+        const int ch = f / V::F4_BLK;
+        const int off = f % V::F4_BLK;
+        reinterpret_cast<float4*>(lds + ch * V::CH_STRIDE)[off] = reg[i];
+    }
+}
+
+// One sweep of a forward chain over its chunk: st <- st * M_t for each token,
+// optionally storing the rows of every P_t.
+template <int N, int R, int TB, bool WRITE>
+__device__ void fwd_sweep(float (&st)[R][N], const float* __restrict__ M, float* __restrict__ P,
+                          float* lds, const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
+    using V = Valu<N, R, TB>;
+    const ChainInfo me = info[g];
+    float4 reg[V::LD];
+    if (maxlen > 0) stage_load<N, R, TB, false>(reg, M, info, 0, 0, T);
+    for (int blk = 0; blk < maxlen; blk += TB) {
+        __syncthreads();
+        stage_store<N, R, TB>(lds, reg);
+        __syncthreads();
+        if (blk + TB < maxlen) stage_load<N, R, TB, false>(reg, M, info, blk + TB, 0, T);
+#pragma unroll
+        for (int tau = 0; tau < TB; ++tau) {
+            const int pos = blk + tau;
+            if (pos < me.len) {
+                float m[V::NN];
+                load_matrix<N>(m, lds + g * V::CH_STRIDE + tau * V::NN);
+                rows_times<N, R>(st, m);
+                if (WRITE) store_rows<N, R>(P + (me.base + pos) * V::NN + li * R * N, st);
+            }
+        }
+    }
+}
+
+template <int N, int R, int TB>
+__global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ M,
+                                                      float* __restrict__ P, int64_t S, int64_t T,
+                                                      int64_t K, int64_t nch, int64_t Z,
+                                                      unsigned char* __restrict__ ws) {
+    using V = Valu<N, R, TB>;
+    __shared__ float lds[V::G * V::CH_STRIDE];
+    __shared__ float xch[V::G * V::NN];
+    __shared__ ChainInfo info[V::G];
+    const int lane = threadIdx.x;
+    const int g = lane / V::LPC;
+    const int li = lane % V::LPC;
+    const int64_t nchunks = S * nch;
+    const bool multi = nch > 1;
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+    const int64_t wave_id = multi ? int64_t(wave_ticket(&hdr->ticket)) : int64_t(blockIdx.x);
+    const int64_t cbase = wave_id * V::G;
+    if (lane < V::G) info[lane] = make_chain(cbase + lane, nchunks, nch, K, T, false);
+    __syncthreads();
+    int maxlen = 0;
+#pragma unroll
+    for (int i = 0; i < V::G; ++i) maxlen = max(maxlen, info[i].len);
+
+    float st[R][N];
+    set_identity_rows<N, R>(st, li * R);
+    if (!multi) {
+        fwd_sweep<N, R, TB, true>(st, M, P, lds, info, g, li, maxlen, T);
+        return;
+    }
+
+    // Multi-chunk: nch and Z are multiples of G, so the wave's G chunks lie in
+    // one sequence and one super.
+    const WsLayout L = ws_layout(nchunks, N, 4, 2);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags_off);
+    float* agg = reinterpret_cast<float*>(ws + L.slot_off[0]);
+    float* incl = reinterpret_cast<float*>(ws + L.slot_off[1]);
+    const int64_t c = cbase + g;
+    const int64_t k = c - (c / nch) * nch;
+    const int64_t first = c - k % Z;  // first chunk of the super (same for the whole wave)
+    const bool later_super = k >= Z;  // wave-uniform
+
+    // 1. chunk aggregate
+    fwd_sweep<N, R, TB, false>(st, M, P, lds, info, g, li, maxlen, T);
+    store_rows<N, R>(agg + c * V::NN + li * R * N, st);
+    fence_release();
+    if (li == 0) store_flag(&flags[c], kFlagAgg);
+
+    // 2. product of the earlier aggregates of the super, left to right
+    wait_range_nonempty(flags, first, cbase, hdr);
+    fence_acquire();
+    float lrow[R][N];
+    set_identity_rows<N, R>(lrow, li * R);
+    float m[V::NN];
+    for (int64_t j = first; j < c; ++j) {
+        load_matrix<N>(m, agg + j * V::NN);
+        rows_times<N, R>(lrow, m);
+    }
+
+    // 3. carry = (prefix of the previous super) * lrow
+    if (later_super) {
+        wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
+        fence_acquire();
+        store_rows<N, R>(xch + g * V::NN + li * R * N, lrow);
+        __syncthreads();
+        load_matrix<N>(m, xch + g * V::NN);
+        load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
+        rows_times<N, R>(st, m);
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int q = 0; q < N; ++q) st[r][q] = lrow[r][q];
+    }
+    const bool boundary = (k % Z == Z - 1) && (k + 1 < nch);
+    if (boundary) {
+        float inc[R][N];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int q = 0; q < N; ++q) inc[r][q] = st[r][q];
+        load_matrix<N>(m, agg + c * V::NN);
+        rows_times<N, R>(inc, m);
+        store_rows<N, R>(incl + c * V::NN + li * R * N, inc);
+    }
+    fence_release();
+    if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
+
+    // 4. re-run the chunk from its carry and write every prefix
+    fwd_sweep<N, R, TB, true>(st, M, P, lds, info, g, li, maxlen, T);
+}
+
+// ---------------------------------------------------------------------------- backward
+
+// One reverse sweep over the chunk.
+//   AGG pass  (GRAD = false): q <- dP_t + q M_{t+1}^T and w <- w M_{t+1}^T, from
+//             q = 0, w = I; afterwards q is the chunk's local adjoint at its first
+//             token and w the rows of (M_{a+1} ... M_{b+1})^T.
+//   GRAD pass (GRAD = true):  q <- dP_t + q M_{t+1}^T from the carry, and
+//             dM_t = P_{t-1}^T Q_t written for the lane's rows.
+// At the last token of a sequence there is no M_{t+1}: q <- dP_t.
+template <int N, int R, int TB, bool GRAD>
+__device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
+                          const float* __restrict__ P, const float* __restrict__ dP,
+                          float* __restrict__ dM, float* lds, float* qx, const ChainInfo* info,
+                          int g, int li, int maxlen, int64_t T) {
+    using V = Valu<N, R, TB>;
+    constexpr int ARR = GRAD ? 3 : 2;  // staged arrays: M(t+1), dP(t), [P(t-1)]
+    const ChainInfo me = info[g];
+    float4 rm[V::LD], rr[V::LD], rp[V::LD];
+    auto load_all = [&](int blk) {
+        stage_load<N, R, TB, true>(rm, M, info, blk, +1, T);
+        stage_load<N, R, TB, true>(rr, dP, info, blk, 0, T);
+        if (GRAD) stage_load<N, R, TB, true>(rp, P, info, blk, -1, T);
+    };
+    if (maxlen > 0) load_all(0);
+    for (int blk = 0; blk < maxlen; blk += TB) {
+        __syncthreads();
+        stage_store<N, R, TB>(lds, rm);
+        stage_store<N, R, TB>(lds + V::G * V::CH_STRIDE, rr);
+        if (GRAD) stage_store<N, R, TB>(lds + 2 * V::G * V::CH_STRIDE, rp);
+        __syncthreads();
+        if (blk + TB < maxlen) load_all(blk + TB);
+#pragma unroll
+        for (int tau = 0; tau < TB; ++tau) {
+            const int i = blk + tau;
+            const int pos = me.len - 1 - i;
+            const bool live = i < me.len;
+            const int64_t tseq = int64_t(me.t0) + pos;
+            const float* mslot = lds + g * V::CH_STRIDE + tau * V::NN;
+            const float* rslot = lds + V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN;
+            if (live) {
+                if (tseq + 1 < T) {
+                    float m[V::NN];
+                    load_matrix<N>(m, mslot);
+                    rows_times_t<N, R>(q, m);
+                    if (!GRAD) rows_times_t<N, R>(w, m);
+                } else {
+                    set_zero_rows<N, R>(q);
+                }
+                add_rows<N, R>(q, rslot + li * R * N);
+            }
+            if (GRAD) {
+                // exchange Q_t rows within the chain, then dM rows a = own rows:
+                // dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
+                __syncthreads();
+                if (live) store_rows<N, R>(qx + g * V::NN + li * R * N, q);
+                __syncthreads();
+                if (live) {
+                    float d[R][N];
+                    if (tseq > 0) {
+                        const float* pslot =
+                            lds + 2 * V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN;
+                        float qa[V::NN];
+                        load_matrix<N>(qa, qx + g * V::NN);
+                        set_zero_rows<N, R>(d);
+#pragma unroll
+                        for (int ii = 0; ii < N; ++ii) {
+                            float pc[R];
+#pragma unroll
+                            for (int r = 0; r < R; ++r) pc[r] = pslot[ii * N + li * R + r];
+#pragma unroll
+                            for (int r = 0; r < R; ++r)
+#pragma unroll
+                                for (int j = 0; j < N; ++j) d[r][j] = fmaf(pc[r], qa[ii * N + j], d[r][j]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int j = 0; j < N; ++j) d[r][j] = q[r][j];
+                    }
+                    store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
+                }
+            }
+        }
+    }
+}
+
+template <int N, int R, int TB>
+__global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ M,
+                                                      const float* __restrict__ P,
+                                                      const float* __restrict__ dP,
+                                                      float* __restrict__ dM, int64_t S,
+                                                      int64_t T, int64_t K, int64_t nch,
+                                                      int64_t Z, unsigned char* __restrict__ ws) {
+    using V = Valu<N, R, TB>;
+    __shared__ float lds[3 * V::G * V::CH_STRIDE];
+    __shared__ float qx[V::G * V::NN];
+    __shared__ ChainInfo info[V::G];
+    const int lane = threadIdx.x;
+    const int g = lane / V::LPC;
+    const int li = lane % V::LPC;
+    const int64_t nchunks = S * nch;
+    const bool multi = nch > 1;
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+    const int64_t wave_id = multi ? int64_t(wave_ticket(&hdr->ticket)) : int64_t(blockIdx.x);
+    const int64_t cbase = wave_id * V::G;
+    if (lane < V::G) info[lane] = make_chain(cbase + lane, nchunks, nch, K, T, true);
+    __syncthreads();
+    int maxlen = 0;
+#pragma unroll
+    for (int i = 0; i < V::G; ++i) maxlen = max(maxlen, info[i].len);
+
+    float q[R][N], w[R][N];
+    set_zero_rows<N, R>(q);
+    set_identity_rows<N, R>(w, li * R);
+    if (!multi) {
+        bwd_sweep<N, R, TB, true>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
+        return;
+    }
+
+    // Chunks run in reverse token order: position r = 0 is the sequence's last
+    // chunk.  The carry of a chunk is the adjoint Q at the first token of the
+    // next chunk (in token order); each chunk's map is Y -> Bl + Y W^T.
+    const WsLayout L = ws_layout(nchunks, N, 4, 3);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags_off);
+    float* swt = reinterpret_cast<float*>(ws + L.slot_off[0]);   // rows of W^T
+    float* sbl = reinterpret_cast<float*>(ws + L.slot_off[1]);   // rows of the local adjoint Bl
+    float* sinc = reinterpret_cast<float*>(ws + L.slot_off[2]);  // rows of the true adjoint
+    const int64_t c = cbase + g;
+    const int64_t r = c - (c / nch) * nch;
+    const int64_t first = c - r % Z;
+    const bool later_super = r >= Z;
+
+    // 1. affine aggregate of the chunk
+    bwd_sweep<N, R, TB, false>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
+    store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
+    store_rows<N, R>(swt + c * V::NN + li * R * N, w);
+    fence_release();
+    if (li == 0) store_flag(&flags[c], kFlagAgg);
+
+    // 2. compose the maps of the earlier chunks of the super (first applied first)
+    wait_range_nonempty(flags, first, cbase, hdr);
+    fence_acquire();
+    float wc[R][N], bc[R][N];
+    set_identity_rows<N, R>(wc, li * R);
+    set_zero_rows<N, R>(bc);
+    float m[V::NN];
+    for (int64_t j = first; j < c; ++j) {
+        load_matrix<N>(m, swt + j * V::NN);
+        if (later_super) rows_times<N, R>(wc, m);
+        rows_times<N, R>(bc, m);
+        add_rows<N, R>(bc, sbl + j * V::NN + li * R * N);
+    }
+
+    // 3. carry = Y Wc^T + Bc with Y the adjoint published by the previous super
+    if (later_super) {
+        wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
+        fence_acquire();
+        store_rows<N, R>(qx + g * V::NN + li * R * N, wc);
+        __syncthreads();
+        load_matrix<N>(m, qx + g * V::NN);
+        load_rows<N, R>(q, sinc + (first - 1) * V::NN + li * R * N);
+        rows_times<N, R>(q, m);
+#pragma unroll
+        for (int a = 0; a < R; ++a)
+#pragma unroll
+            for (int b = 0; b < N; ++b) q[a][b] += bc[a][b];
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int a = 0; a < R; ++a)
+#pragma unroll
+            for (int b = 0; b < N; ++b) q[a][b] = bc[a][b];
+    }
+    const bool boundary = (r % Z == Z - 1) && (r + 1 < nch);
+    if (boundary) {
+        float inc[R][N];
+#pragma unroll
+        for (int a = 0; a < R; ++a)
+#pragma unroll
+            for (int b = 0; b < N; ++b) inc[a][b] = q[a][b];
+        load_matrix<N>(m, swt + c * V::NN);
+        rows_times<N, R>(inc, m);
+        add_rows<N, R>(inc, sbl + c * V::NN + li * R * N);
+        store_rows<N, R>(sinc + c * V::NN + li * R * N, inc);
+    }
+    fence_release();
+    if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
+
+    // 4. re-run the chunk from the carry and write dM
+    bwd_sweep<N, R, TB, true>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
+}
+
+template <int N, int R, int TB>
+hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
+                   int64_t Z, void* ws, hipStream_t stream) {
+    using V = Valu<N, R, TB>;
+    const int64_t waves = (S * nch + V::G - 1) / V::G;
+    hipLaunchKernelGGL((fwd_valu_kernel<N, R, TB>), dim3(unsigned(waves)), dim3(64), 0, stream, M,
+                       P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+    return hipGetLastError();
+}
+
+template <int N, int R, int TB>
+hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
+                   int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
+    using V = Valu<N, R, TB>;
+    const int64_t waves = (S * nch + V::G - 1) / V::G;
+    hipLaunchKernelGGL((bwd_valu_kernel<N, R, TB>), dim3(unsigned(waves)), dim3(64), 0, stream, M,
+                       P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Row split and staging depth per n (rows per lane R, tokens per staged block TB).
+#define MRU_VALU_CFG4 4, 1, 8
+#define MRU_VALU_CFG8 8, 2, 4
+#define MRU_VALU_BWD_CFG4 4, 1, 4
+#define MRU_VALU_BWD_CFG8 8, 2, 2
+
+int valu_chains_per_wave(int n, int dir) {
+    if (n == 4) return dir == 0 ? Valu<MRU_VALU_CFG4>::G : Valu<MRU_VALU_BWD_CFG4>::G;
+    return dir == 0 ? Valu<MRU_VALU_CFG8>::G : Valu<MRU_VALU_BWD_CFG8>::G;
+}
+
+hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
+    if (n == 4) return run_fwd<MRU_VALU_CFG4>(M, P, S, T, K, nch, Z, ws, stream);
+    if (n == 8) return run_fwd<MRU_VALU_CFG8>(M, P, S, T, K, nch, Z, ws, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, float* dM, int64_t S,
+                           int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
+                           hipStream_t stream) {
+    if (n == 4) return run_bwd<MRU_VALU_BWD_CFG4>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+    if (n == 8) return run_bwd<MRU_VALU_BWD_CFG8>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mru

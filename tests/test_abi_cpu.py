@@ -1,0 +1,117 @@
+"""Host-side checks of libmru.so that need no GPU.
+
+The library must load, export every entry point include/mru.h declares, and
+answer its pure host queries (version, status strings, plans).  Argument
+validation happens before any HIP call, so invalid calls can be checked here
+too; no call in this file launches anything.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mru.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:mru_status|int32_t|size_t|const char\s*\*)\s*(mru_\w+)\s*\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def mpp():
+    import matrix_prefix_product_amd as m
+    if not os.path.exists(m.library_path()):
+        pytest.fail("libmru.so is not built: run python -m matrix_prefix_product_amd.build")
+    m.load_library()
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared_functions())
+    assert {"mru_build_inputs", "mru_scan_fwd", "mru_scan_bwd", "mru_scan_workspace_bytes",
+            "mru_scan_chunk", "mru_scan_plan", "mru_status_string", "mru_abi_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(mpp):
+    lib = ctypes.CDLL(mpp.library_path())
+    missing = [name for name in _declared_functions() if not hasattr(lib, name)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings(mpp):
+    lib = mpp.load_library()
+    text = open(HEADER).read()
+    assert lib.mru_abi_version() == int(re.search(r"#define MRU_ABI_VERSION (\d+)", text).group(1))
+    for code in range(8):
+        s = lib.mru_status_string(code).decode()
+        assert s.startswith("MRU_")
+    assert "unknown" in lib.mru_status_string(99).decode()
+
+
+def test_plans_single_and_multi(mpp):
+    # many sequences: one chunk per sequence, no workspace
+    K, nch, Z, ws = mpp.scan_plan(1024, 8, 256, 8, mpp.DIR_FWD)
+    assert (K, nch, ws) == (256, 1, 0)
+    # one long sequence: chunks, padded to whole waves of chains, with a workspace
+    K, nch, Z, ws = mpp.scan_plan(1, 1, 1024, 4, mpp.DIR_FWD)
+    assert K >= 16 and nch * K >= 1024 and nch % 16 == 0 and Z % 16 == 0 and ws > 0
+    # matrix-core path: one chain per wave, no padding
+    K, nch, Z, ws = mpp.scan_plan(1, 8, 65536, 32, mpp.DIR_FWD)
+    assert nch == math.ceil(65536 / K) and 1 <= Z <= 64 and ws > 0
+    # explicit chunk lengths, ragged tails
+    for n in (4, 8, 16, 32):
+        for chunk in (1, 5, 64, 10_000):
+            K, nch, Z, ws = mpp.scan_plan(2, 3, 203, n, mpp.DIR_BWD, chunk)
+            assert K == min(chunk, 203)
+            assert nch >= math.ceil(203 / K)
+            assert (ws == 0) == (nch == 1)
+            assert mpp.workspace_bytes(2, 3, 203, n, mpp.DIR_BWD, chunk) == ws
+    assert mpp.scan_chunk(1024, 8, 256, 8) == 256
+
+
+def test_plan_rejects_bad_arguments(mpp):
+    with pytest.raises(mpp.MRUError) as e:
+        mpp.scan_plan(1, 1, 16, 5)
+    assert e.value.status == 2
+    with pytest.raises(mpp.MRUError) as e:
+        mpp.scan_plan(1, 1, 16, 8, chunk=-1)
+    assert e.value.status == 6
+    assert mpp.workspace_bytes(-1, 1, 16, 8) == 0
+    assert mpp.scan_chunk(1, 1, 16, 6) == 0
+
+
+def test_validation_before_any_launch(mpp):
+    lib = mpp.load_library()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+    odd = ctypes.c_void_p(0x10004)
+    # shape errors
+    assert lib.mru_scan_fwd(fake, fake, 1, 1, 4, 6, 0, nul, 0, nul) == 2
+    assert lib.mru_scan_fwd(fake, fake, -1, 1, 4, 8, 0, nul, 0, nul) == 2
+    assert lib.mru_build_inputs(fake, fake, 1, 1, 4, 3, nul) == 2
+    # chunk error
+    assert lib.mru_scan_fwd(fake, fake, 1, 1, 4, 8, -2, nul, 0, nul) == 6
+    # empty problems are a no-op, even with NULL pointers
+    assert lib.mru_scan_fwd(nul, nul, 0, 4, 16, 8, 0, nul, 0, nul) == 0
+    assert lib.mru_scan_bwd(nul, nul, nul, nul, 2, 2, 0, 16, 0, nul, 0, nul) == 0
+    assert lib.mru_build_inputs(nul, nul, 3, 0, 5, 4, nul) == 0
+    # null, alignment, aliasing, workspace
+    assert lib.mru_scan_fwd(nul, fake, 1, 1, 4, 8, 0, nul, 0, nul) == 1
+    assert lib.mru_scan_bwd(fake, fake, nul, fake, 1, 1, 4, 8, 0, nul, 0, nul) == 1
+    assert lib.mru_scan_fwd(odd, fake, 1, 1, 4, 8, 0, nul, 0, nul) == 3
+    assert lib.mru_scan_fwd(fake, fake, 1, 1, 4, 8, 0, nul, 0, nul) == 4
+    assert lib.mru_build_inputs(fake, ctypes.c_void_p(0x10000 + 16), 1, 1, 4, 4, nul) == 4
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    # one sequence of 1024 tokens needs a workspace: missing / too small
+    assert lib.mru_scan_fwd(a, b, 1, 1, 1024, 4, 0, nul, 0, nul) == 5
+    need = mpp.workspace_bytes(1, 1, 1024, 4)
+    ws = ctypes.c_void_p(0x400000)
+    assert lib.mru_scan_fwd(a, b, 1, 1, 1024, 4, 0, ws, need - 1, nul) == 5
+    # workspace overlapping an output
+    assert lib.mru_scan_fwd(a, b, 1, 1, 1024, 4, 0, ctypes.c_void_p(0x200000 + 64), need, nul) == 4
+    # dM aliasing dP
+    assert lib.mru_scan_bwd(a, b, ws, ws, 1, 1, 8, 8, 1, nul, 0, nul) == 4
