@@ -35,7 +35,7 @@
  *             problem (B*H*T == 0) returns MRU_OK without launching.  The
  *             library never prints, aborts or exits.
  * Arithmetic  inputs and outputs are IEEE fp32.  The running product is kept
- *             in fp32 for n = 4, 8, 32 and in fp64 for n = 16.  Values beyond
+ *             in fp32 for n = 4, 8 and in fp64 for n = 16, 32.  Values beyond
  *             the fp32 range become +-inf / nan exactly as IEEE arithmetic
  *             gives them: nothing is clamped or renormalised.
  */

@@ -21,7 +21,7 @@ constexpr int64_t kMaxT = int64_t(1) << 30;
 
 bool valid_n(int32_t n) { return n == 4 || n == 8 || n == 16 || n == 32; }
 
-int acc_bytes(int n) { return n == 16 ? 8 : 4; }
+int acc_bytes(int n) { return n >= 16 ? 8 : 4; }
 
 int chains_per_wave(int n, int dir) { return n <= 8 ? valu_chains_per_wave(n, dir) : 1; }
 

@@ -1,23 +1,28 @@
-// Chunked look-back scans for n = 16 (fp64 running state) and n = 32 (fp32)
-// on the CDNA matrix cores, one chain per wave.
+// Chunked look-back scans for n = 16 and n = 32 on the CDNA matrix cores, one
+// chain per wave, with an fp64 running state (fp32 inputs and outputs).
 //
-// The chain keeps the TRANSPOSED state X = P^T in the MFMA accumulator layout
-// and advances it as X_t = M_t^T X_{t-1}.  The accumulator layout, read as a B
-// operand, is exactly the B layout of the same matrix once the k index of each
-// k-block is permuted (block b, lane-row kk holds k = sigma(b, kk)), so the
-// result of one step feeds the next step with no lane shuffles; the permutation
-// is absorbed into which entries of M_t each lane loads (M_t comes from memory
-// anyway).  Layouts used (gfx950, checked on the device by the parity pins):
-//   v_mfma_f64_16x16x4_f64:  A[i][k] lane i+16k,  B[k][j] lane j+16k,
-//                            D[i][j] lane j+16(i%4), reg i/4.
-//   v_mfma_f32_32x32x2_f32:  A[i][k] lane i+32k,  B[k][j] lane j+32k,
-//                            D[i][j] lane j+32((i/4)%2), reg 4(i/8)+i%4.
-// For the f64 shape the accumulator interleaves rows across lane groups.  The
-// chain relabels the state's row index with pi(i) = 4(i%4) + i/4 (a fixed
-// permutation, applied to both the rows of X and the rows of A, so the algebra
-// is unchanged); in actual indices every lane then again holds 4 contiguous
-// entries of one row of P, and only the row index of each A-operand entry is
-// permuted (Mf::acol).  Every P_t is written with 16-byte stores.
+// The chain keeps the TRANSPOSED state X = P^T in MFMA accumulator registers
+// and advances it as X_t = M_t^T X_{t-1}.  An n-by-n matrix is held as
+// (n/16)^2 tiles of 16x16, each in the accumulator layout of
+// v_mfma_f64_16x16x4_f64; a 16x16x16 tile product is 4 MFMAs.  Read as a B
+// operand, an accumulator tile is the B layout of the same tile once the k
+// index of each k-block is permuted (block b, lane group kk holds k = 4b+kk),
+// so the result of one step feeds the next step with no lane shuffles; the
+// permutation is absorbed into which entries of M_t each lane loads (M_t comes
+// from memory anyway).  Layout of v_mfma_f64_16x16x4_f64 on gfx950 (checked on
+// the device by the parity pins):
+//   A[i][k] lane i+16k,  B[k][j] lane j+16k,  D[i][j] lane j+16(i%4), reg i/4.
+// The accumulator interleaves rows across lane groups, so the chain relabels a
+// tile's row index with pi(i) = 4(i%4) + i/4 (a fixed permutation applied to
+// both the rows of X and the rows of A, which leaves the algebra unchanged).
+// In actual indices every lane then holds 4 contiguous entries of one row of P
+// per tile, and only the row index of each A-operand entry is permuted
+// (acol below).  Every P_t is written with 16-byte stores.
+//
+// The fp64 state is needed for accuracy, not range: the rounding error of an
+// fp32 state is amplified by the misalignment of prefix and suffix products
+// and reaches the 2e-4 relative error bound within a few thousand tokens at
+// n = 16 and near the fp32 range limit at n = 32.
 //
 // Forward: "MRU Update: ...", section "What MRU Actually Does" (cumulative
 // product, state times new input).  Backward: the gradient of
@@ -30,58 +35,59 @@ namespace mru {
 namespace {
 
 typedef double d4 __attribute__((ext_vector_type(4)));
-typedef float f16 __attribute__((ext_vector_type(16)));
+
+// Lane geometry of one 16x16 tile (actual indices).
+__device__ inline int tcol(int l) { return l & 15; }                     // column of X held
+__device__ inline int trow(int l, int r) { return 4 * (l >> 4) + r; }   // row of entry r / k of block r
+__device__ inline int tacol(int l) { return 4 * (l & 3) + ((l & 15) >> 2); }  // row of A entries
 
 template <int N>
-struct Mf;
-
-template <>
-struct Mf<16> {
+struct Mf {
+    static constexpr int NT = N / 16;  // tiles per dimension
+    static constexpr int NN = N * N;
     using acc_t = double;
-    using vec_t = d4;
-    static constexpr int NR = 4;  // accumulator entries per lane
-    static constexpr int NB = 4;  // k-blocks per 16x16x16 product
-    // actual column of the state held by the lane; actual row of accumulator
-    // entry r (also the k index of block b for this lane); actual row index of
-    // the lane's A-operand entries
-    __device__ static int col(int l) { return l & 15; }
-    __device__ static int row(int l, int r) { return 4 * (l >> 4) + r; }
-    __device__ static int acol(int l) { return 4 * (l & 3) + ((l & 15) >> 2); }
-    __device__ static vec_t mfma(acc_t a, acc_t b, vec_t c) {
-        return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
-    }
+    struct vec_t {
+        d4 t[NT][NT];  // tile (I, J): X[16I + trow][16J + tcol]
+    };
+    // A-operand entries a[I][K][b] of one step (tile (I, K), k-block b)
+    struct aop_t {
+        double v[NT][NT][4];
+    };
 };
 
-template <>
-struct Mf<32> {
-    using acc_t = float;
-    using vec_t = f16;
-    static constexpr int NR = 16;
-    static constexpr int NB = 16;
-    __device__ static int col(int l) { return l & 31; }
-    __device__ static int row(int l, int r) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
-    __device__ static int acol(int l) { return l & 31; }
-    __device__ static vec_t mfma(acc_t a, acc_t b, vec_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-    }
-};
+__device__ inline d4 mfma(double a, double b, d4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
 
-// X <- A X + C for the transposed-state chain; a[b] is this lane's A-operand
-// entry of k-block b, X's accumulator entry b is the matching B entry.
+// X <- A X + C.  a holds this lane's A entries; X's accumulator entry b of tile
+// (K, J) is the matching B entry of k-block b.
 template <int N>
-__device__ inline typename Mf<N>::vec_t chain_step(const typename Mf<N>::acc_t (&a)[Mf<N>::NB],
+__device__ inline typename Mf<N>::vec_t chain_step(const typename Mf<N>::aop_t& a,
                                                    const typename Mf<N>::vec_t& X,
-                                                   typename Mf<N>::vec_t acc) {
+                                                   const typename Mf<N>::vec_t& C) {
+    constexpr int NT = Mf<N>::NT;
+    typename Mf<N>::vec_t out;
 #pragma unroll
-    for (int b = 0; b < Mf<N>::NB; ++b) acc = Mf<N>::mfma(a[b], X[b], acc);
-    return acc;
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+            d4 acc = C.t[I][J];
+#pragma unroll
+            for (int K = 0; K < NT; ++K)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc = mfma(a.v[I][K][b], X.t[K][J][b], acc);
+            out.t[I][J] = acc;
+        }
+    return out;
 }
 
 template <int N>
 __device__ inline typename Mf<N>::vec_t vzero() {
     typename Mf<N>::vec_t v;
 #pragma unroll
-    for (int r = 0; r < Mf<N>::NR; ++r) v[r] = 0;
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) v.t[I][J] = d4{0.0, 0.0, 0.0, 0.0};
     return v;
 }
 
@@ -89,77 +95,83 @@ template <int N>
 __device__ inline typename Mf<N>::vec_t videntity(int l) {
     typename Mf<N>::vec_t v;
 #pragma unroll
-    for (int r = 0; r < Mf<N>::NR; ++r) v[r] = (Mf<N>::row(l, r) == Mf<N>::col(l)) ? 1 : 0;
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v.t[I][J][r] = (16 * I + trow(l, r) == 16 * J + tcol(l)) ? 1.0 : 0.0;
     return v;
 }
 
-// Accumulator entries r of a lane are row col(l), columns row(l, r) of the
-// (untransposed) matrix; columns come in runs of 4.  Store / load that matrix
-// row-major at `p`.
+// The accumulator holds X = Y^T; store / load Y row-major at p.  Lane entries
+// of tile (I, J) are Y[16J + tcol][16I + trow(l, 0..3)], 4 contiguous values.
 template <int N, class T>
 __device__ inline void store_acc_rows(T* p, const typename Mf<N>::vec_t& X) {
     const int l = threadIdx.x & 63;
-    const int c = Mf<N>::col(l);
 #pragma unroll
-    for (int r = 0; r < Mf<N>::NR; r += 4) {
-        const int j = Mf<N>::row(l, r);
-        if constexpr (sizeof(T) == 4) {
-            *reinterpret_cast<float4*>(p + c * N + j) =
-                make_float4(float(X[r]), float(X[r + 1]), float(X[r + 2]), float(X[r + 3]));
-        } else {
-            *reinterpret_cast<double2*>(p + c * N + j) = make_double2(X[r], X[r + 1]);
-            *reinterpret_cast<double2*>(p + c * N + j + 2) = make_double2(X[r + 2], X[r + 3]);
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) {
+            T* q = p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0);
+            const d4 x = X.t[I][J];
+            if constexpr (sizeof(T) == 4) {
+                *reinterpret_cast<float4*>(q) = make_float4(float(x[0]), float(x[1]), float(x[2]), float(x[3]));
+            } else {
+                *reinterpret_cast<double2*>(q) = make_double2(x[0], x[1]);
+                *reinterpret_cast<double2*>(q + 2) = make_double2(x[2], x[3]);
+            }
         }
-    }
 }
 
 template <int N, class T>
 __device__ inline typename Mf<N>::vec_t load_acc_rows(const T* p) {
     const int l = threadIdx.x & 63;
-    const int c = Mf<N>::col(l);
     typename Mf<N>::vec_t X;
 #pragma unroll
-    for (int r = 0; r < Mf<N>::NR; r += 4) {
-        const int j = Mf<N>::row(l, r);
-        if constexpr (sizeof(T) == 4) {
-            const float4 v = *reinterpret_cast<const float4*>(p + c * N + j);
-            X[r] = v.x; X[r + 1] = v.y; X[r + 2] = v.z; X[r + 3] = v.w;
-        } else {
-            const double2 v0 = *reinterpret_cast<const double2*>(p + c * N + j);
-            const double2 v1 = *reinterpret_cast<const double2*>(p + c * N + j + 2);
-            X[r] = v0.x; X[r + 1] = v0.y; X[r + 2] = v1.x; X[r + 3] = v1.y;
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) {
+            const T* q = p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0);
+            if constexpr (sizeof(T) == 4) {
+                const float4 v = *reinterpret_cast<const float4*>(q);
+                X.t[I][J] = d4{v.x, v.y, v.z, v.w};
+            } else {
+                const double2 v0 = *reinterpret_cast<const double2*>(q);
+                const double2 v1 = *reinterpret_cast<const double2*>(q + 2);
+                X.t[I][J] = d4{v0.x, v0.y, v1.x, v1.y};
+            }
         }
-    }
     return X;
 }
 
-// A operand for X <- Y^T X, i.e. right multiplication of the untransposed
-// state by Y (row-major at p): lane entry b = Y[row(l, b)][acol(l)].
+// A operand for X <- Y^T X (right multiplication of the untransposed state by
+// Y, row-major at p): a[I][K][b] = Y[16K + trow(l, b)][16I + tacol(l)].
 template <int N, class T>
-__device__ inline void load_a_transposed(typename Mf<N>::acc_t (&a)[Mf<N>::NB], const T* p) {
+__device__ inline void load_a_transposed(typename Mf<N>::aop_t& a, const T* p) {
     const int l = threadIdx.x & 63;
-    const int c = Mf<N>::acol(l);
 #pragma unroll
-    for (int b = 0; b < Mf<N>::NB; ++b) a[b] = typename Mf<N>::acc_t(p[Mf<N>::row(l, b) * N + c]);
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int K = 0; K < Mf<N>::NT; ++K)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                a.v[I][K][b] = double(p[(16 * K + trow(l, b)) * N + 16 * I + tacol(l)]);
 }
 
 // A operand for X <- Y X (left multiplication of the state by Y, row-major at
-// p): lane entry b = Y[acol(l)][row(l, b)]; runs of 4 are contiguous.
+// p): a[I][K][b] = Y[16I + tacol(l)][16K + trow(l, b)], 4 contiguous values.
 template <int N, class T>
-__device__ inline void load_a_direct(typename Mf<N>::acc_t (&a)[Mf<N>::NB], const T* p) {
+__device__ inline void load_a_direct(typename Mf<N>::aop_t& a, const T* p) {
     const int l = threadIdx.x & 63;
-    const int c = Mf<N>::acol(l);
 #pragma unroll
-    for (int b = 0; b < Mf<N>::NB; b += 4) {
-        const int j = Mf<N>::row(l, b);
-        if constexpr (sizeof(T) == 4) {
-            const float4 v = *reinterpret_cast<const float4*>(p + c * N + j);
-            a[b] = v.x; a[b + 1] = v.y; a[b + 2] = v.z; a[b + 3] = v.w;
-        } else {
+    for (int I = 0; I < Mf<N>::NT; ++I)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) a[b + u] = typename Mf<N>::acc_t(p[c * N + j + u]);
+        for (int K = 0; K < Mf<N>::NT; ++K) {
+            const T* q = p + (16 * I + tacol(l)) * N + 16 * K + trow(l, 0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) a.v[I][K][b] = double(q[b]);
         }
-    }
 }
 
 struct Chunk {
@@ -188,31 +200,36 @@ template <int N, int PF, bool WRITE>
 __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
                           float* __restrict__ P, int64_t base, int len) {
     using F = Mf<N>;
-    using acc_t = typename F::acc_t;
-    constexpr int NN = N * N;
+    constexpr int NT = F::NT;
+    constexpr int NN = F::NN;
+    constexpr int NA = NT * NT * 4;  // A-operand entries per token and lane
     const int l = threadIdx.x & 63;
-    const int ac = F::acol(l);
-    int aoff[F::NB];
+    // entry (I, K, b) of M_t^T's A operand: M_t[16K + trow(l, b)][16I + tacol(l)]
+    int aoff[NA];
 #pragma unroll
-    for (int b = 0; b < F::NB; ++b) aoff[b] = F::row(l, b) * N + ac;
-    float ring[PF][F::NB];
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int K = 0; K < NT; ++K)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                aoff[(I * NT + K) * 4 + b] = (16 * K + trow(l, b)) * N + 16 * I + tacol(l);
+    float ring[PF][NA];
 #pragma unroll
     for (int p = 0; p < PF; ++p)
         if (p < len)
 #pragma unroll
-            for (int b = 0; b < F::NB; ++b) ring[p][b] = M[(base + p) * NN + aoff[b]];
+            for (int e = 0; e < NA; ++e) ring[p][e] = M[(base + p) * NN + aoff[e]];
     for (int t0 = 0; t0 < len; t0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int t = t0 + p;
             if (t < len) {
-                acc_t a[F::NB];
+                typename F::aop_t a;
 #pragma unroll
-                for (int b = 0; b < F::NB; ++b) a[b] = acc_t(ring[p][b]);
+                for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(ring[p][e]);
                 if (t + PF < len)
 #pragma unroll
-                    for (int b = 0; b < F::NB; ++b)
-                        ring[p][b] = M[(base + t + PF) * NN + aoff[b]];
+                    for (int e = 0; e < NA; ++e) ring[p][e] = M[(base + t + PF) * NN + aoff[e]];
                 X = chain_step<N>(a, X, vzero<N>());
                 if (WRITE) store_acc_rows<N, float>(P + (base + t) * NN, X);
             }
@@ -229,7 +246,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
     constexpr int NN = N * N;
-    __shared__ acc_t xl[NN];
+    __shared__ double xl[NN];
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -260,7 +277,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     // 2. Lt = (agg[first] ... agg[c-1])^T
     wait_range_nonempty(flags, first, c, hdr);
     fence_acquire();
-    acc_t a[F::NB];
+    typename F::aop_t a;
     X = videntity<N>(l);
     for (int64_t j = first; j < c; ++j) {
         load_a_transposed<N, acc_t>(a, agg + j * NN);
@@ -297,43 +314,55 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
 template <int N, int PF, bool GRAD>
 __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                           const float* __restrict__ M, const float* __restrict__ P,
-                          const float* __restrict__ dP, float* __restrict__ dM,
-                          typename Mf<N>::acc_t* tr, int64_t base, int64_t t0, int len,
-                          int64_t T) {
+                          const float* __restrict__ dP, float* __restrict__ dM, double* tr,
+                          int64_t base, int64_t t0, int len, int64_t T) {
     using F = Mf<N>;
-    using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
-    constexpr int NN = N * N;
+    constexpr int NT = F::NT;
+    constexpr int NN = F::NN;
+    constexpr int NA = NT * NT * 4;
     constexpr int TS = N + 1;  // LDS row stride of the transpose buffer
     const int l = threadIdx.x & 63;
-    const int c = F::col(l);
-    const int ac = F::acol(l);
-    int poff[F::NB];
-#pragma unroll
-    for (int b = 0; b < F::NB; ++b) poff[b] = F::row(l, b) * N + c;
+    const int c = tcol(l);
+    const int ac = tacol(l);
 
-    // ring of prefetched operands: M_{t+1} and dP_t (runs of 4 in row c), P_{t-1}
-    float rm[PF][F::NB], rr[PF][F::NR], rp[PF][GRAD ? F::NB : 1];
+    // ring of prefetched operands per token: M_{t+1} (A operand, runs of 4),
+    // dP_t (C operand, runs of 4), P_{t-1} (B operand of the dM product)
+    float rm[PF][NA], rr[PF][NA], rp[PF][GRAD ? NA : 1];
     auto fetch = [&](int slot, int i) {
         const int pos = len - 1 - i;
         const int64_t tok = base + pos;
         const int64_t tseq = t0 + pos;
         if (tseq + 1 < T) {
 #pragma unroll
-            for (int b = 0; b < F::NB; b += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(M + (tok + 1) * NN + ac * N + F::row(l, b));
-                rm[slot][b] = v.x; rm[slot][b + 1] = v.y; rm[slot][b + 2] = v.z; rm[slot][b + 3] = v.w;
-            }
+            for (int I = 0; I < NT; ++I)
+#pragma unroll
+                for (int K = 0; K < NT; ++K) {
+                    const float4 v = *reinterpret_cast<const float4*>(
+                        M + (tok + 1) * NN + (16 * I + ac) * N + 16 * K + trow(l, 0));
+                    float* d = &rm[slot][(I * NT + K) * 4];
+                    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+                }
         }
 #pragma unroll
-        for (int r = 0; r < F::NR; r += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(dP + tok * NN + c * N + F::row(l, r));
-            rr[slot][r] = v.x; rr[slot][r + 1] = v.y; rr[slot][r + 2] = v.z; rr[slot][r + 3] = v.w;
-        }
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+                const float4 v = *reinterpret_cast<const float4*>(
+                    dP + tok * NN + (16 * J + c) * N + 16 * I + trow(l, 0));
+                float* d = &rr[slot][(I * NT + J) * 4];
+                d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+            }
         if constexpr (GRAD) {
             if (tseq > 0)
 #pragma unroll
-                for (int b = 0; b < F::NB; ++b) rp[slot][b] = P[(tok - 1) * NN + poff[b]];
+                for (int K = 0; K < NT; ++K)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            rp[slot][(K * NT + J) * 4 + b] =
+                                P[(tok - 1) * NN + (16 * K + trow(l, b)) * N + 16 * J + c];
         }
     };
 #pragma unroll
@@ -348,38 +377,45 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                 const int64_t tok = base + pos;
                 const int64_t tseq = t0 + pos;
                 const bool has_next = tseq + 1 < T;
-                acc_t a[F::NB];
-                vec_t cr;
+                typename F::aop_t a;
+                vec_t cr, bv;
 #pragma unroll
-                for (int b = 0; b < F::NB; ++b) a[b] = acc_t(rm[p][b]);
-#pragma unroll
-                for (int r = 0; r < F::NR; ++r) cr[r] = acc_t(rr[p][r]);
-                acc_t bp[F::NB];
+                for (int e = 0; e < NA; ++e) {
+                    a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rm[p][e]);
+                    cr.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rr[p][e]);
+                }
                 if constexpr (GRAD) {
 #pragma unroll
-                    for (int b = 0; b < F::NB; ++b) bp[b] = acc_t(rp[p][b]);
+                    for (int e = 0; e < NA; ++e) bv.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rp[p][e]);
                 }
                 if (i + PF < len) fetch(p, i + PF);
                 if (has_next) {
                     G = chain_step<N>(a, G, cr);
-                    if (!GRAD) W = chain_step<N>(a, W, vzero<N>());
+                    if constexpr (!GRAD) W = chain_step<N>(a, W, vzero<N>());
                 } else {
                     G = cr;
                 }
                 if constexpr (GRAD) {
                     float* out = dM + tok * NN;
                     if (tseq > 0) {
-                        // transpose G through LDS: A operand entry b = G[col][row(l, b)]
+                        // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
                         __syncthreads();
 #pragma unroll
-                        for (int r = 0; r < F::NR; ++r) tr[F::row(l, r) * TS + c] = G[r];
+                        for (int I = 0; I < NT; ++I)
+#pragma unroll
+                            for (int J = 0; J < NT; ++J)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    tr[(16 * I + trow(l, r)) * TS + 16 * J + c] = G.t[I][J][r];
                         __syncthreads();
-                        acc_t ag[F::NB];
+                        typename F::aop_t ag;
 #pragma unroll
-                        for (int b = 0; b < F::NB; ++b) ag[b] = tr[ac * TS + F::row(l, b)];
-                        vec_t bv;
+                        for (int I = 0; I < NT; ++I)
 #pragma unroll
-                        for (int b = 0; b < F::NB; ++b) bv[b] = bp[b];
+                            for (int K = 0; K < NT; ++K)
+#pragma unroll
+                                for (int b = 0; b < 4; ++b)
+                                    ag.v[I][K][b] = tr[(16 * I + ac) * TS + 16 * K + trow(l, b)];
                         const vec_t D = chain_step<N>(ag, bv, vzero<N>());
                         store_acc_rows<N, float>(out, D);
                     } else {
@@ -402,8 +438,8 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
     constexpr int NN = N * N;
-    __shared__ acc_t tr[N * (N + 1)];
-    __shared__ acc_t xl[NN];
+    __shared__ double tr[N * (N + 1)];
+    __shared__ double xl[NN];
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -441,7 +477,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     // 2. compose the maps of the earlier chunks of the super (first applied first)
     wait_range_nonempty(flags, first, c, hdr);
     fence_acquire();
-    acc_t a[F::NB];
+    typename F::aop_t a;
     vec_t WC = videntity<N>(l);
     G = vzero<N>();
     for (int64_t j = first; j < c; ++j) {
