@@ -118,12 +118,26 @@ hipError_t run_build(const float* x, float* M, int64_t ntok, hipStream_t stream)
 
 }  // namespace
 
+// Rows per lane for each n (overridable at build time for tuning sweeps).
+#ifndef MRU_BUILD_R4
+#define MRU_BUILD_R4 1
+#endif
+#ifndef MRU_BUILD_R8
+#define MRU_BUILD_R8 1
+#endif
+#ifndef MRU_BUILD_R16
+#define MRU_BUILD_R16 2
+#endif
+#ifndef MRU_BUILD_R32
+#define MRU_BUILD_R32 2
+#endif
+
 hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream) {
     switch (n) {
-        case 4: return run_build<4, 1>(x, M, ntok, stream);
-        case 8: return run_build<8, 2>(x, M, ntok, stream);
-        case 16: return run_build<16, 2>(x, M, ntok, stream);
-        case 32: return run_build<32, 2>(x, M, ntok, stream);
+        case 4: return run_build<4, MRU_BUILD_R4>(x, M, ntok, stream);
+        case 8: return run_build<8, MRU_BUILD_R8>(x, M, ntok, stream);
+        case 16: return run_build<16, MRU_BUILD_R16>(x, M, ntok, stream);
+        case 32: return run_build<32, MRU_BUILD_R32>(x, M, ntok, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -76,11 +76,56 @@ __device__ inline void store_flag(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Device-scope fences.  Publishing is: plain stores of the matrix, release
-// fence, relaxed flag store.  Reading is: relaxed flag loads, acquire fence,
-// plain loads of the matrix.  Agent scope covers every XCD of the device.
-__device__ inline void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ inline void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Publishing protocol of the look-back workspace.
+//
+// MRU_WS_COHERENT = 1 (default): every published matrix entry and every flag is
+// written and read with agent-scope atomic accesses, which the compiler makes
+// coherent across all XCDs of the device (they bypass the per-XCD L2 for this
+// data).  A writer waits for its data stores to complete (vmcnt 0) before it
+// stores the flag; a reader only issues its data loads after it has seen the
+// flag.  No cache-wide write-back or invalidate is needed, so other waves'
+// streaming traffic through L2 is not disturbed.
+// MRU_WS_COHERENT = 0: plain accesses with agent-scope release / acquire
+// fences (L2 write-back and invalidate).
+#ifndef MRU_WS_COHERENT
+#define MRU_WS_COHERENT 1
+#endif
+
+template <class T>
+__device__ inline void ws_store(T* p, T v) {
+#if MRU_WS_COHERENT
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    *p = v;
+#endif
+}
+
+template <class T>
+__device__ inline T ws_load(const T* p) {
+#if MRU_WS_COHERENT
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    return *p;
+#endif
+}
+
+// Between a writer's data stores and its flag store.
+__device__ inline void fence_release() {
+#if MRU_WS_COHERENT
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#else
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#endif
+}
+
+// Between a reader's flag loads and its data loads.
+__device__ inline void fence_acquire() {
+#if MRU_WS_COHERENT
+    __asm__ volatile("" ::: "memory");
+#else
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+}
 
 // One ticket per wave, taken by lane 0 and broadcast.
 __device__ inline uint32_t wave_ticket(uint32_t* counter) {

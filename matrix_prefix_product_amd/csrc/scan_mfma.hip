@@ -174,6 +174,49 @@ __device__ inline void load_a_direct(typename Mf<N>::aop_t& a, const T* p) {
         }
 }
 
+// Workspace (look-back) accessors: the same layouts as store_acc_rows /
+// load_acc_rows / load_a_transposed, element by element through ws_store /
+// ws_load so that other XCDs see them coherently.
+template <int N>
+__device__ inline void ws_store_acc_rows(double* p, const typename Mf<N>::vec_t& X) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) {
+            double* q = p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ws_store(q + r, X.t[I][J][r]);
+        }
+}
+
+template <int N>
+__device__ inline typename Mf<N>::vec_t ws_load_acc_rows(const double* p) {
+    const int l = threadIdx.x & 63;
+    typename Mf<N>::vec_t X;
+#pragma unroll
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) {
+            const double* q = p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X.t[I][J][r] = ws_load(q + r);
+        }
+    return X;
+}
+
+template <int N>
+__device__ inline void ws_load_a_transposed(typename Mf<N>::aop_t& a, const double* p) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int K = 0; K < Mf<N>::NT; ++K)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                a.v[I][K][b] = ws_load(p + (16 * K + trow(l, b)) * N + 16 * I + tacol(l));
+}
+
 struct Chunk {
     int64_t c;     // chunk index
     int64_t base;  // token index s*T + t0
@@ -196,6 +239,10 @@ __device__ inline Chunk chunk_at(int64_t c, int64_t nch, int64_t K, int64_t T, b
 
 // ---------------------------------------------------------------------------- forward
 
+// The operand ring: the loads for token t + PF are issued right after token t's
+// operands are consumed.  Loads are unconditional (addresses clamped into the
+// chunk), and the main loop runs whole blocks of PF tokens, so every ring slot
+// stays in fixed registers and PF tokens of loads stay in flight.
 template <int N, int PF, bool WRITE>
 __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
                           float* __restrict__ P, int64_t base, int len) {
@@ -203,6 +250,7 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
     constexpr int NT = F::NT;
     constexpr int NN = F::NN;
     constexpr int NA = NT * NT * 4;  // A-operand entries per token and lane
+    if (len <= 0) return;
     const int l = threadIdx.x & 63;
     // entry (I, K, b) of M_t^T's A operand: M_t[16K + trow(l, b)][16I + tacol(l)]
     int aoff[NA];
@@ -213,28 +261,34 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
 #pragma unroll
             for (int b = 0; b < 4; ++b)
                 aoff[(I * NT + K) * 4 + b] = (16 * K + trow(l, b)) * N + 16 * I + tacol(l);
+    const float* Mb = M + base * NN;
     float ring[PF][NA];
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < len)
+    for (int p = 0; p < PF; ++p) {
+        const int u = min(p, len - 1);
 #pragma unroll
-            for (int e = 0; e < NA; ++e) ring[p][e] = M[(base + p) * NN + aoff[e]];
-    for (int t0 = 0; t0 < len; t0 += PF) {
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int t = t0 + p;
-            if (t < len) {
-                typename F::aop_t a;
-#pragma unroll
-                for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(ring[p][e]);
-                if (t + PF < len)
-#pragma unroll
-                    for (int e = 0; e < NA; ++e) ring[p][e] = M[(base + t + PF) * NN + aoff[e]];
-                X = chain_step<N>(a, X, vzero<N>());
-                if (WRITE) store_acc_rows<N, float>(P + (base + t) * NN, X);
-            }
-        }
+        for (int e = 0; e < NA; ++e) ring[p][e] = Mb[u * NN + aoff[e]];
     }
+    auto step = [&](int p, int t, bool refill) {
+        typename F::aop_t a;
+#pragma unroll
+        for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(ring[p][e]);
+        if (refill) {
+            const int u = min(t + PF, len - 1);
+#pragma unroll
+            for (int e = 0; e < NA; ++e) ring[p][e] = Mb[u * NN + aoff[e]];
+        }
+        X = chain_step<N>(a, X, vzero<N>());
+        if (WRITE) store_acc_rows<N, float>(P + (base + t) * NN, X);
+    };
+    int t0 = 0;
+    for (; t0 + PF <= len; t0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) step(p, t0 + p, true);
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (t0 + p < len) step(p, t0 + p, false);
 }
 
 template <int N, int PF>
@@ -270,7 +324,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
 
     // 1. chunk aggregate
     fwd_sweep<N, PF, false>(X, M, P, ch.base, ch.len);
-    store_acc_rows<N, acc_t>(agg + c * NN, X);
+    ws_store_acc_rows<N>(agg + c * NN, X);
     fence_release();
     if (l == 0) store_flag(&flags[c], kFlagAgg);
 
@@ -280,7 +334,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     typename F::aop_t a;
     X = videntity<N>(l);
     for (int64_t j = first; j < c; ++j) {
-        load_a_transposed<N, acc_t>(a, agg + j * NN);
+        ws_load_a_transposed<N>(a, agg + j * NN);
         X = chain_step<N>(a, X, vzero<N>());
     }
 
@@ -291,12 +345,12 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
         fence_acquire();
         __syncthreads();
         load_a_transposed<N, acc_t>(a, xl);
-        X = chain_step<N>(a, load_acc_rows<N, acc_t>(incl + (first - 1) * NN), vzero<N>());
+        X = chain_step<N>(a, ws_load_acc_rows<N>(incl + (first - 1) * NN), vzero<N>());
     }
     if (k % Z == Z - 1 && k + 1 < nch) {
-        load_a_transposed<N, acc_t>(a, agg + c * NN);
+        ws_load_a_transposed<N>(a, agg + c * NN);
         const vec_t inc = chain_step<N>(a, X, vzero<N>());
-        store_acc_rows<N, acc_t>(incl + c * NN, inc);
+        ws_store_acc_rows<N>(incl + c * NN, inc);
         fence_release();
         if (l == 0) store_flag(&flags[c], kFlagPrefix);
     }
@@ -322,109 +376,113 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
     constexpr int NN = F::NN;
     constexpr int NA = NT * NT * 4;
     constexpr int TS = N + 1;  // LDS row stride of the transpose buffer
+    if (len <= 0) return;
     const int l = threadIdx.x & 63;
     const int c = tcol(l);
     const int ac = tacol(l);
+    // positions relative to the chunk start whose loads are always in bounds:
+    // M_{t+1} exists for pos < hi_m, P_{t-1} for pos >= lo_p
+    const int hi_m = int(min<int64_t>(len, T - 1 - t0));  // pos + 1 + t0 < T
+    const int lo_p = t0 > 0 ? 0 : 1;                      // pos - 1 + t0 >= 0
+    const float* Mb = M + base * NN;
+    const float* Pb = P + base * NN;
+    const float* Rb = dP + base * NN;
 
     // ring of prefetched operands per token: M_{t+1} (A operand, runs of 4),
     // dP_t (C operand, runs of 4), P_{t-1} (B operand of the dM product)
     float rm[PF][NA], rr[PF][NA], rp[PF][GRAD ? NA : 1];
     auto fetch = [&](int slot, int i) {
-        const int pos = len - 1 - i;
-        const int64_t tok = base + pos;
-        const int64_t tseq = t0 + pos;
-        if (tseq + 1 < T) {
+        const int pos = max(len - 1 - i, 0);
+        const int pm = min(pos, hi_m - 1) + 1;  // clamped: only used when pos < hi_m
 #pragma unroll
-            for (int I = 0; I < NT; ++I)
+        for (int I = 0; I < NT; ++I)
 #pragma unroll
-                for (int K = 0; K < NT; ++K) {
-                    const float4 v = *reinterpret_cast<const float4*>(
-                        M + (tok + 1) * NN + (16 * I + ac) * N + 16 * K + trow(l, 0));
-                    float* d = &rm[slot][(I * NT + K) * 4];
-                    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-                }
-        }
+            for (int K = 0; K < NT; ++K) {
+                const float4 v = *reinterpret_cast<const float4*>(
+                    Mb + int64_t(hi_m > 0 ? pm : pos) * NN + (16 * I + ac) * N + 16 * K + trow(l, 0));
+                float* d = &rm[slot][(I * NT + K) * 4];
+                d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+            }
 #pragma unroll
         for (int I = 0; I < NT; ++I)
 #pragma unroll
             for (int J = 0; J < NT; ++J) {
                 const float4 v = *reinterpret_cast<const float4*>(
-                    dP + tok * NN + (16 * J + c) * N + 16 * I + trow(l, 0));
+                    Rb + int64_t(pos) * NN + (16 * J + c) * N + 16 * I + trow(l, 0));
                 float* d = &rr[slot][(I * NT + J) * 4];
                 d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
             }
         if constexpr (GRAD) {
-            if (tseq > 0)
+            const int pp = max(pos, lo_p) - 1;  // clamped: only used when pos >= lo_p
 #pragma unroll
-                for (int K = 0; K < NT; ++K)
+            for (int K = 0; K < NT; ++K)
+#pragma unroll
+                for (int J = 0; J < NT; ++J)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        rp[slot][(K * NT + J) * 4 + b] =
+                            Pb[int64_t(pp) * NN + (16 * K + trow(l, b)) * N + 16 * J + c];
+        }
+    };
+    auto step = [&](int p, int i, bool refill) {
+        const int pos = len - 1 - i;
+        const bool has_next = pos < hi_m;
+        typename F::aop_t a;
+        vec_t cr, bv;
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rm[p][e]);
+            cr.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rr[p][e]);
+        }
+        if constexpr (GRAD) {
+#pragma unroll
+            for (int e = 0; e < NA; ++e) bv.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rp[p][e]);
+        }
+        if (refill) fetch(p, i + PF);
+        if (has_next) {
+            G = chain_step<N>(a, G, cr);
+            if constexpr (!GRAD) W = chain_step<N>(a, W, vzero<N>());
+        } else {
+            G = cr;
+        }
+        if constexpr (GRAD) {
+            float* out = dM + (base + pos) * NN;
+            if (pos >= lo_p) {
+                // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
+                __syncthreads();
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
 #pragma unroll
                     for (int J = 0; J < NT; ++J)
 #pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            tr[(16 * I + trow(l, r)) * TS + 16 * J + c] = G.t[I][J][r];
+                __syncthreads();
+                typename F::aop_t ag;
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
+#pragma unroll
+                    for (int K = 0; K < NT; ++K)
+#pragma unroll
                         for (int b = 0; b < 4; ++b)
-                            rp[slot][(K * NT + J) * 4 + b] =
-                                P[(tok - 1) * NN + (16 * K + trow(l, b)) * N + 16 * J + c];
+                            ag.v[I][K][b] = tr[(16 * I + ac) * TS + 16 * K + trow(l, b)];
+                const vec_t D = chain_step<N>(ag, bv, vzero<N>());
+                store_acc_rows<N, float>(out, D);
+            } else {
+                store_acc_rows<N, float>(out, G);  // t = 0: P_{-1} = I
+            }
         }
     };
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < len) fetch(p, p);
-    for (int i0 = 0; i0 < len; i0 += PF) {
+    for (int p = 0; p < PF; ++p) fetch(p, min(p, len - 1));
+    int i0 = 0;
+    for (; i0 + PF <= len; i0 += PF) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int i = i0 + p;
-            if (i < len) {
-                const int pos = len - 1 - i;
-                const int64_t tok = base + pos;
-                const int64_t tseq = t0 + pos;
-                const bool has_next = tseq + 1 < T;
-                typename F::aop_t a;
-                vec_t cr, bv;
-#pragma unroll
-                for (int e = 0; e < NA; ++e) {
-                    a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rm[p][e]);
-                    cr.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rr[p][e]);
-                }
-                if constexpr (GRAD) {
-#pragma unroll
-                    for (int e = 0; e < NA; ++e) bv.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rp[p][e]);
-                }
-                if (i + PF < len) fetch(p, i + PF);
-                if (has_next) {
-                    G = chain_step<N>(a, G, cr);
-                    if constexpr (!GRAD) W = chain_step<N>(a, W, vzero<N>());
-                } else {
-                    G = cr;
-                }
-                if constexpr (GRAD) {
-                    float* out = dM + tok * NN;
-                    if (tseq > 0) {
-                        // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
-                        __syncthreads();
-#pragma unroll
-                        for (int I = 0; I < NT; ++I)
-#pragma unroll
-                            for (int J = 0; J < NT; ++J)
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    tr[(16 * I + trow(l, r)) * TS + 16 * J + c] = G.t[I][J][r];
-                        __syncthreads();
-                        typename F::aop_t ag;
-#pragma unroll
-                        for (int I = 0; I < NT; ++I)
-#pragma unroll
-                            for (int K = 0; K < NT; ++K)
-#pragma unroll
-                                for (int b = 0; b < 4; ++b)
-                                    ag.v[I][K][b] = tr[(16 * I + ac) * TS + 16 * K + trow(l, b)];
-                        const vec_t D = chain_step<N>(ag, bv, vzero<N>());
-                        store_acc_rows<N, float>(out, D);
-                    } else {
-                        store_acc_rows<N, float>(out, G);
-                    }
-                }
-            }
-        }
+        for (int p = 0; p < PF; ++p) step(p, i0 + p, true);
     }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (i0 + p < len) step(p, i0 + p, false);
 }
 
 template <int N, int PF>
@@ -469,8 +527,8 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
 
     // 1. affine aggregate
     bwd_sweep<N, PF, false>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T);
-    store_acc_rows<N, acc_t>(sbl + c * NN, G);
-    store_acc_rows<N, acc_t>(swt + c * NN, W);
+    ws_store_acc_rows<N>(sbl + c * NN, G);
+    ws_store_acc_rows<N>(swt + c * NN, W);
     fence_release();
     if (l == 0) store_flag(&flags[c], kFlagAgg);
 
@@ -481,9 +539,9 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     vec_t WC = videntity<N>(l);
     G = vzero<N>();
     for (int64_t j = first; j < c; ++j) {
-        load_a_transposed<N, acc_t>(a, swt + j * NN);  // A entries of W_j
+        ws_load_a_transposed<N>(a, swt + j * NN);  // A entries of W_j
         if (later) WC = chain_step<N>(a, WC, vzero<N>());
-        G = chain_step<N>(a, G, load_acc_rows<N, acc_t>(sbl + j * NN));
+        G = chain_step<N>(a, G, ws_load_acc_rows<N>(sbl + j * NN));
     }
 
     // 3. carry = WC Y + BC with Y published by the previous super
@@ -493,12 +551,12 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
         fence_acquire();
         __syncthreads();
         load_a_transposed<N, acc_t>(a, xl);  // A entries of WC
-        G = chain_step<N>(a, load_acc_rows<N, acc_t>(sinc + (first - 1) * NN), G);
+        G = chain_step<N>(a, ws_load_acc_rows<N>(sinc + (first - 1) * NN), G);
     }
     if (r % Z == Z - 1 && r + 1 < nch) {
-        load_a_transposed<N, acc_t>(a, swt + c * NN);
-        const vec_t inc = chain_step<N>(a, G, load_acc_rows<N, acc_t>(sbl + c * NN));
-        store_acc_rows<N, acc_t>(sinc + c * NN, inc);
+        ws_load_a_transposed<N>(a, swt + c * NN);
+        const vec_t inc = chain_step<N>(a, G, ws_load_acc_rows<N>(sbl + c * NN));
+        ws_store_acc_rows<N>(sinc + c * NN, inc);
         fence_release();
         if (l == 0) store_flag(&flags[c], kFlagPrefix);
     }

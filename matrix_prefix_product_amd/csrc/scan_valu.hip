@@ -156,6 +156,38 @@ __device__ inline void add_rows(float (&st)[R][N], const float* src) {
         for (int j = 0; j < N; ++j) st[r][j] += t[r][j];
 }
 
+// Workspace (look-back) accessors, element by element through ws_store /
+// ws_load so that other XCDs see them coherently.
+template <int N, int R>
+__device__ inline void ws_store_rows(float* dst, const float (&st)[R][N]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) ws_store(dst + r * N + j, st[r][j]);
+}
+
+template <int N, int R>
+__device__ inline void ws_load_rows(float (&st)[R][N], const float* src) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] = ws_load(src + r * N + j);
+}
+
+template <int N, int R>
+__device__ inline void ws_add_rows(float (&st)[R][N], const float* src) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] += ws_load(src + r * N + j);
+}
+
+template <int N>
+__device__ inline void ws_load_matrix(float (&m)[N * N], const float* src) {
+#pragma unroll
+    for (int q = 0; q < N * N; ++q) m[q] = ws_load(src + q);
+}
+
 // Staging of one block of TB tokens for every chain of the wave.  Token slot
 // tau of chain ch holds global token  base + pos(tau) + shift, where
 // pos(tau) = blk + tau going forward and len-1-(blk+tau) going backward; it is
@@ -266,7 +298,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
 
     // 1. chunk aggregate
     fwd_sweep<N, R, TB, false>(st, M, P, lds, info, g, li, maxlen, T);
-    store_rows<N, R>(agg + c * V::NN + li * R * N, st);
+    ws_store_rows<N, R>(agg + c * V::NN + li * R * N, st);
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
 
@@ -277,7 +309,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     set_identity_rows<N, R>(lrow, li * R);
     float m[V::NN];
     for (int64_t j = first; j < c; ++j) {
-        load_matrix<N>(m, agg + j * V::NN);
+        ws_load_matrix<N>(m, agg + j * V::NN);
         rows_times<N, R>(lrow, m);
     }
 
@@ -288,7 +320,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
         store_rows<N, R>(xch + g * V::NN + li * R * N, lrow);
         __syncthreads();
         load_matrix<N>(m, xch + g * V::NN);
-        load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
+        ws_load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
         rows_times<N, R>(st, m);
     } else {
 #pragma unroll
@@ -303,9 +335,9 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int q = 0; q < N; ++q) inc[r][q] = st[r][q];
-        load_matrix<N>(m, agg + c * V::NN);
+        ws_load_matrix<N>(m, agg + c * V::NN);
         rows_times<N, R>(inc, m);
-        store_rows<N, R>(incl + c * V::NN + li * R * N, inc);
+        ws_store_rows<N, R>(incl + c * V::NN + li * R * N, inc);
     }
     fence_release();
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
@@ -449,8 +481,8 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
 
     // 1. affine aggregate of the chunk
     bwd_sweep<N, R, TB, false>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
-    store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
-    store_rows<N, R>(swt + c * V::NN + li * R * N, w);
+    ws_store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
+    ws_store_rows<N, R>(swt + c * V::NN + li * R * N, w);
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
 
@@ -462,10 +494,10 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     set_zero_rows<N, R>(bc);
     float m[V::NN];
     for (int64_t j = first; j < c; ++j) {
-        load_matrix<N>(m, swt + j * V::NN);
+        ws_load_matrix<N>(m, swt + j * V::NN);
         if (later_super) rows_times<N, R>(wc, m);
         rows_times<N, R>(bc, m);
-        add_rows<N, R>(bc, sbl + j * V::NN + li * R * N);
+        ws_add_rows<N, R>(bc, sbl + j * V::NN + li * R * N);
     }
 
     // 3. carry = Y Wc^T + Bc with Y the adjoint published by the previous super
@@ -475,7 +507,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
         store_rows<N, R>(qx + g * V::NN + li * R * N, wc);
         __syncthreads();
         load_matrix<N>(m, qx + g * V::NN);
-        load_rows<N, R>(q, sinc + (first - 1) * V::NN + li * R * N);
+        ws_load_rows<N, R>(q, sinc + (first - 1) * V::NN + li * R * N);
         rows_times<N, R>(q, m);
 #pragma unroll
         for (int a = 0; a < R; ++a)
@@ -495,10 +527,10 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
         for (int a = 0; a < R; ++a)
 #pragma unroll
             for (int b = 0; b < N; ++b) inc[a][b] = q[a][b];
-        load_matrix<N>(m, swt + c * V::NN);
+        ws_load_matrix<N>(m, swt + c * V::NN);
         rows_times<N, R>(inc, m);
-        add_rows<N, R>(inc, sbl + c * V::NN + li * R * N);
-        store_rows<N, R>(sinc + c * V::NN + li * R * N, inc);
+        ws_add_rows<N, R>(inc, sbl + c * V::NN + li * R * N);
+        ws_store_rows<N, R>(sinc + c * V::NN + li * R * N, inc);
     }
     fence_release();
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
@@ -529,11 +561,20 @@ hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, i
 
 }  // namespace
 
-// Row split and staging depth per n (rows per lane R, tokens per staged block TB).
+// Row split and staging depth per n: (n, rows per lane R, tokens per staged
+// block TB).  Overridable at build time for tuning sweeps.
+#ifndef MRU_VALU_CFG4
 #define MRU_VALU_CFG4 4, 1, 8
-#define MRU_VALU_CFG8 8, 2, 4
+#endif
+#ifndef MRU_VALU_CFG8
+#define MRU_VALU_CFG8 8, 1, 4
+#endif
+#ifndef MRU_VALU_BWD_CFG4
 #define MRU_VALU_BWD_CFG4 4, 1, 4
-#define MRU_VALU_BWD_CFG8 8, 2, 2
+#endif
+#ifndef MRU_VALU_BWD_CFG8
+#define MRU_VALU_BWD_CFG8 8, 1, 4
+#endif
 
 int valu_chains_per_wave(int n, int dir) {
     if (n == 4) return dir == 0 ? Valu<MRU_VALU_CFG4>::G : Valu<MRU_VALU_BWD_CFG4>::G;
