@@ -91,14 +91,11 @@ def time_cpu_baseline(w, budget_s: float):
 
     with threadpool_limits(limits=1):
         T = min(w.T, 4096)
-        b_rows, h_rows = [0], [0]
-        dt = run(b_rows, h_rows, T)
-        # grow the sample (more sequences) toward the time budget
-        seqs = max(1, min(w.B * w.H, int(budget_s / max(dt, 1e-4) * 0.8)))
-        nb = max(1, min(w.B, seqs // w.H)) if seqs >= w.H else 1
-        nh = w.H if seqs >= w.H else seqs
-        b_rows, h_rows = list(range(nb)), list(range(nh))
-        dt = run(b_rows, h_rows, T)
+        dt1 = run([0], [0], T)  # one sequence, to size the sample
+        seqs = max(1, min(w.B * w.H, int(budget_s / max(dt1, 1e-4))))
+        nh = min(w.H, seqs)
+        nb = max(1, min(w.B, seqs // nh))
+        dt = run(list(range(nb)), list(range(nh)), T)
     head_tokens = nb * nh * T
     tokens = head_tokens / w.H
     return {
@@ -153,7 +150,7 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
     # chunks that need a carry (all but the first chunk of a sequence)
     prod = S * T * (2.0 if nch > 1 else 1.0) - (S * K if nch > 1 else 0)
     impl_flops = prod * 2 * n ** 3
-    peak = FP64_PEAK_TFLOPS if n == 16 else FP32_PEAK_TFLOPS
+    peak = FP64_PEAK_TFLOPS  # n = 16 and 32 keep an fp64 running state
     del M, P, ws
     torch.cuda.empty_cache()
     return {
@@ -168,6 +165,33 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
         "matrix_util": round(impl_flops / (med * 1e-3) / 1e12 / peak, 4),
         "data": "synthetic, seeded on the GPU (torch.Generator), same scales as the workload",
     }
+
+
+def copy_reference(torch, gib: int = 1, reps: int = 10):
+    """A plain device-to-device copy of known size on the same GPU: the practical
+    streaming bandwidth this machine reaches, and the known-size kernel that scales
+    the HBM traffic counters."""
+    n = gib * (2 ** 30) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        b.copy_(a)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    med = t[len(t) // 2]
+    del a, b
+    torch.cuda.empty_cache()
+    moved = 2 * gib * 2 ** 30
+    return {"bytes_per_launch": moved, "median_us": round(med * 1e3, 1),
+            "GBs": round(moved / (med * 1e-3) / 1e9, 1),
+            "frac_hbm": round(moved / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "torch copy_ of a 1 GiB fp32 tensor"}
 
 
 def main():
@@ -284,6 +308,7 @@ def main():
     }
     del x, R, M, P, dM, ws_f, ws_b
     torch.cuda.empty_cache()
+    out["copy_reference"] = copy_reference(torch)
 
     if not args.no_extra:
         c3, c4 = WORKLOADS["c3"], WORKLOADS["c4"]
