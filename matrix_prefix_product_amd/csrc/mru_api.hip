@@ -66,6 +66,9 @@ int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir) {
     const int64_t nch = (target + S - 1) / S;
     int64_t K = (T + nch - 1) / nch;
     if (K < 16) K = 16;
+    // a forward chunk that fits the register buffer reads its inputs once
+    const int64_t keep = dir == 0 ? mfma_retain_tokens(n) : 0;
+    if (keep > 0 && K > keep) K = keep;
     return K < T ? K : T;
 }
 

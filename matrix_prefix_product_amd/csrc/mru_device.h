@@ -127,6 +127,17 @@ __device__ inline void fence_acquire() {
 #endif
 }
 
+// Ticket order of a multi-chunk scan: ticket t takes chunk group t / S of
+// sequence t % S, i.e. sequences are interleaved.  Chunks that run at the same
+// time then come from many sequences, and every chunk's predecessors were handed
+// out at least S tickets earlier, which keeps the carry chains short.  A chunk
+// only ever waits on earlier chunks of its own sequence, which have smaller
+// tickets.  Returns the first chunk index of the group (groups of G chunks).
+__device__ inline int64_t ticket_to_chunk(int64_t t, int64_t S, int64_t groups_per_seq, int G) {
+    const int64_t s = t % S;
+    return (s * groups_per_seq + t / S) * G;
+}
+
 // One ticket per wave, taken by lane 0 and broadcast.
 __device__ inline uint32_t wave_ticket(uint32_t* counter) {
     uint32_t t = 0;

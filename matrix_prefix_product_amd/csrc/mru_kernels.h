@@ -25,6 +25,10 @@ hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, floa
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
                            hipStream_t stream);
 
+// Tokens per chunk the matrix-core forward kernel keeps in registers between
+// its two passes (0 = none): chunks of at most this length read M once.
+int mfma_retain_tokens(int n);
+
 // Chains per wave of the vector-ALU kernels (n = 4, 8) for direction dir.
 int valu_chains_per_wave(int n, int dir);
 

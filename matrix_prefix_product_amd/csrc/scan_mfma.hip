@@ -237,6 +237,10 @@ __device__ inline Chunk chunk_at(int64_t c, int64_t nch, int64_t K, int64_t T, b
     return ch;
 }
 
+// Aggregates fetched per batch in the look-back walk (bounded by registers).
+template <int N, bool BWD>
+constexpr int walk_depth() { return N == 16 ? 4 : (BWD ? 1 : 2); }
+
 // ---------------------------------------------------------------------------- forward
 
 // The operand ring: the loads for token t + PF are issued right after token t's
@@ -291,7 +295,68 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
         if (t0 + p < len) step(p, t0 + p, false);
 }
 
-template <int N, int PF>
+// Retained chunk (KR > 0): the aggregate pass loads the chunk's A-operand
+// entries into a register buffer of KR tokens (loads issued PF tokens ahead,
+// clamped into the chunk) and the apply pass reuses them, so each input matrix
+// is read from HBM once even when the chunk needs a carry.
+template <int N, int KR, int PF>
+__device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, const float* __restrict__ M,
+                                int64_t base, int len, float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
+    using F = Mf<N>;
+    constexpr int NT = F::NT;
+    constexpr int NN = F::NN;
+    constexpr int NA = NT * NT * 4;
+    const int l = threadIdx.x & 63;
+    int aoff[NA];
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int K = 0; K < NT; ++K)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                aoff[(I * NT + K) * 4 + b] = (16 * K + trow(l, b)) * N + 16 * I + tacol(l);
+    const float* Mb = M + base * NN;
+#pragma unroll
+    for (int p = 0; p < PF && p < KR; ++p) {
+        const int u = min(p, len - 1);
+#pragma unroll
+        for (int e = 0; e < NA; ++e) buf[p][e] = Mb[u * NN + aoff[e]];
+    }
+#pragma unroll
+    for (int t = 0; t < KR; ++t) {
+        if (t + PF < KR) {
+            const int u = min(t + PF, len - 1);
+#pragma unroll
+            for (int e = 0; e < NA; ++e) buf[t + PF][e] = Mb[u * NN + aoff[e]];
+        }
+        if (t < len) {
+            typename F::aop_t a;
+#pragma unroll
+            for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(buf[t][e]);
+            X = chain_step<N>(a, X, vzero<N>());
+        }
+    }
+}
+
+template <int N, int KR>
+__device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, float* __restrict__ P, int64_t base,
+                                 int len, const float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
+    using F = Mf<N>;
+    constexpr int NT = F::NT;
+    constexpr int NA = NT * NT * 4;
+#pragma unroll
+    for (int t = 0; t < KR; ++t) {
+        if (t < len) {
+            typename F::aop_t a;
+#pragma unroll
+            for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(buf[t][e]);
+            X = chain_step<N>(a, X, vzero<N>());
+            store_acc_rows<N, float>(P + (base + t) * F::NN, X);
+        }
+    }
+}
+
+template <int N, int PF, int KR>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
@@ -305,7 +370,8 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    const int64_t cidx = multi ? int64_t(wave_ticket(&hdr->ticket)) : int64_t(blockIdx.x);
+    const int64_t cidx =
+        multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
     const Chunk ch = chunk_at(cidx, nch, K, T, false);
 
@@ -323,7 +389,11 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     const int64_t first = c - k % Z;
 
     // 1. chunk aggregate
-    fwd_sweep<N, PF, false>(X, M, P, ch.base, ch.len);
+    float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
+    if constexpr (KR > 0)
+        fwd_pass_retain<N, KR, PF>(X, M, ch.base, ch.len, buf);
+    else
+        fwd_sweep<N, PF, false>(X, M, P, ch.base, ch.len);
     ws_store_acc_rows<N>(agg + c * NN, X);
     fence_release();
     if (l == 0) store_flag(&flags[c], kFlagAgg);
@@ -333,9 +403,16 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     fence_acquire();
     typename F::aop_t a;
     X = videntity<N>(l);
-    for (int64_t j = first; j < c; ++j) {
-        ws_load_a_transposed<N>(a, agg + j * NN);
-        X = chain_step<N>(a, X, vzero<N>());
+    // aggregates are loaded kWalk at a time so their loads are in flight together
+    constexpr int kWalk = walk_depth<N, false>();
+    for (int64_t j0 = first; j0 < c; j0 += kWalk) {
+        typename F::aop_t w[kWalk];
+#pragma unroll
+        for (int d = 0; d < kWalk; ++d)
+            if (j0 + d < c) ws_load_a_transposed<N>(w[d], agg + (j0 + d) * NN);
+#pragma unroll
+        for (int d = 0; d < kWalk; ++d)
+            if (j0 + d < c) X = chain_step<N>(w[d], X, vzero<N>());
     }
 
     // 3. carry^T = Lt * prefix^T, prefix from the previous super's last chunk
@@ -356,7 +433,10 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     }
 
     // 4. re-run from the carry
-    fwd_sweep<N, PF, true>(X, M, P, ch.base, ch.len);
+    if constexpr (KR > 0)
+        fwd_apply_retain<N, KR>(X, P, ch.base, ch.len, buf);
+    else
+        fwd_sweep<N, PF, true>(X, M, P, ch.base, ch.len);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -502,7 +582,8 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    const int64_t cidx = multi ? int64_t(wave_ticket(&hdr->ticket)) : int64_t(blockIdx.x);
+    const int64_t cidx =
+        multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
     const Chunk ch = chunk_at(cidx, nch, K, T, true);
 
@@ -538,10 +619,22 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     typename F::aop_t a;
     vec_t WC = videntity<N>(l);
     G = vzero<N>();
-    for (int64_t j = first; j < c; ++j) {
-        ws_load_a_transposed<N>(a, swt + j * NN);  // A entries of W_j
-        if (later) WC = chain_step<N>(a, WC, vzero<N>());
-        G = chain_step<N>(a, G, ws_load_acc_rows<N>(sbl + j * NN));
+    constexpr int kWalk = walk_depth<N, true>();
+    for (int64_t j0 = first; j0 < c; j0 += kWalk) {
+        typename F::aop_t w[kWalk];
+        vec_t bl[kWalk];
+#pragma unroll
+        for (int d = 0; d < kWalk; ++d)
+            if (j0 + d < c) {
+                ws_load_a_transposed<N>(w[d], swt + (j0 + d) * NN);  // A entries of W_j
+                bl[d] = ws_load_acc_rows<N>(sbl + (j0 + d) * NN);
+            }
+#pragma unroll
+        for (int d = 0; d < kWalk; ++d)
+            if (j0 + d < c) {
+                if (later) WC = chain_step<N>(w[d], WC, vzero<N>());
+                G = chain_step<N>(w[d], G, bl[d]);
+            }
     }
 
     // 3. carry = WC Y + BC with Y published by the previous super
@@ -565,11 +658,11 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T);
 }
 
-template <int N, int PF>
+template <int N, int PF, int KR>
 hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
                    int64_t Z, void* ws, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_mfma_kernel<N, PF>), dim3(unsigned(S * nch)), dim3(64), 0, stream, M,
-                       P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+    hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR>), dim3(unsigned(S * nch)), dim3(64), 0, stream,
+                       M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
     return hipGetLastError();
 }
 
@@ -583,10 +676,21 @@ hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, i
 
 }  // namespace
 
+#ifndef MRU_RETAIN16
+#define MRU_RETAIN16 64
+#endif
+// Tokens of one chunk kept in registers by the n = 16 forward kernel.
+constexpr int kRetain16 = MRU_RETAIN16;
+
+int mfma_retain_tokens(int n) { return n == 16 ? kRetain16 : 0; }
+
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
                            int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
-    if (n == 16) return run_fwd<16, 16>(M, P, S, T, K, nch, Z, ws, stream);
-    if (n == 32) return run_fwd<32, 4>(M, P, S, T, K, nch, Z, ws, stream);
+    if (n == 16) {
+        if (nch > 1 && K <= kRetain16) return run_fwd<16, 16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream);
+        return run_fwd<16, 16, 0>(M, P, S, T, K, nch, Z, ws, stream);
+    }
+    if (n == 32) return run_fwd<32, 4, 0>(M, P, S, T, K, nch, Z, ws, stream);
     return hipErrorInvalidValue;
 }
 

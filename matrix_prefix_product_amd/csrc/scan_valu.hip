@@ -270,8 +270,9 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    const int64_t wave_id = multi ? int64_t(wave_ticket(&hdr->ticket)) : int64_t(blockIdx.x);
-    const int64_t cbase = wave_id * V::G;
+    const int64_t cbase =
+        multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch / V::G, V::G)
+              : int64_t(blockIdx.x) * V::G;
     if (lane < V::G) info[lane] = make_chain(cbase + lane, nchunks, nch, K, T, false);
     __syncthreads();
     int maxlen = 0;
@@ -450,8 +451,9 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    const int64_t wave_id = multi ? int64_t(wave_ticket(&hdr->ticket)) : int64_t(blockIdx.x);
-    const int64_t cbase = wave_id * V::G;
+    const int64_t cbase =
+        multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch / V::G, V::G)
+              : int64_t(blockIdx.x) * V::G;
     if (lane < V::G) info[lane] = make_chain(cbase + lane, nchunks, nch, K, T, true);
     __syncthreads();
     int maxlen = 0;
