@@ -6,6 +6,7 @@ by the product path.  See ``mru_oracle`` for the definitions and citations.
 from .mru_oracle import (  # noqa: F401
     FP32_DOMAIN_LIMIT,
     build_ref,
+    build_vjp_ref,
     bwd_ref,
     flatten_ref,
     loss_ref,

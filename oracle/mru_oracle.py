@@ -32,7 +32,8 @@ Readings taken where the pages are silent:
 * Flattening is the row-major reshape of P_t to an n*n vector, per head.
 * The backward pass is the vector-Jacobian product of L = sum_t <R_t, P_t>_F
   with respect to every M_t (the pages describe training through the product
-  but give no formula; the chain rule fixes it).
+  but give no formula; the chain rule fixes it), and build_vjp_ref carries a
+  gradient dL/dM back to the raw token vectors.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 against closed forms, library routines, brute force, finite differences and
@@ -43,7 +44,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "build_ref", "scan_ref", "bwd_ref", "flatten_ref", "loss_ref",
+    "build_ref", "build_vjp_ref", "scan_ref", "bwd_ref", "flatten_ref", "loss_ref",
     "rel_fro_err", "representable", "FP32_DOMAIN_LIMIT",
 ]
 
@@ -80,6 +81,39 @@ def build_ref(x: np.ndarray, n: int) -> np.ndarray:
     det = np.linalg.det(LDU)
     c = np.abs(det) ** (-1.0 / n)
     return c[..., None, None] * LDU
+
+
+def build_vjp_ref(x: np.ndarray, dM: np.ndarray, n: int) -> np.ndarray:
+    """Gradient with respect to the raw token vector x of <dM, build_ref(x)>.
+
+    ``x``: ``[..., n*n]``; ``dM``: ``[..., n, n]``; returns float64 ``[..., n*n]``.
+
+    Training through the input construction ("Improving Matrix Recurrent Units
+    as an Attention Alternative", Key Points: LDU fill, determinant-correcting
+    scalar) needs this step; the pages give no formula, the chain rule fixes it.
+    With det L = det U = 1 the scalar is c = exp(-mean_k X_kk), so
+    M = L diag(e) U with e_k = exp(X_kk - mean X_jj).  For G = dM:
+      through L:  G (diag(e) U)^T, kept on the strictly lower part of X;
+      through U:  (L diag(e))^T G, kept on the strictly upper part;
+      through e:  g_k = (L^T G U^T)_kk, and X_kk enters every e_j via the mean,
+                  so dX_kk = e_k g_k - mean_j(e_j g_j).
+    """
+    X = _as_matrices(x, n)
+    G = np.asarray(dM, dtype=np.float64)
+    eye = np.eye(n)
+    L = np.tril(X, -1) + eye
+    U = np.triu(X, 1) + eye
+    d = np.diagonal(X, axis1=-2, axis2=-1)
+    e = np.exp(d - d.mean(axis=-1, keepdims=True))
+    DU = e[..., :, None] * U                      # diag(e) U
+    LD = L * e[..., None, :]                      # L diag(e)
+    gL = G @ np.swapaxes(DU, -1, -2)
+    gU = np.swapaxes(LD, -1, -2) @ G
+    g = np.diagonal(np.swapaxes(L, -1, -2) @ G @ np.swapaxes(U, -1, -2), axis1=-2, axis2=-1)
+    eg = e * g
+    dX = np.tril(gL, -1) + np.triu(gU, 1)
+    dX = dX + (eg - eg.mean(axis=-1, keepdims=True))[..., :, None] * eye
+    return dX.reshape(*dX.shape[:-2], n * n)
 
 
 def scan_ref(M: np.ndarray) -> np.ndarray:

@@ -376,3 +376,66 @@ def test_golden_c1_head_regression():
     assert np.array_equal(x.astype(np.float64), g["x"])
     np.testing.assert_allclose(build_ref(x, w.n), g["M"], rtol=1e-15, atol=1e-15)
     np.testing.assert_allclose(scan_ref(g["M"].astype(np.float32)), g["P"], rtol=1e-15, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- build backward
+
+from oracle import build_vjp_ref  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_build_vjp_finite_differences(n):
+    x = RNG.normal(0, 0.4, size=(3, n * n))
+    G = RNG.normal(size=(3, n, n))
+    g = build_vjp_ref(x, G, n)
+    h = 1e-6
+    fd = np.empty_like(x)
+    for idx in np.ndindex(x.shape):
+        xp = x.copy(); xp[idx] += h
+        xm = x.copy(); xm[idx] -= h
+        fd[idx] = (np.sum(G * build_ref(xp, n)) - np.sum(G * build_ref(xm, n))) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=0, atol=2e-8)
+
+
+def test_build_vjp_torch_autograd():
+    # an independent torch implementation of the construction, determinant included
+    torch = pytest.importorskip("torch")
+    n = 5
+    x = RNG.normal(0, 0.3, size=(4, n * n))
+    G = RNG.normal(size=(4, n, n))
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    X = xt.reshape(4, n, n)
+    eye = torch.eye(n, dtype=torch.float64)
+    L = torch.tril(X, -1) + eye
+    U = torch.triu(X, 1) + eye
+    D = torch.diag_embed(torch.exp(torch.diagonal(X, dim1=-2, dim2=-1)))
+    LDU = L @ D @ U
+    c = torch.abs(torch.linalg.det(LDU)) ** (-1.0 / n)
+    M = c[:, None, None] * LDU
+    (M * torch.tensor(G)).sum().backward()
+    np.testing.assert_allclose(build_vjp_ref(x, G, n), xt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_build_vjp_at_zero_closed_form(n):
+    # X = 0: L = U = I, e = 1, so dX = offdiag(G) + diag(G_kk - mean G_jj)
+    G = RNG.normal(size=(n, n))
+    dx = build_vjp_ref(np.zeros(n * n), G, n).reshape(n, n)
+    expect = G - np.diag(np.diag(G)) + np.diag(np.diag(G) - np.diag(G).mean())
+    np.testing.assert_allclose(dx, expect, rtol=0, atol=1e-15)
+    assert abs(np.trace(dx)) < 1e-14       # the det correction removes the trace direction
+
+
+def test_training_gradient_chain():
+    # d/dx of sum_t <R_t, P_t(build(x))> by finite differences = build_vjp(bwd_ref)
+    n, T = 3, 4
+    x = RNG.normal(0, 0.3, size=(T, n * n))
+    R = RNG.normal(size=(T, n, n))
+    g = build_vjp_ref(x, bwd_ref(build_ref(x, n), R), n)
+    h = 1e-6
+    fd = np.empty_like(x)
+    for idx in np.ndindex(x.shape):
+        xp = x.copy(); xp[idx] += h
+        xm = x.copy(); xm[idx] -= h
+        fd[idx] = (loss_ref(scan_ref(build_ref(xp, n)), R) - loss_ref(scan_ref(build_ref(xm, n)), R)) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=0, atol=5e-8)
