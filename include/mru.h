@@ -89,6 +89,20 @@ mru_status mru_build_inputs(const float* x, float* M, int64_t B, int64_t H, int6
                             int32_t n, void* stream);
 
 /*
+ * Gradient through the input construction: dx = d<dM, build(x)>/dx, i.e. the
+ * vector-Jacobian product of mru_build_inputs.  Source of the construction:
+ * "Improving Matrix Recurrent Units as an Attention Alternative", Key Points;
+ * the pages train through it but give no formula (this is the exact gradient,
+ * including the scalar's dependence on the diagonal: dx has zero trace).
+ *
+ * x   [B][H][T][n*n] fp32, read (the forward's raw token vectors).
+ * dM  [B][H][T][n][n] fp32, read (e.g. the output of mru_scan_bwd).
+ * dx  [B][H][T][n*n] fp32, written.  dx must not overlap x or dM.
+ */
+mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int64_t B, int64_t H,
+                                int64_t T, int32_t n, void* stream);
+
+/*
  * Chunk length (tokens per scan chunk) that chunk = 0 resolves to for this
  * shape and direction; a pure function of its arguments.  Returns 0 for an
  * invalid shape.

@@ -9,10 +9,12 @@ pointers and the current stream to the C ABI declared in include/mru.h.
 
 Functions (tensors are contiguous fp32 on a ROCm device):
     build_inputs(x, n)        x [B,H,T,n*n] -> M [B,H,T,n,n]
+    build_inputs_bwd(x, dM)   gradient through the build: dx [B,H,T,n*n]
     scan_fwd(M, chunk=0)      M -> P, P_t = M_1 ... M_t
     scan_bwd(M, P, dP)        -> dM, gradient of sum_t <dP_t, P_t>
     flatten(P)                P [B,H,T,n,n] -> [B,H,T,n*n] (a view)
     mru_scan(M)               scan_fwd with autograd (backward = scan_bwd)
+    mru_layer(x, n)           build + scan with autograd down to the token vectors
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import os
 import torch
 
 __all__ = [
-    "build_inputs", "scan_fwd", "scan_bwd", "flatten", "mru_scan", "MRUScan",
+    "build_inputs", "build_inputs_bwd", "scan_fwd", "mru_layer", "MRUBuild", "scan_bwd", "flatten", "mru_scan", "MRUScan",
     "scan_plan", "scan_chunk", "workspace_bytes", "library_path", "load_library",
     "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N",
 ]
@@ -69,6 +71,8 @@ def load_library():
     lib.mru_status_string.argtypes = [i32]
     lib.mru_build_inputs.restype = i32
     lib.mru_build_inputs.argtypes = [vp, vp, i64, i64, i64, i32, vp]
+    lib.mru_build_inputs_bwd.restype = i32
+    lib.mru_build_inputs_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
     lib.mru_scan_chunk.restype = i32
     lib.mru_scan_chunk.argtypes = [i64, i64, i64, i32, i32]
     lib.mru_scan_plan.restype = i32
@@ -171,6 +175,25 @@ def build_inputs(x: torch.Tensor, n: int, out: torch.Tensor | None = None) -> to
     return M
 
 
+def build_inputs_bwd(x: torch.Tensor, dM: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient through the LDU build: dx [B,H,T,n*n] from x and dM = dL/dM [B,H,T,n,n]."""
+    _require(x, "x", 4)
+    B, H, T, n = _mshape(dM, "dM")
+    if tuple(x.shape) != (B, H, T, n * n) or x.device != dM.device:
+        raise ValueError("x must be [B,H,T,n*n] matching dM on the same device")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _require(out, "out", 4)
+        if out.shape != x.shape or out.device != x.device:
+            raise ValueError("out must match x")
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.mru_build_inputs_bwd(_ptr(x), _ptr(dM), _ptr(out), B, H, T, n, _stream_handle(x.device))
+    _check(st, "mru_build_inputs_bwd")
+    return out
+
+
 def scan_fwd(M: torch.Tensor, chunk: int = 0, out: torch.Tensor | None = None,
              workspace: torch.Tensor | None = None) -> torch.Tensor:
     """All prefix products P_t = M_1 ... M_t (P_0 = I), [B,H,T,n,n]."""
@@ -237,3 +260,24 @@ class MRUScan(torch.autograd.Function):
 
 def mru_scan(M: torch.Tensor, chunk: int = 0) -> torch.Tensor:
     return MRUScan.apply(M, chunk)
+
+
+class MRUBuild(torch.autograd.Function):
+    """M = build_inputs(x, n) with the exact VJP from build_inputs_bwd."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, n: int):
+        x = x.contiguous()
+        ctx.save_for_backward(x)
+        return build_inputs(x, n)
+
+    @staticmethod
+    def backward(ctx, dM: torch.Tensor):
+        (x,) = ctx.saved_tensors
+        return build_inputs_bwd(x, dM.contiguous()), None
+
+
+def mru_layer(x: torch.Tensor, n: int, chunk: int = 0) -> torch.Tensor:
+    """The MRU token mixer up to the output state matrices: x [B,H,T,n*n] ->
+    P [B,H,T,n,n] (flatten() gives the output vectors), differentiable in x."""
+    return MRUScan.apply(MRUBuild.apply(x, n), chunk)

@@ -106,6 +106,129 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(const float* __res
     }
 }
 
+// Gradient through the LDU build (training through the input construction).
+// For G = dL/dM, e_k = exp(X_kk - mean X) and H = G U^T:
+//   dX_ij = e_j H_ij                     (i > j, through L)
+//   dX_ij = e_i (L^T G)_ij               (i < j, through U)
+//   dX_kk = e_k g_k - mean_j e_j g_j     (through e; X_kk also enters the mean)
+// with g_k = (L^T G U^T)_kk = sum_r L_rk H_rk.  One lane per row of dX; the
+// column sums for g go through LDS.
+template <int N>
+__global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* __restrict__ x,
+                                                                  const float* __restrict__ dM,
+                                                                  float* __restrict__ dx,
+                                                                  int64_t ntok) {
+    constexpr int NN = N * N;
+    constexpr int TPI = kBuildThreads / N;  // tokens per block iteration
+    constexpr int XS = NN + 4;
+    __shared__ float sx[TPI * XS];
+    __shared__ float sg[TPI * XS];
+    __shared__ float sc[TPI * XS];
+    __shared__ float se[TPI * N];
+    __shared__ float seg[TPI * N];
+    const int tid = threadIdx.x;
+    const int tk = tid / N;
+    const int i = tid % N;  // row of dX owned by this lane
+    const float* xt = sx + tk * XS;
+    const float* gt = sg + tk * XS;
+    float* ct = sc + tk * XS;
+    for (int64_t tok0 = int64_t(blockIdx.x) * TPI; tok0 < ntok; tok0 += int64_t(gridDim.x) * TPI) {
+        __syncthreads();
+        for (int f = tid; f < TPI * NN / 4; f += kBuildThreads) {
+            const int t = f / (NN / 4);
+            const int q = f % (NN / 4);
+            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f), vg = vx;
+            if (tok0 + t < ntok) {
+                vx = reinterpret_cast<const float4*>(x + (tok0 + t) * NN)[q];
+                vg = reinterpret_cast<const float4*>(dM + (tok0 + t) * NN)[q];
+            }
+            *reinterpret_cast<float4*>(sx + t * XS + 4 * q) = vx;
+            *reinterpret_cast<float4*>(sg + t * XS + 4 * q) = vg;
+        }
+        __syncthreads();
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) sum += xt[k * N + k];
+        const float mean = sum * (1.0f / N);
+        se[tk * N + i] = expf(xt[i * N + i] - mean);
+        __syncthreads();
+        // H row i: H_ij = sum_{m >= j} G_im U_jm (U_jj = 1)
+        float h[N];
+        if constexpr (N <= 8) {
+            float grow[N];
+#pragma unroll
+            for (int m = 0; m < N; ++m) grow[m] = gt[i * N + m];
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                float acc = grow[j];
+#pragma unroll
+                for (int m = j + 1; m < N; ++m) acc = fmaf(grow[m], xt[j * N + m], acc);
+                h[j] = acc;
+            }
+        } else {
+            // m loop kept rolled (register pressure); U's zeros are masked
+#pragma unroll
+            for (int j = 0; j < N; ++j) h[j] = 0.f;
+#pragma unroll 2
+            for (int m = 0; m < N; ++m) {
+                const float gm = gt[i * N + m];
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    const float ujm = (m > j) ? xt[j * N + m] : ((m == j) ? 1.f : 0.f);
+                    h[j] = fmaf(gm, ujm, h[j]);
+                }
+            }
+        }
+        // row i's terms of g_k = sum_r L_rk H_rk (L_ik = X_ik for k < i, L_ii = 1)
+#pragma unroll
+        for (int k = 0; k < N; ++k) ct[i * N + k] = (k < i) ? xt[i * N + k] * h[k] : ((k == i) ? h[k] : 0.f);
+        // (L^T G) row i: sum_{m >= i} L_mi G_mj
+        float u[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) u[j] = 0.f;
+#pragma unroll(N <= 8 ? N : 2)
+        for (int m = 0; m < N; ++m) {
+            const float coef = (m > i) ? xt[m * N + i] : ((m == i) ? 1.f : 0.f);
+#pragma unroll
+            for (int j = 0; j < N; ++j) u[j] = fmaf(coef, gt[m * N + j], u[j]);
+        }
+        const float ei = se[tk * N + i];
+        float out[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) out[j] = (j < i) ? se[tk * N + j] * h[j] : ((j > i) ? ei * u[j] : 0.f);
+        __syncthreads();
+        float gi = 0.f;
+#pragma unroll
+        for (int r = 0; r < N; ++r) gi += ct[r * N + i];
+        seg[tk * N + i] = ei * gi;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) tot += seg[tk * N + k];
+        const float meaneg = tot * (1.0f / N);
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            if (j == i) out[j] = seg[tk * N + i] - meaneg;
+        const int64_t tok = tok0 + tk;
+        if (tok < ntok) {
+            float* dst = dx + tok * NN + i * N;
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q)
+                reinterpret_cast<float4*>(dst)[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+        }
+    }
+}
+
+template <int N>
+hipError_t run_build_bwd(const float* x, const float* dM, float* dx, int64_t ntok, hipStream_t stream) {
+    constexpr int TPI = kBuildThreads / N;
+    int64_t blocks = (ntok + TPI - 1) / TPI;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    hipLaunchKernelGGL((build_bwd_kernel<N>), dim3(unsigned(blocks)), dim3(kBuildThreads), 0, stream,
+                       x, dM, dx, ntok);
+    return hipGetLastError();
+}
+
 template <int N, int R>
 hipError_t run_build(const float* x, float* M, int64_t ntok, hipStream_t stream) {
     constexpr int TPI = kBuildThreads / (N / R);
@@ -138,6 +261,17 @@ hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream
         case 8: return run_build<8, MRU_BUILD_R8>(x, M, ntok, stream);
         case 16: return run_build<16, MRU_BUILD_R16>(x, M, ntok, stream);
         case 32: return run_build<32, MRU_BUILD_R32>(x, M, ntok, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_build_bwd(const float* x, const float* dM, float* dx, int64_t ntok, int n,
+                            hipStream_t stream) {
+    switch (n) {
+        case 4: return run_build_bwd<4>(x, dM, dx, ntok, stream);
+        case 8: return run_build_bwd<8>(x, dM, dx, ntok, stream);
+        case 16: return run_build_bwd<16>(x, dM, dx, ntok, stream);
+        case 32: return run_build_bwd<32>(x, dM, dx, ntok, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -163,6 +163,19 @@ mru_status mru_build_inputs(const float* x, float* M, int64_t B, int64_t H, int6
     return launched(launch_build(x, M, S * T, n, static_cast<hipStream_t>(stream)));
 }
 
+mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int64_t B, int64_t H,
+                                int64_t T, int32_t n, void* stream) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (elems == 0) return MRU_OK;
+    if (!x || !dM || !dx) return MRU_ERR_NULL;
+    if (!aligned16(x) || !aligned16(dM) || !aligned16(dx)) return MRU_ERR_ALIGN;
+    const size_t bytes = size_t(elems) * sizeof(float);
+    if (overlap(dx, bytes, x, bytes) || overlap(dx, bytes, dM, bytes)) return MRU_ERR_ALIAS;
+    (void)hipGetLastError();
+    return launched(launch_build_bwd(x, dM, dx, S * T, n, static_cast<hipStream_t>(stream)));
+}
+
 int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems) || elems == 0) return 0;

@@ -10,6 +10,9 @@ namespace mru {
 
 // LDU fill + determinant correction for ntok = B*H*T token matrices.
 hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream);
+// Its gradient: dx from x and dL/dM.
+hipError_t launch_build_bwd(const float* x, const float* dM, float* dx, int64_t ntok, int n,
+                            hipStream_t stream);
 
 // Chunked scans over S sequences of T tokens: chunk length K, nch chunks per
 // sequence (possibly padded with empty chunks), supers of Z chunks.  nch == 1

@@ -32,7 +32,8 @@ def mpp():
 
 def test_header_declares_the_boundary():
     names = set(_declared_functions())
-    assert {"mru_build_inputs", "mru_scan_fwd", "mru_scan_bwd", "mru_scan_workspace_bytes",
+    assert {"mru_build_inputs", "mru_build_inputs_bwd", "mru_scan_fwd", "mru_scan_bwd",
+            "mru_scan_workspace_bytes",
             "mru_scan_chunk", "mru_scan_plan", "mru_status_string", "mru_abi_version"} <= names
 
 
@@ -115,3 +116,9 @@ def test_validation_before_any_launch(mpp):
     assert lib.mru_scan_fwd(a, b, 1, 1, 1024, 4, 0, ctypes.c_void_p(0x200000 + 64), need, nul) == 4
     # dM aliasing dP
     assert lib.mru_scan_bwd(a, b, ws, ws, 1, 1, 8, 8, 1, nul, 0, nul) == 4
+    # build gradient: shape, null, alias, empty
+    assert lib.mru_build_inputs_bwd(a, b, ws, 1, 1, 4, 5, nul) == 2
+    assert lib.mru_build_inputs_bwd(a, nul, ws, 1, 1, 4, 8, nul) == 1
+    assert lib.mru_build_inputs_bwd(a, b, a, 1, 1, 4, 8, nul) == 4
+    assert lib.mru_build_inputs_bwd(odd, b, ws, 1, 1, 4, 8, nul) == 3
+    assert lib.mru_build_inputs_bwd(nul, nul, nul, 0, 1, 4, 8, nul) == 0

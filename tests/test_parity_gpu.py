@@ -290,3 +290,56 @@ def test_binding_errors(mpp):
     with pytest.raises(mpp.MRUError) as e:
         mpp.scan_fwd(M, out=M)
     assert e.value.status == 4
+
+
+# ----------------------------------------------------------------------------- build backward
+
+from oracle import build_vjp_ref  # noqa: E402
+
+BUILD_BWD_TOL = 2e-6  # fp32 sums of <= 2n products per entry (bound ~(2n+3) eps); measured worst 1.6e-7
+
+
+@pytest.mark.parametrize("n", [4, 8, 16, 32])
+def test_build_bwd_parity(mpp, n):
+    say(f"[build bwd] n={n}")
+    so, sd = SIGMA[n]
+    for scale in (1.0, 5.0):
+        x = gen_x(2, 3, 77, n, so * scale, sd * scale, seed=13)
+        G = gen_R(2, 3, 77, n, seed=14)
+        dx = host(mpp.build_inputs_bwd(dev(x), dev(G)))
+        ref = build_vjp_ref(x, G, n)
+        err = rel_fro_err(dx.reshape(*dx.shape[:-1], n, n), ref.reshape(*ref.shape[:-1], n, n))
+        say(f"  scale {scale}: max rel err {err.max():.3e}")
+        assert err.max() <= BUILD_BWD_TOL
+        # the determinant correction makes every dx traceless
+        tr = np.trace(dx.reshape(-1, n, n), axis1=1, axis2=2)
+        assert np.abs(tr).max() <= 1e-5 * np.abs(dx).max()
+
+
+@pytest.mark.parametrize("n", [4, 8, 16, 32])
+def test_build_bwd_at_zero(mpp, n):
+    G = gen_R(1, 1, 5, n, seed=n)
+    dx = host(mpp.build_inputs_bwd(torch.zeros(1, 1, 5, n * n, device="cuda"), dev(G)))
+    for t in range(5):
+        g = G[0, 0, t].astype(np.float64)
+        expect = g - np.diag(np.diag(g)) + np.diag(np.diag(g) - np.diag(g).mean())
+        np.testing.assert_allclose(dx[0, 0, t].reshape(n, n), expect, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("n", [8, 16])
+def test_layer_autograd_to_token_vectors(mpp, n):
+    # gradient of sum_t <R_t, P_t> down to x through build, scan and their VJPs
+    say(f"[layer autograd] n={n}")
+    so, sd = SIGMA[n]
+    T = 300
+    x = gen_x(1, 2, T, n, so, sd, seed=31)
+    R = gen_R(1, 2, T, n, seed=32)
+    xd = dev(x).requires_grad_(True)
+    P = mpp.mru_layer(xd, n, chunk=37)
+    (P * dev(R)).sum().backward()
+    M64 = build_ref(x, n)
+    ref = build_vjp_ref(x, bwd_ref(M64, R), n)
+    g = host(xd.grad)
+    err = rel_fro_err(g.reshape(1, 2, T, n, n), ref.reshape(1, 2, T, n, n))
+    say(f"  max rel err {err.max():.3e}")
+    assert err.max() <= BWD_TOL
