@@ -150,6 +150,18 @@ mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t 
                         int32_t chunk, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Forward scan straight from raw token vectors: mru_build_inputs followed by
+ * mru_scan_fwd in one pass that reads x once and writes P once.  No input
+ * state matrix is formed: each step multiplies the running state by the LDU
+ * factors in turn (L, then diag(e), then U, same cost as a dense product), so
+ * results agree with the two-call path up to rounding order.  Arguments as
+ * for mru_scan_fwd with x ([B][H][T][n*n]) in place of M; x and P must not
+ * overlap.  n in {4, 8}; other n return MRU_ERR_SHAPE.
+ */
+mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
+                          int32_t chunk, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Backward scan: vector-Jacobian product of the forward scan.
  * Given dP = dL/dP_t for every t, writes dM = dL/dM_t, where (chain rule on
  * P_t = P_{t-1} M_t) with Q_T = dP_T and Q_t = dP_t + Q_{t+1} M_{t+1}^T,
@@ -168,6 +180,16 @@ mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t 
 mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
                         int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
                         size_t ws_bytes, void* stream);
+
+/*
+ * Backward scan from raw token vectors: dM as from mru_build_inputs followed
+ * by mru_scan_bwd, multiplying by the transposed factors of M_{t+1}
+ * (U^T, diag(e), L^T) read from x.  Arguments as for mru_scan_bwd with x in
+ * place of M.  n in {4, 8}; other n return MRU_ERR_SHAPE.
+ */
+mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float* dM, int64_t B,
+                          int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,8 @@ __all__ = [
 DIR_FWD = 0
 DIR_BWD = 1
 SUPPORTED_N = (4, 8, 16, 32)
+# Sizes whose scans can start from raw token vectors (input matrices built on chip).
+FUSED_N = (4, 8)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmru.so")
 _LIB = None
@@ -83,6 +85,10 @@ def load_library():
     lib.mru_scan_fwd.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.mru_scan_bwd.restype = i32
     lib.mru_scan_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_fwd_x.restype = i32
+    lib.mru_scan_fwd_x.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_bwd_x.restype = i32
+    lib.mru_scan_bwd_x.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     _LIB = lib
     return lib
 
@@ -236,6 +242,58 @@ def scan_bwd(M: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
     return out
 
 
+def _xshape(x: torch.Tensor, n: int):
+    _require(x, "x", 4)
+    B, H, T, nn = x.shape
+    if n not in FUSED_N or nn != n * n:
+        raise ValueError(f"x must be [B,H,T,n*n] with n in {FUSED_N}, got {tuple(x.shape)}, n={n}")
+    return B, H, T
+
+
+def scan_fwd_x(x: torch.Tensor, n: int, chunk: int = 0, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """scan_fwd(build_inputs(x, n)) in one pass that never writes the input matrices."""
+    B, H, T = _xshape(x, n)
+    if out is None:
+        out = torch.empty((B, H, T, n, n), dtype=torch.float32, device=x.device)
+    else:
+        _require(out, "out", 5)
+        if tuple(out.shape) != (B, H, T, n, n) or out.device != x.device:
+            raise ValueError("out must be [B,H,T,n,n] on x's device")
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_FWD, chunk, x.device, workspace)
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.mru_scan_fwd_x(_ptr(x), _ptr(out), B, H, T, n, chunk, _ptr(ws), ws_bytes,
+                                _stream_handle(x.device))
+    _check(st, "mru_scan_fwd_x")
+    return out
+
+
+def scan_bwd_x(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """scan_bwd(build_inputs(x, n), P, dP) with the input matrices rebuilt on chip."""
+    _require(P, "P", 5)
+    n = P.shape[-1]
+    B, H, T = _xshape(x, n)
+    for name, t in (("P", P), ("dP", dP)):
+        _require(t, name, 5)
+        if tuple(t.shape) != (B, H, T, n, n) or t.device != x.device:
+            raise ValueError(f"{name} must be [B,H,T,n,n] on x's device")
+    if out is None:
+        out = torch.empty_like(P)
+    else:
+        _require(out, "out", 5)
+        if out.shape != P.shape or out.device != x.device:
+            raise ValueError("out must match P")
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_BWD, chunk, x.device, workspace)
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.mru_scan_bwd_x(_ptr(x), _ptr(P), _ptr(dP), _ptr(out), B, H, T, n, chunk, _ptr(ws),
+                                ws_bytes, _stream_handle(x.device))
+    _check(st, "mru_scan_bwd_x")
+    return out
+
+
 def flatten(P: torch.Tensor) -> torch.Tensor:
     """Row-major flatten of each output state matrix: [B,H,T,n,n] -> [B,H,T,n*n] view."""
     return P.view(*P.shape[:-2], P.shape[-2] * P.shape[-1])
@@ -277,7 +335,29 @@ class MRUBuild(torch.autograd.Function):
         return build_inputs_bwd(x, dM.contiguous()), None
 
 
+class MRULayerFused(torch.autograd.Function):
+    """P = scan_fwd_x(x, n); backward rebuilds M on chip (scan_bwd_x), then
+    build_inputs_bwd.  The input matrices are never stored."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, n: int, chunk: int = 0):
+        x = x.contiguous()
+        P = scan_fwd_x(x, n, chunk)
+        ctx.save_for_backward(x, P)
+        ctx.chunk = chunk
+        return P
+
+    @staticmethod
+    def backward(ctx, dP: torch.Tensor):
+        x, P = ctx.saved_tensors
+        dM = scan_bwd_x(x, P, dP.contiguous(), ctx.chunk)
+        return build_inputs_bwd(x, dM), None, None
+
+
 def mru_layer(x: torch.Tensor, n: int, chunk: int = 0) -> torch.Tensor:
     """The MRU token mixer up to the output state matrices: x [B,H,T,n*n] ->
-    P [B,H,T,n,n] (flatten() gives the output vectors), differentiable in x."""
+    P [B,H,T,n,n] (flatten() gives the output vectors), differentiable in x.
+    For n in FUSED_N the scans build the input matrices on chip."""
+    if n in FUSED_N:
+        return MRULayerFused.apply(x, n, chunk)
     return MRUScan.apply(MRUBuild.apply(x, n), chunk)

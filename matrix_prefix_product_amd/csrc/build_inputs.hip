@@ -9,6 +9,7 @@
 // so  M_ij = sum_{k <= min(i, j)} L_ik e_k U_kj.
 // Elementwise over tokens: a group of n/R lanes builds one token, each lane R
 // rows of M, from the token staged in LDS.  HBM-bound (8 n^2 bytes per token).
+#include "mru_build.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
 
@@ -41,10 +42,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(const float* __res
             *reinterpret_cast<float4*>(sx + t * XS + 4 * q) = v;
         }
         __syncthreads();
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < N; ++k) sum += xt[k * N + k];
-        const float mean = sum * (1.0f / N);
+        const float mean = ldu_mean<N>(xt);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = li * R + r;
@@ -54,45 +52,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(const float* __res
         float acc[R][N];
 #pragma unroll
         for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int j = 0; j < N; ++j) acc[r][j] = 0.f;
-        if constexpr (N <= 16) {
-            // fully unrolled: the zero pattern of U is resolved at compile time
-#pragma unroll
-            for (int k = 0; k < N; ++k) {
-                const float ek = se[tk * N + k];
-                float coef[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int i = li * R + r;
-                    coef[r] = (k < i) ? xt[i * N + k] * ek : ((k == i) ? ek : 0.f);
-                }
-#pragma unroll
-                for (int j = k; j < N; ++j) {
-                    const float u = (j == k) ? 1.f : xt[k * N + j];
-#pragma unroll
-                    for (int r = 0; r < R; ++r) acc[r][j] = fmaf(coef[r], u, acc[r][j]);
-                }
-            }
-        } else {
-            // k loop kept rolled (register pressure); U's zeros are masked
-#pragma unroll 2
-            for (int k = 0; k < N; ++k) {
-                const float ek = se[tk * N + k];
-                float coef[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int i = li * R + r;
-                    coef[r] = (k < i) ? xt[i * N + k] * ek : ((k == i) ? ek : 0.f);
-                }
-#pragma unroll
-                for (int j = 0; j < N; ++j) {
-                    const float u = (j > k) ? xt[k * N + j] : ((j == k) ? 1.f : 0.f);
-#pragma unroll
-                    for (int r = 0; r < R; ++r) acc[r][j] = fmaf(coef[r], u, acc[r][j]);
-                }
-            }
-        }
+            ldu_row<N>(xt, li * R + r, [&](int k) { return se[tk * N + k]; }, acc[r]);
         const int64_t tok = tok0 + tk;
         if (tok < ntok) {
             float* dst = M + tok * NN + li * R * N;

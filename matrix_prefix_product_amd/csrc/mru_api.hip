@@ -203,10 +203,15 @@ int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direct
     return MRU_OK;
 }
 
-mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
-                        int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
+                         int32_t chunk, void* ws, size_t ws_bytes, void* stream, bool from_x) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (from_x && n > 8 && !mfma_from_x_supported(n)) return MRU_ERR_SHAPE;
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P) return MRU_ERR_NULL;
@@ -227,15 +232,16 @@ mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t 
         const mru_status st = reset_ws(ws, p, s);
         if (st != MRU_OK) return st;
     }
-    if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s));
-    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s));
+    if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x));
+    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x));
 }
 
-mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
-                        int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
-                        size_t ws_bytes, void* stream) {
+mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float* dM, int64_t B,
+                         int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                         size_t ws_bytes, void* stream, bool from_x) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (from_x && n > 8) return MRU_ERR_SHAPE;
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P || !dP || !dM) return MRU_ERR_NULL;
@@ -260,8 +266,34 @@ mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* 
         const mru_status st = reset_ws(ws, p, s);
         if (st != MRU_OK) return st;
     }
-    if (n <= 8) return launched(launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s));
+    if (n <= 8) return launched(launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x));
     return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
+                        int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+    return scan_fwd_impl(M, P, B, H, T, n, chunk, ws, ws_bytes, stream, false);
+}
+
+mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
+                          int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+    return scan_fwd_impl(x, P, B, H, T, n, chunk, ws, ws_bytes, stream, true);
+}
+
+mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
+                        int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                        size_t ws_bytes, void* stream) {
+    return scan_bwd_impl(M, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, false);
+}
+
+mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float* dM, int64_t B,
+                          int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                          size_t ws_bytes, void* stream) {
+    return scan_bwd_impl(x, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -17,13 +17,17 @@ hipError_t launch_build_bwd(const float* x, const float* dM, float* dx, int64_t 
 // Chunked scans over S sequences of T tokens: chunk length K, nch chunks per
 // sequence (possibly padded with empty chunks), supers of Z chunks.  nch == 1
 // runs without workspace; nch > 1 needs a cleared workspace header and flags.
+// from_x: the first array holds raw token vectors and the kernel builds the
+// input matrices on the fly (never writing them).
 hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream);
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x);
 hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, bool from_x);
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream);
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x);
+// Whether the matrix-core forward can start from raw token vectors for this n.
+bool mfma_from_x_supported(int n);
 hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
                            hipStream_t stream);

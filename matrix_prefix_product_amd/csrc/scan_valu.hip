@@ -13,6 +13,7 @@
 // Backward (gradient of sum_t <dP_t, P_t>): the chain state is R rows of
 // Q_t = dP_t + Q_{t+1} M_{t+1}^T, swept from the last token to the first, and
 // dM_t = P_{t-1}^T Q_t needs all rows of Q_t, exchanged through LDS.
+#include "mru_build.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
 
@@ -228,11 +229,97 @@ __device__ inline void stage_store(float* lds, const float4* reg) {
     }
 }
 
+// Scans that start from raw token vectors (FX) never form an input matrix.
+// With X the staged token vector viewed n-by-n, M = L diag(e) U where L is unit
+// lower with L_ij = X_ij (i > j), U unit upper with U_ij = X_ij (i < j) and
+// e_k = exp(X_kk - mean_j X_jj) ("Improving Matrix Recurrent Units as an
+// Attention Alternative", Key Points).  A row vector times L, diag(e), U in
+// turn costs n(n-1)/2 + n + n(n-1)/2 = n^2 multiply-adds, the same as one
+// times a dense M, so the fused scans do the same work as the plain ones and
+// move x in place of M.
+//
+// stage_e: e for every staged token (chain-major, TB tokens per chain).
+template <int N, int R, int TB>
+__device__ inline void stage_e(const float* lds, float* se) {
+    using V = Valu<N, R, TB>;
+    constexpr int VALS = V::G * TB * N;
+    static_assert(VALS % 64 == 0, "e values must tile the wave");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < VALS / 64; ++q) {
+        const int f = q * 64 + lane;
+        const int tok = f / N;
+        const int k = f % N;
+        const float* X = lds + (tok / TB) * V::CH_STRIDE + (tok % TB) * V::NN;
+        se[f] = expf(X[k * N + k] - ldu_mean<N>(X));
+    }
+}
+
+template <int N>
+__device__ inline void load_vec(float (&v)[N], const float* src) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        const float4 t = reinterpret_cast<const float4*>(src)[q];
+        v[4 * q] = t.x;
+        v[4 * q + 1] = t.y;
+        v[4 * q + 2] = t.z;
+        v[4 * q + 3] = t.w;
+    }
+}
+
+// st <- st * (L diag(e) U), in place per row.
+template <int N, int R>
+__device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const float* e) {
+    float x[N * N], ev[N];
+    load_matrix<N>(x, X);
+    load_vec<N>(ev, e);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        // times L: r_j += sum_{i > j} r_i X_ij, ascending j reads only untouched r_i
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+#pragma unroll
+            for (int i = j + 1; i < N; ++i) st[r][j] = fmaf(st[r][i], x[i * N + j], st[r][j]);
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] *= ev[j];
+        // times U: r_j += sum_{k < j} r_k X_kj, descending j reads only untouched r_k
+#pragma unroll
+        for (int j = N - 1; j > 0; --j)
+#pragma unroll
+            for (int k = 0; k < j; ++k) st[r][j] = fmaf(st[r][k], x[k * N + j], st[r][j]);
+    }
+}
+
+// st <- st * (L diag(e) U)^T = st * U^T diag(e) L^T, in place per row.
+template <int N, int R>
+__device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X, const float* e) {
+    float x[N * N], ev[N];
+    load_matrix<N>(x, X);
+    load_vec<N>(ev, e);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        // times U^T: r_j += sum_{k > j} r_k X_jk, ascending j
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+#pragma unroll
+            for (int k = j + 1; k < N; ++k) st[r][j] = fmaf(st[r][k], x[j * N + k], st[r][j]);
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] *= ev[j];
+        // times L^T: r_j += sum_{k < j} r_k X_jk, descending j
+#pragma unroll
+        for (int j = N - 1; j > 0; --j)
+#pragma unroll
+            for (int k = 0; k < j; ++k) st[r][j] = fmaf(st[r][k], x[j * N + k], st[r][j]);
+    }
+}
+
 // One sweep of a forward chain over its chunk: st <- st * M_t for each token,
-// optionally storing the rows of every P_t.
-template <int N, int R, int TB, bool WRITE>
+// optionally storing the rows of every P_t.  With FX the input is x and each
+// step multiplies by M_t's factors (se holds the staged tokens' e).
+template <int N, int R, int TB, bool WRITE, bool FX>
 __device__ void fwd_sweep(float (&st)[R][N], const float* __restrict__ M, float* __restrict__ P,
-                          float* lds, const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
+                          float* lds, float* se, const ChainInfo* info, int g, int li, int maxlen,
+                          int64_t T) {
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
     float4 reg[V::LD];
@@ -242,26 +329,36 @@ __device__ void fwd_sweep(float (&st)[R][N], const float* __restrict__ M, float*
         stage_store<N, R, TB>(lds, reg);
         __syncthreads();
         if (blk + TB < maxlen) stage_load<N, R, TB, false>(reg, M, info, blk + TB, 0, T);
+        if constexpr (FX) {
+            stage_e<N, R, TB>(lds, se);
+            __syncthreads();
+        }
 #pragma unroll
         for (int tau = 0; tau < TB; ++tau) {
             const int pos = blk + tau;
             if (pos < me.len) {
-                float m[V::NN];
-                load_matrix<N>(m, lds + g * V::CH_STRIDE + tau * V::NN);
-                rows_times<N, R>(st, m);
+                const float* slot = lds + g * V::CH_STRIDE + tau * V::NN;
+                if constexpr (FX) {
+                    rows_times_ldu<N, R>(st, slot, se + (g * TB + tau) * N);
+                } else {
+                    float m[V::NN];
+                    load_matrix<N>(m, slot);
+                    rows_times<N, R>(st, m);
+                }
                 if (WRITE) store_rows<N, R>(P + (me.base + pos) * V::NN + li * R * N, st);
             }
         }
     }
 }
 
-template <int N, int R, int TB>
+template <int N, int R, int TB, bool FX>
 __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
                                                       unsigned char* __restrict__ ws) {
     using V = Valu<N, R, TB>;
     __shared__ float lds[V::G * V::CH_STRIDE];
+    __shared__ float se[FX ? V::G * TB * N : 4];
     __shared__ float xch[V::G * V::NN];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
@@ -282,7 +379,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     float st[R][N];
     set_identity_rows<N, R>(st, li * R);
     if (!multi) {
-        fwd_sweep<N, R, TB, true>(st, M, P, lds, info, g, li, maxlen, T);
+        fwd_sweep<N, R, TB, true, FX>(st, M, P, lds, se, info, g, li, maxlen, T);
         return;
     }
 
@@ -298,7 +395,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     const bool later_super = k >= Z;  // wave-uniform
 
     // 1. chunk aggregate
-    fwd_sweep<N, R, TB, false>(st, M, P, lds, info, g, li, maxlen, T);
+    fwd_sweep<N, R, TB, false, FX>(st, M, P, lds, se, info, g, li, maxlen, T);
     ws_store_rows<N, R>(agg + c * V::NN + li * R * N, st);
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
@@ -344,7 +441,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from its carry and write every prefix
-    fwd_sweep<N, R, TB, true>(st, M, P, lds, info, g, li, maxlen, T);
+    fwd_sweep<N, R, TB, true, FX>(st, M, P, lds, se, info, g, li, maxlen, T);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -356,11 +453,11 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
 //   GRAD pass (GRAD = true):  q <- dP_t + q M_{t+1}^T from the carry, and
 //             dM_t = P_{t-1}^T Q_t written for the lane's rows.
 // At the last token of a sequence there is no M_{t+1}: q <- dP_t.
-template <int N, int R, int TB, bool GRAD>
+template <int N, int R, int TB, bool GRAD, bool FX>
 __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
                           const float* __restrict__ P, const float* __restrict__ dP,
-                          float* __restrict__ dM, float* lds, float* qx, const ChainInfo* info,
-                          int g, int li, int maxlen, int64_t T) {
+                          float* __restrict__ dM, float* lds, float* se, float* qx,
+                          const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
     using V = Valu<N, R, TB>;
     constexpr int ARR = GRAD ? 3 : 2;  // staged arrays: M(t+1), dP(t), [P(t-1)]
     const ChainInfo me = info[g];
@@ -378,6 +475,10 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
         if (GRAD) stage_store<N, R, TB>(lds + 2 * V::G * V::CH_STRIDE, rp);
         __syncthreads();
         if (blk + TB < maxlen) load_all(blk + TB);
+        if constexpr (FX) {
+            stage_e<N, R, TB>(lds, se);  // factors of M_{t+1} from x_{t+1}
+            __syncthreads();
+        }
 #pragma unroll
         for (int tau = 0; tau < TB; ++tau) {
             const int i = blk + tau;
@@ -385,13 +486,19 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
             const bool live = i < me.len;
             const int64_t tseq = int64_t(me.t0) + pos;
             const float* mslot = lds + g * V::CH_STRIDE + tau * V::NN;
+            const float* eslot = se + (g * TB + tau) * N;
             const float* rslot = lds + V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN;
             if (live) {
                 if (tseq + 1 < T) {
-                    float m[V::NN];
-                    load_matrix<N>(m, mslot);
-                    rows_times_t<N, R>(q, m);
-                    if (!GRAD) rows_times_t<N, R>(w, m);
+                    if constexpr (FX) {
+                        rows_times_ldu_t<N, R>(q, mslot, eslot);
+                        if (!GRAD) rows_times_ldu_t<N, R>(w, mslot, eslot);
+                    } else {
+                        float m[V::NN];
+                        load_matrix<N>(m, mslot);
+                        rows_times_t<N, R>(q, m);
+                        if (!GRAD) rows_times_t<N, R>(w, m);
+                    }
                 } else {
                     set_zero_rows<N, R>(q);
                 }
@@ -434,7 +541,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
     }
 }
 
-template <int N, int R, int TB>
+template <int N, int R, int TB, bool FX>
 __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ P,
                                                       const float* __restrict__ dP,
@@ -443,6 +550,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
                                                       int64_t Z, unsigned char* __restrict__ ws) {
     using V = Valu<N, R, TB>;
     __shared__ float lds[3 * V::G * V::CH_STRIDE];
+    __shared__ float se[FX ? V::G * TB * N : 4];
     __shared__ float qx[V::G * V::NN];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
@@ -464,7 +572,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     set_zero_rows<N, R>(q);
     set_identity_rows<N, R>(w, li * R);
     if (!multi) {
-        bwd_sweep<N, R, TB, true>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
+        bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T);
         return;
     }
 
@@ -482,7 +590,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     const bool later_super = r >= Z;
 
     // 1. affine aggregate of the chunk
-    bwd_sweep<N, R, TB, false>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
+    bwd_sweep<N, R, TB, false, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T);
     ws_store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
     ws_store_rows<N, R>(swt + c * V::NN + li * R * N, w);
     fence_release();
@@ -538,26 +646,26 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from the carry and write dM
-    bwd_sweep<N, R, TB, true>(q, w, M, P, dP, dM, lds, qx, info, g, li, maxlen, T);
+    bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T);
 }
 
-template <int N, int R, int TB>
+template <int N, int R, int TB, bool FX>
 hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
                    int64_t Z, void* ws, hipStream_t stream) {
     using V = Valu<N, R, TB>;
     const int64_t waves = (S * nch + V::G - 1) / V::G;
-    hipLaunchKernelGGL((fwd_valu_kernel<N, R, TB>), dim3(unsigned(waves)), dim3(64), 0, stream, M,
-                       P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+    hipLaunchKernelGGL((fwd_valu_kernel<N, R, TB, FX>), dim3(unsigned(waves)), dim3(64), 0, stream,
+                       M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
     return hipGetLastError();
 }
 
-template <int N, int R, int TB>
+template <int N, int R, int TB, bool FX>
 hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                    int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
     using V = Valu<N, R, TB>;
     const int64_t waves = (S * nch + V::G - 1) / V::G;
-    hipLaunchKernelGGL((bwd_valu_kernel<N, R, TB>), dim3(unsigned(waves)), dim3(64), 0, stream, M,
-                       P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+    hipLaunchKernelGGL((bwd_valu_kernel<N, R, TB, FX>), dim3(unsigned(waves)), dim3(64), 0, stream,
+                       M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
     return hipGetLastError();
 }
 
@@ -584,17 +692,29 @@ int valu_chains_per_wave(int n, int dir) {
 }
 
 hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
-    if (n == 4) return run_fwd<MRU_VALU_CFG4>(M, P, S, T, K, nch, Z, ws, stream);
-    if (n == 8) return run_fwd<MRU_VALU_CFG8>(M, P, S, T, K, nch, Z, ws, stream);
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x) {
+    if (n == 4) {
+        if (from_x) return run_fwd<MRU_VALU_CFG4, true>(M, P, S, T, K, nch, Z, ws, stream);
+        return run_fwd<MRU_VALU_CFG4, false>(M, P, S, T, K, nch, Z, ws, stream);
+    }
+    if (n == 8) {
+        if (from_x) return run_fwd<MRU_VALU_CFG8, true>(M, P, S, T, K, nch, Z, ws, stream);
+        return run_fwd<MRU_VALU_CFG8, false>(M, P, S, T, K, nch, Z, ws, stream);
+    }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream) {
-    if (n == 4) return run_bwd<MRU_VALU_BWD_CFG4>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
-    if (n == 8) return run_bwd<MRU_VALU_BWD_CFG8>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+                           hipStream_t stream, bool from_x) {
+    if (n == 4) {
+        if (from_x) return run_bwd<MRU_VALU_BWD_CFG4, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+        return run_bwd<MRU_VALU_BWD_CFG4, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+    }
+    if (n == 8) {
+        if (from_x) return run_bwd<MRU_VALU_BWD_CFG8, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+        return run_bwd<MRU_VALU_BWD_CFG8, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -122,3 +122,21 @@ def test_validation_before_any_launch(mpp):
     assert lib.mru_build_inputs_bwd(a, b, a, 1, 1, 4, 8, nul) == 4
     assert lib.mru_build_inputs_bwd(odd, b, ws, 1, 1, 4, 8, nul) == 3
     assert lib.mru_build_inputs_bwd(nul, nul, nul, 0, 1, 4, 8, nul) == 0
+
+
+def test_fused_entries_validate_before_any_launch(mpp):
+    lib = mpp.load_library()
+    nul = ctypes.c_void_p(0)
+    a, b, c, d = (ctypes.c_void_p(v) for v in (0x100000, 0x200000, 0x300000, 0x400000))
+    # only n = 4, 8 start from token vectors
+    assert lib.mru_scan_fwd_x(a, b, 1, 1, 16, 16, 0, nul, 0, nul) == 2
+    assert lib.mru_scan_bwd_x(a, b, c, d, 1, 1, 16, 32, 0, nul, 0, nul) == 2
+    assert lib.mru_scan_fwd_x(a, b, 1, 1, 16, 6, 0, nul, 0, nul) == 2
+    # empty, null, alias, workspace, chunk
+    assert lib.mru_scan_fwd_x(nul, nul, 0, 1, 16, 8, 0, nul, 0, nul) == 0
+    assert lib.mru_scan_fwd_x(nul, b, 1, 1, 16, 8, 0, nul, 0, nul) == 1
+    assert lib.mru_scan_fwd_x(a, a, 1, 1, 16, 8, 0, nul, 0, nul) == 4
+    assert lib.mru_scan_fwd_x(a, b, 1, 1, 1024, 4, 0, nul, 0, nul) == 5
+    assert lib.mru_scan_fwd_x(a, b, 1, 1, 16, 8, -1, nul, 0, nul) == 6
+    assert lib.mru_scan_bwd_x(a, b, c, c, 1, 1, 8, 8, 1, nul, 0, nul) == 4
+    assert lib.mru_scan_bwd_x(a, b, nul, d, 1, 1, 8, 8, 1, nul, 0, nul) == 1

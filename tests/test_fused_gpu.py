@@ -1,0 +1,135 @@
+"""GPU parity of the scans that start from raw token vectors (n = 4, 8).
+
+mru_scan_fwd_x / mru_scan_bwd_x multiply by the LDU factors of each input
+state matrix instead of forming it, so they agree with build-then-scan up to
+rounding order; both are graded against the fp64 oracle
+(scan_ref(build_ref(x)), bwd_ref(build_ref(x), R)) with the forward / backward
+tolerances, and must be deterministic run to run.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import BUILD_TOL, BWD_TOL, FWD_TOL, dev, fwd_errors, host, say, summary
+from oracle import build_ref, build_vjp_ref, bwd_ref, rel_fro_err
+from workloads import gen_R, gen_x
+
+pytestmark = pytest.mark.gpu
+
+SIGMA = {4: (0.1, 0.05), 8: (0.1, 0.05)}
+
+CASES = [
+    (4, 1, 1, 1024, 0), (4, 3, 2, 203, 3), (4, 2, 2, 97, 1), (4, 5, 1, 120, 120),
+    (4, 1, 1, 4096, 0),
+    (8, 8, 8, 256, 0), (8, 2, 3, 203, 5), (8, 1, 2, 203, 1), (8, 33, 1, 64, 64),
+    (8, 2, 2, 500, 16), (8, 1, 1, 1024, 0),
+]
+# (longer n = 8 sequences at these scales leave the fp32-state domain: by 2048
+# tokens the backward error reaches the 5e-4 bound, by ~2900 the products overflow)
+
+
+@pytest.fixture(scope="module")
+def mpp():
+    import matrix_prefix_product_amd as m
+    m.load_library()
+    return m
+
+
+def _x(B, H, T, n, seed):
+    so, sd = SIGMA[n]
+    return gen_x(B, H, T, n, so, sd, seed)
+
+
+@pytest.mark.parametrize("n,B,H,T,chunk", CASES)
+def test_fused_fwd(mpp, n, B, H, T, chunk):
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD, chunk)
+    say(f"[fused fwd] n={n} B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    x = _x(B, H, T, n, seed=T + n)
+    xd = dev(x)
+    P = mpp.scan_fwd_x(xd, n, chunk)
+    again = mpp.scan_fwd_x(xd, n, chunk)
+    assert torch.equal(P.view(torch.int32), again.view(torch.int32)), "not deterministic"
+    err, dom, P_ref = fwd_errors(host(P), build_ref(x, n))
+    say("  " + summary(err, dom))
+    assert err[dom].max() <= FWD_TOL
+    # for comparison only: build + scan on the same tokens (its own parity cases
+    # are elsewhere; it rounds every M_t to fp32 first, and at n = 8 over 2048
+    # tokens that alone costs more than the whole fused error)
+    P_two = host(mpp.scan_fwd(mpp.build_inputs(xd, n), chunk))
+    say(f"  build + scan: max {rel_fro_err(P_two, P_ref)[dom].max():.3e}")
+
+
+@pytest.mark.parametrize("n,B,H,T,chunk", CASES)
+def test_fused_bwd(mpp, n, B, H, T, chunk):
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_BWD, chunk)
+    say(f"[fused bwd] n={n} B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    x = _x(B, H, T, n, seed=T + 3 * n)
+    R = gen_R(B, H, T, n, seed=T + 1)
+    xd, Rd = dev(x), dev(R)
+    P = mpp.scan_fwd_x(xd, n)
+    ws = torch.empty(max(plan[3], 256), dtype=torch.uint8, device="cuda")
+    dM = mpp.scan_bwd_x(xd, P, Rd, chunk, workspace=ws)
+    again = mpp.scan_bwd_x(xd, P, Rd, chunk)
+    assert torch.equal(dM.view(torch.int32), again.view(torch.int32)), "not deterministic"
+    err = rel_fro_err(host(dM), bwd_ref(build_ref(x, n), R))
+    say(f"  max {err.max():.3e} median {np.median(err):.3e}")
+    assert err.max() <= BWD_TOL
+    if plan[3] > 0:
+        assert int(host(ws[4:8].view(torch.int32))[0]) == 0, "a flag wait timed out"
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_fused_zero_input_is_identity(mpp, n):
+    # x = 0 builds M_t = I exactly, so every prefix is I and dM is the reverse cumsum of R
+    T = 300
+    xd = torch.zeros(2, 1, T, n * n, device="cuda")
+    for chunk in (0, 7):
+        P = host(mpp.scan_fwd_x(xd, n, chunk))
+        assert np.array_equal(P, np.broadcast_to(np.eye(n, dtype=np.float32), P.shape))
+        R = gen_R(2, 1, T, n, seed=n)
+        dM = host(mpp.scan_bwd_x(xd, dev(P), dev(R), chunk))
+        expect = np.cumsum(R[:, :, ::-1].astype(np.float64), axis=2)[:, :, ::-1]
+        assert rel_fro_err(dM, expect).max() <= BWD_TOL
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_fused_edges(mpp, n):
+    say(f"[fused edges] n={n}")
+    # empty sequences and empty batches are no-ops
+    e = mpp.scan_fwd_x(torch.zeros(2, 3, 0, n * n, device="cuda"), n)
+    assert e.shape == (2, 3, 0, n, n)
+    # one token: P_1 = M_1, dM_1 = R_1
+    x = _x(3, 2, 1, n, seed=5)
+    P = host(mpp.scan_fwd_x(dev(x), n))
+    assert rel_fro_err(P, build_ref(x, n)).max() <= BUILD_TOL
+    R = gen_R(3, 2, 1, n, seed=6)
+    dM = host(mpp.scan_bwd_x(dev(x), dev(P), dev(R)))
+    assert np.array_equal(dM, R)
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_fused_layer_autograd(mpp, n):
+    # mru_layer takes the fused path for n = 4, 8: gradient down to x against the oracle
+    say(f"[fused layer autograd] n={n}")
+    T = 300
+    x = _x(1, 2, T, n, seed=41)
+    R = gen_R(1, 2, T, n, seed=42)
+    xd = dev(x).requires_grad_(True)
+    P = mpp.mru_layer(xd, n, chunk=37)
+    (P * dev(R)).sum().backward()
+    ref = build_vjp_ref(x, bwd_ref(build_ref(x, n), R), n)
+    err = rel_fro_err(host(xd.grad).reshape(1, 2, T, n, n), ref.reshape(1, 2, T, n, n))
+    say(f"  max rel err {err.max():.3e}")
+    assert err.max() <= BWD_TOL
+
+
+def test_fused_rejects_matrix_core_sizes(mpp):
+    x = torch.zeros(1, 1, 4, 256, device="cuda")
+    with pytest.raises(ValueError):
+        mpp.scan_fwd_x(x, 16)
+    lib = mpp.load_library()
+    P = torch.empty(1, 1, 4, 16, 16, device="cuda")
+    import ctypes
+    st = lib.mru_scan_fwd_x(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(P.data_ptr()),
+                            1, 1, 4, 16, 0, None, 0, None)
+    assert st == 2
