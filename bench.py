@@ -2,8 +2,10 @@
 """Benchmark of the MRU hot path on one MI355X (gfx950).
 
 One step = the whole path over one batch of seeded synthetic input already
-resident in HBM: LDU build (x -> M), forward prefix scan (M -> P) and backward
-scan (M, P, dL/dP -> dL/dM).  Prints ONE JSON line:
+resident in HBM: the forward prefix scan straight from the raw token vectors
+(LDU build folded in: x -> P) and the backward scan (x, P, dL/dP -> dL/dM),
+which rebuilds each input's factors the same way; the input state matrices are
+never stored.  Prints ONE JSON line:
 
   value         tokens/s of the whole step (a token = one position of one batch
                 row, all heads included), timed with HIP events over exactly
@@ -14,6 +16,8 @@ scan (M, P, dL/dP -> dL/dM).  Prints ONE JSON line:
                 from profiles/hbm_traffic.json when that record was taken on the
                 current kernel sources, else null
   kernels       the same figures for every kernel of the step
+  unfused       the separate kernels (build x -> M, scan M -> P, backward from M,
+                and the build's own backward x, dM -> dx) timed alone
   n16, n32      forward-scan throughput on the n=16 and n=32 workloads
   cpu_baseline  the fp64 oracle (oracle/) timed on the host on a bounded sample
                 of the same workload
@@ -50,13 +54,15 @@ def source_hash() -> str:
 
 
 def algorithmic_bytes(kind: str, S: int, T: int, n: int) -> int:
-    per = {"build": 8, "fwd": 8, "bwd": 16}[kind]  # bytes per matrix entry per token-head
+    # bytes per matrix entry per token-head
+    per = {"build": 8, "fwd": 8, "bwd": 16, "fwd_x": 8, "bwd_x": 16, "build_bwd": 12}[kind]
     return per * n * n * S * T
 
 
 def algorithmic_flops(kind: str, S: int, T: int, n: int) -> int:
     # serial-product flops: forward n^3 mult-adds per token-head, backward 2 n^3
-    return {"build": n ** 3 // 3 * 2, "fwd": 2 * n ** 3, "bwd": 4 * n ** 3}[kind] * S * T
+    return {"build": n ** 3 // 3 * 2, "fwd": 2 * n ** 3, "bwd": 4 * n ** 3,
+            "fwd_x": 2 * n ** 3, "bwd_x": 4 * n ** 3}[kind] * S * T
 
 
 def load_traffic(workload: str, kernel: str):
@@ -167,6 +173,33 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
     }
 
 
+def unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, workload, reps: int = 10):
+    """The separate kernels on the same inputs: build x -> M, scan M -> P,
+    backward from M, and the build's backward (x, dM -> dx)."""
+    M = mpp.build_inputs(x, n)
+    dx = torch.empty_like(x)
+    calls = {
+        "build": lambda: mpp.build_inputs(x, n, out=M),
+        "fwd": lambda: mpp.scan_fwd(M, out=P, workspace=ws_f),
+        "bwd": lambda: mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b),
+        "build_bwd": lambda: mpp.build_inputs_bwd(x, dM, out=dx),
+    }
+    rec = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        avg = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
+        rec[name] = kernel_record(name, avg, S, T, n, workload)
+    del M, dx
+    return rec
+
+
 def copy_reference(torch, gib: int = 1, reps: int = 10):
     """A plain device-to-device copy of known size on the same GPU: the practical
     streaming bandwidth this machine reaches, and the known-size kernel that scales
@@ -226,29 +259,28 @@ def main():
 
     x = torch.from_numpy(gen_x(B, H, T, n, w.sigma_off, w.sigma_diag, w.seed)).to(dev)
     R = torch.from_numpy(gen_R(B, H, T, n, w.seed)).to(dev)
-    M = torch.empty((B, H, T, n, n), device=dev)
-    P = torch.empty_like(M)
-    dM = torch.empty_like(M)
+    if n not in mpp.FUSED_N:
+        sys.exit(f"the step starts from raw token vectors, available for n in {mpp.FUSED_N}")
+    P = torch.empty((B, H, T, n, n), device=dev)
+    dM = torch.empty_like(P)
     ws_f = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_FWD), 256), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_BWD), 256), dtype=torch.uint8, device=dev)
 
+    # events are recorded on torch's current stream, the stream every call below launches on
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        mpp.build_inputs(x, n, out=M)
+        mpp.scan_fwd_x(x, n, out=P, workspace=ws_f)
         if ev is not None:
             ev[1].record()
-        mpp.scan_fwd(M, out=P, workspace=ws_f)
+        mpp.scan_bwd_x(x, P, R, out=dM, workspace=ws_b)
         if ev is not None:
             ev[2].record()
-        mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b)
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -260,11 +292,10 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    per = {k: [] for k in ("build", "fwd", "bwd")}
+    per = {k: [] for k in ("fwd_x", "bwd_x")}
     for e in evs:
-        per["build"].append(e[0].elapsed_time(e[1]))
-        per["fwd"].append(e[1].elapsed_time(e[2]))
-        per["bwd"].append(e[2].elapsed_time(e[3]))
+        per["fwd_x"].append(e[0].elapsed_time(e[1]))
+        per["bwd_x"].append(e[1].elapsed_time(e[2]))
     kernels = {k: kernel_record(k, float(np.mean(v)), S, T, n, w.name) for k, v in per.items()}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
     dk = kernels[dom]
@@ -285,8 +316,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: char-LM-shaped MRU layer, B={B}, H={H} heads, T={T}, n={n} "
-                        "(d_model 512 as 8 heads of 8x8); one step = LDU build + forward scan + "
-                        "backward scan",
+                        "(d_model 512 as 8 heads of 8x8); one step = forward scan from the raw "
+                        "token vectors (LDU build fused) + backward scan to dL/dM",
             "B": B, "H": H, "T": T, "n": n,
             "fwd_plan": dict(zip(("chunk", "chunks_per_seq", "super", "ws_bytes"),
                                  mpp.scan_plan(B, H, T, n, mpp.DIR_FWD))),
@@ -306,7 +337,8 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 4),
     }
-    del x, R, M, P, dM, ws_f, ws_b
+    out["unfused"] = unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, w.name)
+    del x, R, P, dM, ws_f, ws_b
     torch.cuda.empty_cache()
     out["copy_reference"] = copy_reference(torch)
 
