@@ -12,5 +12,6 @@ from .mru_oracle import (  # noqa: F401
     loss_ref,
     rel_fro_err,
     representable,
+    scaled_ref,
     scan_ref,
 )

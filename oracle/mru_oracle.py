@@ -28,7 +28,9 @@ Readings taken where the pages are silent:
 * The determinant-correcting scalar is c = |det(L D U)|^(-1/n), so that
   det(M) = 1 for M = c L D U.
 * The scan is inclusive with P_0 = I and right multiplication,
-  P_t = P_{t-1} M_t.
+  P_t = P_{t-1} M_t; a carried-in state replaces I by a given P_0 (segment
+  continuation), and the scaled form writes each P_t as 2^E times a matrix
+  whose largest entry lies in [0.5, 1).
 * Flattening is the row-major reshape of P_t to an n*n vector, per head.
 * The backward pass is the vector-Jacobian product of L = sum_t <R_t, P_t>_F
   with respect to every M_t (the pages describe training through the product
@@ -44,7 +46,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "build_ref", "build_vjp_ref", "scan_ref", "bwd_ref", "flatten_ref", "loss_ref",
+    "build_ref", "build_vjp_ref", "scan_ref", "bwd_ref", "scaled_ref", "flatten_ref", "loss_ref",
     "rel_fro_err", "representable", "FP32_DOMAIN_LIMIT",
 ]
 
@@ -116,10 +118,22 @@ def build_vjp_ref(x: np.ndarray, dM: np.ndarray, n: int) -> np.ndarray:
     return dX.reshape(*dX.shape[:-2], n * n)
 
 
-def scan_ref(M: np.ndarray) -> np.ndarray:
-    """All prefix products P_t = M_1 M_2 ... M_t, serial, left to right.
+def _initial_state(C0, batch: tuple, n: int) -> np.ndarray:
+    if C0 is None:
+        return np.broadcast_to(np.eye(n), batch + (n, n)).copy()    # P_0 = I
+    C0 = np.asarray(C0, dtype=np.float64)
+    if C0.shape != batch + (n, n):
+        raise ValueError(f"C0 must have shape {batch + (n, n)}, got {C0.shape}")
+    return C0.copy()
 
-    ``M``: ``[..., T, n, n]``; returns float64 of the same shape.
+
+def scan_ref(M: np.ndarray, C0: np.ndarray | None = None) -> np.ndarray:
+    """All prefix products P_t = P_0 M_1 M_2 ... M_t, serial, left to right.
+
+    ``M``: ``[..., T, n, n]``; returns float64 of the same shape.  ``C0``
+    (``[..., n, n]``) is the state before the first token, I when omitted;
+    a sequence cut into segments is scanned by passing each segment the last
+    prefix of the one before.
 
     Follows "MRU Update: ..." (openai-hub.net), section "What MRU Actually
     Does": cumulative multiplication along the sequence, each step being the
@@ -130,7 +144,7 @@ def scan_ref(M: np.ndarray) -> np.ndarray:
     T, n = M.shape[-3], M.shape[-1]
     batch = M.shape[:-3]
     P = np.empty(M.shape, dtype=np.float64)
-    state = np.broadcast_to(np.eye(n), batch + (n, n)).copy()    # P_0 = I
+    state = _initial_state(C0, batch, n)
     for t in range(T):
         state = state @ M[..., t, :, :]
         P[..., t, :, :] = state
@@ -149,16 +163,20 @@ def loss_ref(P: np.ndarray, R: np.ndarray) -> float:
     return float(np.sum(np.asarray(P, np.float64) * np.asarray(R, np.float64)))
 
 
-def bwd_ref(M: np.ndarray, R: np.ndarray) -> np.ndarray:
+def bwd_ref(M: np.ndarray, R: np.ndarray, C0: np.ndarray | None = None,
+            want_dC0: bool = False):
     """Gradient dL/dM_t of L = sum_t <R_t, P_t> with P_t = P_{t-1} M_t.
 
-    ``M``, ``R``: ``[..., T, n, n]``; returns float64 ``dM`` of the same shape.
+    ``M``, ``R``: ``[..., T, n, n]``; returns float64 ``dM`` of the same shape,
+    or ``(dM, dC0)`` with ``want_dC0``.  ``C0`` is the state P_0 before the
+    first token (I when omitted), as in ``scan_ref``.
 
     Reverse-mode chain rule, serial from the last token to the first: with
     Q_t the total adjoint of P_t (R_t plus what flows back from P_{t+1} =
     P_t M_{t+1}), Q_T = R_T, Q_t = R_t + Q_{t+1} M_{t+1}^T, and since P_t
-    depends on M_t only through P_{t-1} M_t, dL/dM_t = P_{t-1}^T Q_t with
-    P_0 = I.  The prefixes come from this module's own fp64 forward.
+    depends on M_t only through P_{t-1} M_t, dL/dM_t = P_{t-1}^T Q_t.  P_1 =
+    P_0 M_1 also gives dL/dP_0 = Q_1 M_1^T (zero when T = 0).  The prefixes
+    come from this module's own fp64 forward.
     """
     M = np.asarray(M, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
@@ -166,8 +184,8 @@ def bwd_ref(M: np.ndarray, R: np.ndarray) -> np.ndarray:
         raise ValueError("M and R must have the same shape")
     T, n = M.shape[-3], M.shape[-1]
     batch = M.shape[:-3]
-    P = scan_ref(M)
-    eye = np.broadcast_to(np.eye(n), batch + (n, n))
+    P = scan_ref(M, C0)
+    P0 = _initial_state(C0, batch, n)
     dM = np.empty(M.shape, dtype=np.float64)
     Q = np.zeros(batch + (n, n))
     for t in range(T - 1, -1, -1):
@@ -175,9 +193,30 @@ def bwd_ref(M: np.ndarray, R: np.ndarray) -> np.ndarray:
             Q = R[..., t, :, :] + Q @ np.swapaxes(M[..., t + 1, :, :], -1, -2)
         else:
             Q = R[..., t, :, :].copy()
-        P_prev = P[..., t - 1, :, :] if t > 0 else eye
+        P_prev = P[..., t - 1, :, :] if t > 0 else P0
         dM[..., t, :, :] = np.swapaxes(P_prev, -1, -2) @ Q
-    return dM
+    if not want_dC0:
+        return dM
+    dC0 = Q @ np.swapaxes(M[..., 0, :, :], -1, -2) if T > 0 else np.zeros(batch + (n, n))
+    return dM, dC0
+
+
+def scaled_ref(P: np.ndarray):
+    """Power-of-two form of each matrix: ``P = 2^E * Pm`` with ``E`` the frexp
+    exponent of the largest |entry| (so max |Pm| lies in [0.5, 1)), and E = 0,
+    Pm = 0 for a zero matrix.  ``P``: ``[..., n, n]``; returns float64 ``Pm``
+    and int64 ``E`` of shape ``P.shape[:-2]``.
+
+    The exponent side output of a scaled scan; the pages name unbounded states
+    as a failure mode ("MRU Update: ...", section "The Two Fatal Issues From a
+    Year Ago"), and this form keeps every P_t representable.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    big = np.abs(P).max(axis=(-1, -2))
+    _, E = np.frexp(big)
+    E = np.where(big > 0, E, 0).astype(np.int64)
+    Pm = np.ldexp(P, -E[..., None, None])
+    return Pm, E
 
 
 def rel_fro_err(test: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -439,3 +439,99 @@ def test_training_gradient_chain():
         xm = x.copy(); xm[idx] -= h
         fd[idx] = (loss_ref(scan_ref(build_ref(xp, n)), R) - loss_ref(scan_ref(build_ref(xm, n)), R)) / (2 * h)
     np.testing.assert_allclose(g, fd, rtol=0, atol=5e-8)
+
+
+# ----------------------------------------------------------------------------- carried-in state, scaled form
+
+from oracle import scaled_ref  # noqa: E402
+
+
+def test_scan_carry_brute_force_multidot():
+    # P_t = C0 M_1 ... M_t as one library product per t (no recurrence)
+    n, T = 3, 6
+    M = RNG.normal(0, 0.6, size=(T, n, n))
+    C0 = RNG.normal(size=(n, n))
+    P = scan_ref(M, C0)
+    for t in range(T):
+        np.testing.assert_allclose(P[t], np.linalg.multi_dot([C0, *M[: t + 1]]), rtol=1e-12,
+                                   atol=1e-12)
+    # carry on the left, not the right: the two differ for non-commuting inputs
+    assert not np.allclose(P[0], M[0] @ C0)
+
+
+def test_scan_carry_segments_continue():
+    n, T, k = 4, 30, 11
+    M = build_ref(RNG.normal(0, 0.3, size=(2, T, n * n)), n)
+    whole = scan_ref(M)
+    head = scan_ref(M[:, :k])
+    tail = scan_ref(M[:, k:], C0=head[:, -1])
+    np.testing.assert_allclose(np.concatenate([head, tail], axis=1), whole, rtol=1e-12, atol=1e-12)
+    # the identity carry is the plain scan, bit for bit
+    assert np.array_equal(scan_ref(M, np.broadcast_to(np.eye(n), (2, n, n))), whole)
+
+
+def _loss_c(M, R, C0):
+    return loss_ref(scan_ref(M, C0), R)
+
+
+def test_bwd_carry_finite_differences():
+    n, T = 3, 5
+    M = build_ref(RNG.normal(0, 0.3, size=(T, n * n)), n)
+    R = RNG.normal(size=(T, n, n))
+    C0 = RNG.normal(size=(n, n))
+    dM, dC0 = bwd_ref(M, R, C0, want_dC0=True)
+    h = 1e-6
+    fdC = np.empty_like(C0)
+    for idx in np.ndindex(C0.shape):
+        Cp = C0.copy(); Cp[idx] += h
+        Cm = C0.copy(); Cm[idx] -= h
+        fdC[idx] = (_loss_c(M, R, Cp) - _loss_c(M, R, Cm)) / (2 * h)
+    np.testing.assert_allclose(dC0, fdC, rtol=0, atol=1e-8)
+    fdM = np.empty_like(M)
+    for idx in np.ndindex(M.shape):
+        Mp = M.copy(); Mp[idx] += h
+        Mm = M.copy(); Mm[idx] -= h
+        fdM[idx] = (_loss_c(Mp, R, C0) - _loss_c(Mm, R, C0)) / (2 * h)
+    np.testing.assert_allclose(dM, fdM, rtol=0, atol=1e-8)
+
+
+def test_bwd_carry_explicit_sum_and_torch():
+    # dC0 = sum_t R_t (M_1 ... M_t)^T, products of the raw inputs only
+    n, T = 4, 7
+    M = RNG.normal(0, 0.5, size=(2, T, n, n))
+    R = RNG.normal(size=(2, T, n, n))
+    C0 = RNG.normal(size=(2, n, n))
+    _, dC0 = bwd_ref(M, R, C0, want_dC0=True)
+    for b in range(2):
+        acc = np.zeros((n, n))
+        for t in range(T):
+            acc += R[b, t] @ np.linalg.multi_dot([np.eye(n), *M[b, : t + 1]]).T
+        np.testing.assert_allclose(dC0[b], acc, rtol=1e-12, atol=1e-12)
+    torch = pytest.importorskip("torch")
+    Ct = torch.tensor(C0, dtype=torch.float64, requires_grad=True)
+    Mt = torch.tensor(M, dtype=torch.float64, requires_grad=True)
+    state, loss = Ct, torch.zeros((), dtype=torch.float64)
+    for t in range(T):
+        state = torch.matmul(state, Mt[:, t])
+        loss = loss + (state * torch.tensor(R[:, t])).sum()
+    loss.backward()
+    dM, dC0 = bwd_ref(M, R, C0, want_dC0=True)
+    np.testing.assert_allclose(dC0, Ct.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dM, Mt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    # no tokens: no gradient
+    _, dz = bwd_ref(M[:, :0], R[:, :0], C0, want_dC0=True)
+    assert np.array_equal(dz, np.zeros_like(C0))
+
+
+def test_scaled_ref_values():
+    P = np.array([[[3.0, -0.25], [0.0, 1.0]], [[0.0, 0.0], [0.0, 0.0]],
+                  [[1e200, 1.0], [-2e199, 0.0]], [[-0.5, 0.125], [0.25, 0.0]]])
+    Pm, E = scaled_ref(P)
+    # 3 = 0.75 * 2^2; a zero matrix stays 0 with exponent 0; -0.5 = -0.5 * 2^0
+    assert E[0] == 2 and np.array_equal(Pm[0], P[0] / 4)
+    assert E[1] == 0 and np.array_equal(Pm[1], P[1])
+    assert E[2] == math.frexp(1e200)[1] and E[3] == 0
+    for k in range(4):
+        assert np.array_equal(np.ldexp(Pm[k], int(E[k])), P[k])       # exact
+        big = np.abs(Pm[k]).max()
+        assert big == 0 or 0.5 <= big < 1.0
