@@ -222,14 +222,18 @@ def scaled_ref(P: np.ndarray):
 def rel_fro_err(test: np.ndarray, ref: np.ndarray) -> np.ndarray:
     """Per-matrix relative Frobenius error ||test - ref||_F / ||ref||_F in float64.
 
-    Reduces the last two axes.  A zero reference norm gives inf (or nan for
-    0/0), which every tolerance check treats as a failure.
+    Reduces the last two axes.  Both matrices are divided by the reference's
+    largest |entry| first (the ratio does not change), so that references far
+    beyond 1e154 do not overflow the squares.  A zero reference norm gives inf
+    (or nan for 0/0), which every tolerance check treats as a failure.
     """
     test = np.asarray(test, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    num = np.sqrt(np.sum((test - ref) ** 2, axis=(-2, -1)))
-    den = np.sqrt(np.sum(ref ** 2, axis=(-2, -1)))
-    with np.errstate(divide="ignore", invalid="ignore"):
+    scale = np.abs(ref).max(axis=(-2, -1), keepdims=True)
+    scale = np.where((scale > 0) & np.isfinite(scale), scale, 1.0)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        num = np.sqrt(np.sum(((test - ref) / scale) ** 2, axis=(-2, -1)))
+        den = np.sqrt(np.sum((ref / scale) ** 2, axis=(-2, -1)))
         return num / den
 
 

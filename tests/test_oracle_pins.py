@@ -332,6 +332,10 @@ def test_rel_fro_err_and_domain():
     test = ref.copy()
     test[1, 0, 0] += 3.0       # ||diff|| = 3, ||ref|| = 3
     np.testing.assert_allclose(rel_fro_err(test, ref), [0.0, 1.0])
+    # the same ratios for references far beyond the range where squares overflow
+    np.testing.assert_allclose(rel_fro_err(test * 1e300, ref * 1e300), [0.0, 1.0])
+    np.testing.assert_allclose(rel_fro_err(test * 1e-300, ref * 1e-300), [0.0, 1.0])
+    assert np.isinf(rel_fro_err(np.ones((2, 2)), np.zeros((2, 2))))
     big = np.full((2, 2), 2.0 ** 126)
     assert list(representable(np.stack([np.eye(2), big]))) == [True, False]
 
