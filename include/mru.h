@@ -191,6 +191,59 @@ mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float
                           int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
                           size_t ws_bytes, void* stream);
 
+/*
+ * Forward scan with a carried-in state and an optional exponent side output:
+ * segment continuation, token-by-token streaming and sequences whose products
+ * leave the fp32 range.  The running product is the same recurrence, state
+ * times new input ("MRU Update: ...", section "What MRU Actually Does"),
+ * started from a given state instead of I:
+ *   P_t = P_0 M_1 ... M_t,   P_0 = 2^carry_exp[b][h] * carry[b][h]  (t = 1..T).
+ *
+ * in         M [B][H][T][n][n], or x [B][H][T][n*n] when from_x != 0 (then
+ *            n in {4, 8}, as mru_scan_fwd_x).
+ * carry      [B][H][n][n] fp32, 16-byte aligned, or NULL for P_0 = I.
+ * carry_exp  [B][H] int32, or NULL for exponents 0.
+ * P          [B][H][T][n][n] fp32, written.
+ * P_exp      NULL: P holds P_t itself (IEEE fp32, +-inf where it overflows).
+ *            Otherwise [B][H][T] int32, written, and the scan is scaled:
+ *            P_t = 2^P_exp[t] * P[t] with the largest |entry| of P[t] in
+ *            [0.5, 1] (exactly 0 only if P_t is 0).  The running state is
+ *            rescaled by exact powers of two, so wherever P_t is a normal fp32
+ *            matrix, 2^P_exp[t] * P[t] carries the same bits as the unscaled
+ *            result, and beyond that range the scan keeps going.
+ * The carry out of a segment is its last token's (P, P_exp); passing it as
+ * the next segment's (carry, carry_exp) continues the scan.
+ * chunk, ws, ws_bytes as for mru_scan_fwd (the same workspace size).
+ * Errors: as mru_scan_fwd; MRU_ERR_ALIGN for a misaligned carry (16 bytes)
+ * or exponent array (4 bytes); MRU_ERR_ALIAS if P or P_exp overlaps an input,
+ * each other or ws.  B*H*T = 0 writes nothing.
+ */
+mru_status mru_scan_fwd_ex(const float* in, int32_t from_x, const float* carry,
+                           const int32_t* carry_exp, float* P, int32_t* P_exp, int64_t B,
+                           int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Backward of mru_scan_fwd_ex's unscaled form: with L = sum_t <dP_t, P_t> and
+ * P_t = P_0 M_1 ... M_t, writes dM = dL/dM_t (dM_1 = P_0^T Q_1) and, when
+ * dcarry is not NULL, dL/dP_0 = Q_1 M_1^T, where Q_t is the adjoint of P_t.
+ * in, from_x  as for mru_scan_fwd_ex.
+ * carry       [B][H][n][n] fp32 (P_0, with any exponent already applied) or
+ *             NULL for I.
+ * P, dP       [B][H][T][n][n] fp32: the plain forward outputs and dL/dP.
+ * dM          [B][H][T][n][n] fp32, written.
+ * dcarry      [B][H][n][n] fp32, written, or NULL.  For a segmented
+ *             sequence, the next segment's dcarry is added into this
+ *             segment's dP at its last token.
+ * chunk, ws, ws_bytes as for mru_scan_bwd.  Errors as mru_scan_bwd, plus
+ * MRU_ERR_ALIGN / MRU_ERR_ALIAS for carry and dcarry.  B*H*T = 0 writes
+ * nothing (dcarry included).
+ */
+mru_status mru_scan_bwd_ex(const float* in, int32_t from_x, const float* carry, const float* P,
+                           const float* dP, float* dM, float* dcarry, int64_t B, int64_t H,
+                           int64_t T, int32_t n, int32_t chunk, void* ws, size_t ws_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

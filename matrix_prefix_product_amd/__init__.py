@@ -89,6 +89,10 @@ def load_library():
     lib.mru_scan_fwd_x.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.mru_scan_bwd_x.restype = i32
     lib.mru_scan_bwd_x.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_fwd_ex.restype = i32
+    lib.mru_scan_fwd_ex.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_bwd_ex.restype = i32
+    lib.mru_scan_bwd_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     _LIB = lib
     return lib
 
@@ -292,6 +296,75 @@ def scan_bwd_x(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 
                                 ws_bytes, _stream_handle(x.device))
     _check(st, "mru_scan_bwd_x")
     return out
+
+
+def _inshape(inp: torch.Tensor, from_x: bool, n: int | None):
+    if from_x:
+        if n is None:
+            raise ValueError("n is required when the input is raw token vectors")
+        return (*_xshape(inp, n), n)
+    return _mshape(inp)
+
+
+def _carry_arg(carry, B, H, n, dev, name="carry"):
+    if carry is None:
+        return None
+    _require(carry, name, 4)
+    if tuple(carry.shape) != (B, H, n, n) or carry.device != dev:
+        raise ValueError(f"{name} must be [B,H,n,n] = {(B, H, n, n)} on the input's device")
+    return carry
+
+
+def scan_fwd_ex(inp: torch.Tensor, carry: torch.Tensor | None = None,
+                carry_exp: torch.Tensor | None = None, scaled: bool = False,
+                from_x: bool = False, n: int | None = None, chunk: int = 0,
+                workspace: torch.Tensor | None = None):
+    """P_t = P_0 M_1 ... M_t with P_0 = 2^carry_exp * carry (I when carry is None).
+
+    inp is M [B,H,T,n,n], or x [B,H,T,n*n] with from_x (n = 4, 8).  Returns P,
+    or (P, E) with scaled: P_t = 2^E[t] * P[t], max |P[t]| in [0.5, 1].  The
+    last token's (P, E) is the carry into the next segment."""
+    B, H, T, n = _inshape(inp, from_x, n)
+    dev = inp.device
+    carry = _carry_arg(carry, B, H, n, dev)
+    if carry_exp is not None:
+        if (carry_exp.dtype != torch.int32 or tuple(carry_exp.shape) != (B, H)
+                or carry_exp.device != dev or not carry_exp.is_contiguous()):
+            raise ValueError("carry_exp must be a contiguous int32 [B,H] tensor on the input's device")
+    P = torch.empty((B, H, T, n, n), dtype=torch.float32, device=dev)
+    E = torch.empty((B, H, T), dtype=torch.int32, device=dev) if scaled else None
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_FWD, chunk, dev, workspace)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.mru_scan_fwd_ex(_ptr(inp), int(from_x), _ptr(carry), _ptr(carry_exp), _ptr(P),
+                                 _ptr(E), B, H, T, n, chunk, _ptr(ws), ws_bytes, _stream_handle(dev))
+    _check(st, "mru_scan_fwd_ex")
+    return (P, E) if scaled else P
+
+
+def scan_bwd_ex(inp: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
+                carry: torch.Tensor | None = None, want_dcarry: bool = False,
+                from_x: bool = False, chunk: int = 0, workspace: torch.Tensor | None = None):
+    """dM of sum_t <dP_t, P_t> for P_t = P_0 M_1 ... M_t (P_0 = carry, or I),
+    and with want_dcarry also dL/dP_0.  P is the plain (unscaled) forward."""
+    _require(P, "P", 5)
+    n = P.shape[-1]
+    B, H, T, n = _inshape(inp, from_x, n)
+    dev = inp.device
+    for name, t in (("P", P), ("dP", dP)):
+        _require(t, name, 5)
+        if tuple(t.shape) != (B, H, T, n, n) or t.device != dev:
+            raise ValueError(f"{name} must be [B,H,T,n,n] on the input's device")
+    carry = _carry_arg(carry, B, H, n, dev)
+    dM = torch.empty_like(P)
+    dC = torch.zeros((B, H, n, n), dtype=torch.float32, device=dev) if want_dcarry else None
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_BWD, chunk, dev, workspace)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.mru_scan_bwd_ex(_ptr(inp), int(from_x), _ptr(carry), _ptr(P), _ptr(dP), _ptr(dM),
+                                 _ptr(dC), B, H, T, n, chunk, _ptr(ws), ws_bytes, _stream_handle(dev))
+    _check(st, "mru_scan_bwd_ex")
+    return (dM, dC) if want_dcarry else dM
 
 
 def flatten(P: torch.Tensor) -> torch.Tensor:

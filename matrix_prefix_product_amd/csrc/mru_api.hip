@@ -207,8 +207,11 @@ int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direct
 
 namespace {
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
-                         int32_t chunk, void* ws, size_t ws_bytes, void* stream, bool from_x) {
+                         int32_t chunk, void* ws, size_t ws_bytes, void* stream, bool from_x,
+                         const ScanCarry& cy) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
     if (from_x && n > 8 && !mfma_from_x_supported(n)) return MRU_ERR_SHAPE;
@@ -216,48 +219,28 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
     if (elems == 0) return MRU_OK;
     if (!M || !P) return MRU_ERR_NULL;
     if (!aligned16(M) || !aligned16(P)) return MRU_ERR_ALIGN;
+    if ((cy.carry && !aligned16(cy.carry)) || (cy.carry_exp && !aligned4(cy.carry_exp)) ||
+        (cy.out_exp && !aligned4(cy.out_exp)))
+        return MRU_ERR_ALIGN;
     const Plan p = make_plan(S, T, n, 0, chunk);
     if (!grid_ok(p, n, 0)) return MRU_ERR_SHAPE;
     const size_t bytes = size_t(elems) * sizeof(float);
-    if (overlap(M, bytes, P, bytes)) return MRU_ERR_ALIAS;
-    if (p.ws > 0) {
-        if (!ws) return MRU_ERR_WORKSPACE;
-        if (!aligned16(ws)) return MRU_ERR_ALIGN;
-        if (ws_bytes < p.ws) return MRU_ERR_WORKSPACE;
-        if (overlap(ws, p.ws, P, bytes) || overlap(ws, p.ws, M, bytes)) return MRU_ERR_ALIAS;
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (p.multi) {
-        const mru_status st = reset_ws(ws, p, s);
-        if (st != MRU_OK) return st;
-    }
-    if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x));
-    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x));
-}
-
-mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float* dM, int64_t B,
-                         int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
-                         size_t ws_bytes, void* stream, bool from_x) {
-    int64_t S, elems;
-    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
-    if (from_x && n > 8) return MRU_ERR_SHAPE;
-    if (chunk < 0) return MRU_ERR_CHUNK;
-    if (elems == 0) return MRU_OK;
-    if (!M || !P || !dP || !dM) return MRU_ERR_NULL;
-    if (!aligned16(M) || !aligned16(P) || !aligned16(dP) || !aligned16(dM)) return MRU_ERR_ALIGN;
-    const Plan p = make_plan(S, T, n, 1, chunk);
-    if (!grid_ok(p, n, 1)) return MRU_ERR_SHAPE;
-    const size_t bytes = size_t(elems) * sizeof(float);
-    if (overlap(dM, bytes, M, bytes) || overlap(dM, bytes, P, bytes) ||
-        overlap(dM, bytes, dP, bytes))
+    const size_t cbytes = size_t(S) * n * n * sizeof(float);
+    const size_t ebytes = size_t(S) * T * sizeof(int32_t);
+    if (overlap(M, bytes, P, bytes) || overlap(cy.carry, cbytes, P, bytes) ||
+        overlap(cy.carry_exp, size_t(S) * 4, P, bytes))
+        return MRU_ERR_ALIAS;
+    if (cy.out_exp && (overlap(cy.out_exp, ebytes, P, bytes) || overlap(cy.out_exp, ebytes, M, bytes) ||
+                       overlap(cy.out_exp, ebytes, cy.carry, cbytes) ||
+                       overlap(cy.out_exp, ebytes, cy.carry_exp, size_t(S) * 4)))
         return MRU_ERR_ALIAS;
     if (p.ws > 0) {
         if (!ws) return MRU_ERR_WORKSPACE;
         if (!aligned16(ws)) return MRU_ERR_ALIGN;
         if (ws_bytes < p.ws) return MRU_ERR_WORKSPACE;
-        if (overlap(ws, p.ws, dM, bytes) || overlap(ws, p.ws, M, bytes) ||
-            overlap(ws, p.ws, P, bytes) || overlap(ws, p.ws, dP, bytes))
+        if (overlap(ws, p.ws, P, bytes) || overlap(ws, p.ws, M, bytes) ||
+            overlap(ws, p.ws, cy.carry, cbytes) || overlap(ws, p.ws, cy.carry_exp, size_t(S) * 4) ||
+            overlap(ws, p.ws, cy.out_exp, ebytes))
             return MRU_ERR_ALIAS;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -266,8 +249,51 @@ mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float*
         const mru_status st = reset_ws(ws, p, s);
         if (st != MRU_OK) return st;
     }
-    if (n <= 8) return launched(launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x));
-    return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s));
+    if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
+    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
+}
+
+mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float* dM, int64_t B,
+                         int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                         size_t ws_bytes, void* stream, bool from_x, const ScanCarry& cy) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (from_x && n > 8) return MRU_ERR_SHAPE;
+    if (chunk < 0) return MRU_ERR_CHUNK;
+    if (elems == 0) return MRU_OK;
+    if (!M || !P || !dP || !dM) return MRU_ERR_NULL;
+    if (!aligned16(M) || !aligned16(P) || !aligned16(dP) || !aligned16(dM)) return MRU_ERR_ALIGN;
+    if ((cy.carry && !aligned16(cy.carry)) || (cy.dcarry && !aligned16(cy.dcarry)))
+        return MRU_ERR_ALIGN;
+    const Plan p = make_plan(S, T, n, 1, chunk);
+    if (!grid_ok(p, n, 1)) return MRU_ERR_SHAPE;
+    const size_t bytes = size_t(elems) * sizeof(float);
+    const size_t cbytes = size_t(S) * n * n * sizeof(float);
+    if (overlap(dM, bytes, M, bytes) || overlap(dM, bytes, P, bytes) ||
+        overlap(dM, bytes, dP, bytes) || overlap(dM, bytes, cy.carry, cbytes))
+        return MRU_ERR_ALIAS;
+    if (cy.dcarry && (overlap(cy.dcarry, cbytes, M, bytes) || overlap(cy.dcarry, cbytes, P, bytes) ||
+                      overlap(cy.dcarry, cbytes, dP, bytes) || overlap(cy.dcarry, cbytes, dM, bytes) ||
+                      overlap(cy.dcarry, cbytes, cy.carry, cbytes)))
+        return MRU_ERR_ALIAS;
+    if (p.ws > 0) {
+        if (!ws) return MRU_ERR_WORKSPACE;
+        if (!aligned16(ws)) return MRU_ERR_ALIGN;
+        if (ws_bytes < p.ws) return MRU_ERR_WORKSPACE;
+        if (overlap(ws, p.ws, dM, bytes) || overlap(ws, p.ws, M, bytes) ||
+            overlap(ws, p.ws, P, bytes) || overlap(ws, p.ws, dP, bytes) ||
+            overlap(ws, p.ws, cy.carry, cbytes) || overlap(ws, p.ws, cy.dcarry, cbytes))
+            return MRU_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (p.multi) {
+        const mru_status st = reset_ws(ws, p, s);
+        if (st != MRU_OK) return st;
+    }
+    if (n <= 8)
+        return launched(launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
+    return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, cy));
 }
 
 }  // namespace
@@ -276,24 +302,45 @@ extern "C" {
 
 mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
                         int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
-    return scan_fwd_impl(M, P, B, H, T, n, chunk, ws, ws_bytes, stream, false);
+    return scan_fwd_impl(M, P, B, H, T, n, chunk, ws, ws_bytes, stream, false, ScanCarry{});
 }
 
 mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
                           int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
-    return scan_fwd_impl(x, P, B, H, T, n, chunk, ws, ws_bytes, stream, true);
+    return scan_fwd_impl(x, P, B, H, T, n, chunk, ws, ws_bytes, stream, true, ScanCarry{});
 }
 
 mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
                         int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
                         size_t ws_bytes, void* stream) {
-    return scan_bwd_impl(M, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, false);
+    return scan_bwd_impl(M, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, false, ScanCarry{});
 }
 
 mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float* dM, int64_t B,
                           int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
                           size_t ws_bytes, void* stream) {
-    return scan_bwd_impl(x, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, true);
+    return scan_bwd_impl(x, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, true, ScanCarry{});
+}
+
+mru_status mru_scan_fwd_ex(const float* in, int32_t from_x, const float* carry,
+                           const int32_t* carry_exp, float* P, int32_t* P_exp, int64_t B,
+                           int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
+                           size_t ws_bytes, void* stream) {
+    ScanCarry cy;
+    cy.carry = carry;
+    cy.carry_exp = carry_exp;
+    cy.out_exp = P_exp;
+    return scan_fwd_impl(in, P, B, H, T, n, chunk, ws, ws_bytes, stream, from_x != 0, cy);
+}
+
+mru_status mru_scan_bwd_ex(const float* in, int32_t from_x, const float* carry, const float* P,
+                           const float* dP, float* dM, float* dcarry, int64_t B, int64_t H,
+                           int64_t T, int32_t n, int32_t chunk, void* ws, size_t ws_bytes,
+                           void* stream) {
+    ScanCarry cy;
+    cy.carry = carry;
+    cy.dcarry = dcarry;
+    return scan_bwd_impl(in, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, from_x != 0, cy);
 }
 
 }  // extern "C"

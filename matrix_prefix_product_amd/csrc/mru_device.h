@@ -26,6 +26,8 @@
 
 namespace mru {
 
+constexpr int kNoExp = INT32_MIN;  // max_exp of an all-zero set
+
 constexpr uint32_t kFlagEmpty = 0;
 constexpr uint32_t kFlagAgg = 1;
 constexpr uint32_t kFlagPrefix = 2;
@@ -41,6 +43,8 @@ constexpr uint32_t kSpinLimit = 1u << 21;
 //   [0, 256)          header: ticket counter, status word
 //   flags             uint32[nchunks]
 //   slot 0 .. slot k  nchunks * n * n elements of the chain's accumulator type
+//   exponents         int32[nslots][nchunks]: power-of-two exponents of the
+//                     slots' matrices (used by the scaled forward scan only)
 struct WsHeader {
     uint32_t ticket;
     uint32_t status;
@@ -52,6 +56,7 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~si
 struct WsLayout {
     size_t flags_off;
     size_t slot_off[3];
+    size_t exp_off;
     size_t total;
 };
 
@@ -64,6 +69,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t nchunks, int n, int elem_b
         L.slot_off[i] = off;
         if (i < nslots) off = align256(off + size_t(nchunks) * size_t(n) * n * elem_bytes);
     }
+    L.exp_off = off;
+    off = align256(off + size_t(nchunks) * size_t(nslots) * sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -178,6 +185,25 @@ __device__ inline void wait_range_nonempty(const uint32_t* flags, int64_t lo, in
             __builtin_amdgcn_s_sleep(2);
         }
     }
+}
+
+// frexp exponent: a finite nonzero v with exponent e has 2^(e-1) <= |v| < 2^e.
+// max_exp folds the exponent of a nonzero v into a running maximum that starts
+// at kNoExp (so an all-zero set keeps kNoExp).
+__device__ inline int frexp_exp(float v) { return __builtin_amdgcn_frexp_expf(v); }
+__device__ inline int frexp_exp(double v) { return __builtin_amdgcn_frexp_exp(v); }
+
+template <class T>
+__device__ inline int max_exp(int e, T v) {
+    return v != T(0) ? max(e, frexp_exp(v)) : e;
+}
+
+// Maximum of e over groups of W consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ inline int group_max(int e) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) e = max(e, __shfl_xor(e, m, 64));
+    return e;
 }
 
 // Kernel that clears the workspace header and flags before a multi-chunk scan.

@@ -174,6 +174,56 @@ __device__ inline void load_a_direct(typename Mf<N>::aop_t& a, const T* p) {
         }
 }
 
+// Scaled state (scaled forward scan): the accumulators hold S^T with
+// P = 2^ex S.  renorm_acc multiplies S by a power of two (exact) so that its
+// largest entry has magnitude in [0.5, 1) and adds the shift to ex (the same in
+// every lane).  An all-zero S is left as it is.
+template <int N>
+__device__ inline void renorm_acc(typename Mf<N>::vec_t& X, int& ex) {
+    int e = kNoExp;
+#pragma unroll
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e = max_exp(e, X.t[I][J][r]);
+    e = group_max<64>(e);
+    if (e == kNoExp) return;
+#pragma unroll
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X.t[I][J][r] = ldexp(X.t[I][J][r], -e);
+    ex += e;
+}
+
+// Transposed carried-in state of sequence s (2^carry_exp * carry, or I).
+template <int N, bool SC>
+__device__ inline typename Mf<N>::vec_t init_acc(int& ex, const ScanCarry& cy, int64_t s) {
+    const int l = threadIdx.x & 63;
+    ex = 0;
+    typename Mf<N>::vec_t X;
+    if (!cy.carry) {
+        X = videntity<N>(l);
+    } else {
+        X = load_acc_rows<N, float>(cy.carry + s * N * N);
+        const int ce = cy.carry_exp ? cy.carry_exp[s] : 0;
+        if (SC) {
+            ex = ce;
+        } else if (ce != 0) {
+#pragma unroll
+            for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+                for (int J = 0; J < Mf<N>::NT; ++J)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) X.t[I][J][r] = ldexp(X.t[I][J][r], ce);
+        }
+    }
+    if constexpr (SC) renorm_acc<N>(X, ex);
+    return X;
+}
+
 // Workspace (look-back) accessors: the same layouts as store_acc_rows /
 // load_acc_rows / load_a_transposed, element by element through ws_store /
 // ws_load so that other XCDs see them coherently.
@@ -247,9 +297,9 @@ constexpr int walk_depth() { return N == 16 ? 4 : (BWD ? 1 : 2); }
 // operands are consumed.  Loads are unconditional (addresses clamped into the
 // chunk), and the main loop runs whole blocks of PF tokens, so every ring slot
 // stays in fixed registers and PF tokens of loads stay in flight.
-template <int N, int PF, bool WRITE>
-__device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
-                          float* __restrict__ P, int64_t base, int len) {
+template <int N, int PF, bool WRITE, bool SC>
+__device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
+                          float* __restrict__ P, int32_t* __restrict__ pexp, int64_t base, int len) {
     using F = Mf<N>;
     constexpr int NT = F::NT;
     constexpr int NN = F::NN;
@@ -283,7 +333,11 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
             for (int e = 0; e < NA; ++e) ring[p][e] = Mb[u * NN + aoff[e]];
         }
         X = chain_step<N>(a, X, vzero<N>());
-        if (WRITE) store_acc_rows<N, float>(P + (base + t) * NN, X);
+        if constexpr (SC) renorm_acc<N>(X, ex);
+        if (WRITE) {
+            store_acc_rows<N, float>(P + (base + t) * NN, X);
+            if (SC && l == 0) pexp[base + t] = ex;
+        }
     };
     int t0 = 0;
     for (; t0 + PF <= len; t0 += PF) {
@@ -299,8 +353,8 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, const float* __restrict__ M,
 // entries into a register buffer of KR tokens (loads issued PF tokens ahead,
 // clamped into the chunk) and the apply pass reuses them, so each input matrix
 // is read from HBM once even when the chunk needs a carry.
-template <int N, int KR, int PF>
-__device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, const float* __restrict__ M,
+template <int N, int KR, int PF, bool SC>
+__device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
                                 int64_t base, int len, float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
     using F = Mf<N>;
     constexpr int NT = F::NT;
@@ -334,13 +388,15 @@ __device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, const float* __restric
 #pragma unroll
             for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(buf[t][e]);
             X = chain_step<N>(a, X, vzero<N>());
+            if constexpr (SC) renorm_acc<N>(X, ex);
         }
     }
 }
 
-template <int N, int KR>
-__device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, float* __restrict__ P, int64_t base,
-                                 int len, const float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
+template <int N, int KR, bool SC>
+__device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __restrict__ P,
+                                 int32_t* __restrict__ pexp, int64_t base, int len,
+                                 const float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
     using F = Mf<N>;
     constexpr int NT = F::NT;
     constexpr int NA = NT * NT * 4;
@@ -351,16 +407,18 @@ __device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, float* __restrict__ P
 #pragma unroll
             for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(buf[t][e]);
             X = chain_step<N>(a, X, vzero<N>());
+            if constexpr (SC) renorm_acc<N>(X, ex);
             store_acc_rows<N, float>(P + (base + t) * F::NN, X);
+            if (SC && (threadIdx.x & 63) == 0) pexp[base + t] = ex;
         }
     }
 }
 
-template <int N, int PF, int KR>
+template <int N, int PF, int KR, bool SC>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
-                                                      unsigned char* __restrict__ ws) {
+                                                      unsigned char* __restrict__ ws, ScanCarry cy) {
     using F = Mf<N>;
     using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
@@ -374,27 +432,34 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
     const Chunk ch = chunk_at(cidx, nch, K, T, false);
+    const int64_t seq = cidx / nch;
 
-    vec_t X = videntity<N>(l);
+    int ex = 0;
     if (!multi) {
-        fwd_sweep<N, PF, true>(X, M, P, ch.base, ch.len);
+        vec_t X = init_acc<N, SC>(ex, cy, seq);
+        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len);
         return;
     }
     const WsLayout L = ws_layout(nchunks, N, sizeof(acc_t), 2);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags_off);
     acc_t* agg = reinterpret_cast<acc_t*>(ws + L.slot_off[0]);
     acc_t* incl = reinterpret_cast<acc_t*>(ws + L.slot_off[1]);
+    int32_t* agg_exp = reinterpret_cast<int32_t*>(ws + L.exp_off);
+    int32_t* incl_exp = agg_exp + nchunks;
     const int64_t c = ch.c;
     const int64_t k = ch.pos;
     const int64_t first = c - k % Z;
 
-    // 1. chunk aggregate
+    // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised matrix)
+    vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0)
-        fwd_pass_retain<N, KR, PF>(X, M, ch.base, ch.len, buf);
+        fwd_pass_retain<N, KR, PF, SC>(X, ex, M, ch.base, ch.len, buf);
     else
-        fwd_sweep<N, PF, false>(X, M, P, ch.base, ch.len);
+        fwd_sweep<N, PF, false, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len);
+    const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
+    if (SC && l == 0) ws_store(&agg_exp[c], int32_t(a_ex));
     fence_release();
     if (l == 0) store_flag(&flags[c], kFlagAgg);
 
@@ -403,6 +468,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     fence_acquire();
     typename F::aop_t a;
     X = videntity<N>(l);
+    int l_ex = 0;
     // aggregates are loaded kWalk at a time so their loads are in flight together
     constexpr int kWalk = walk_depth<N, false>();
     for (int64_t j0 = first; j0 < c; j0 += kWalk) {
@@ -412,31 +478,54 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
             if (j0 + d < c) ws_load_a_transposed<N>(w[d], agg + (j0 + d) * NN);
 #pragma unroll
         for (int d = 0; d < kWalk; ++d)
-            if (j0 + d < c) X = chain_step<N>(w[d], X, vzero<N>());
+            if (j0 + d < c) {
+                X = chain_step<N>(w[d], X, vzero<N>());
+                if constexpr (SC) {
+                    l_ex += ws_load(&agg_exp[j0 + d]);
+                    renorm_acc<N>(X, l_ex);
+                }
+            }
     }
 
     // 3. carry^T = Lt * prefix^T, prefix from the previous super's last chunk
-    if (k >= Z) {
+    //    (first super: the carried-in state, if any)
+    if (k >= Z || cy.carry) {
         store_acc_rows<N, acc_t>(xl, X);  // L row-major
-        wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
-        fence_acquire();
+        vec_t pre;
+        if (k >= Z) {
+            wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
+            fence_acquire();
+            pre = ws_load_acc_rows<N>(incl + (first - 1) * NN);
+            ex = SC ? ws_load(&incl_exp[first - 1]) : 0;
+        } else {
+            pre = init_acc<N, SC>(ex, cy, seq);
+        }
         __syncthreads();
         load_a_transposed<N, acc_t>(a, xl);
-        X = chain_step<N>(a, ws_load_acc_rows<N>(incl + (first - 1) * NN), vzero<N>());
+        X = chain_step<N>(a, pre, vzero<N>());
+        if constexpr (SC) {
+            ex += l_ex;
+            renorm_acc<N>(X, ex);
+        }
+    } else {
+        ex = l_ex;
     }
     if (k % Z == Z - 1 && k + 1 < nch) {
         ws_load_a_transposed<N>(a, agg + c * NN);
-        const vec_t inc = chain_step<N>(a, X, vzero<N>());
+        vec_t inc = chain_step<N>(a, X, vzero<N>());
+        int i_ex = ex + a_ex;
+        if constexpr (SC) renorm_acc<N>(inc, i_ex);
         ws_store_acc_rows<N>(incl + c * NN, inc);
+        if (SC && l == 0) ws_store(&incl_exp[c], int32_t(i_ex));
         fence_release();
         if (l == 0) store_flag(&flags[c], kFlagPrefix);
     }
 
     // 4. re-run from the carry
     if constexpr (KR > 0)
-        fwd_apply_retain<N, KR>(X, P, ch.base, ch.len, buf);
+        fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf);
     else
-        fwd_sweep<N, PF, true>(X, M, P, ch.base, ch.len);
+        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -449,7 +538,7 @@ template <int N, int PF, bool GRAD>
 __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                           const float* __restrict__ M, const float* __restrict__ P,
                           const float* __restrict__ dP, float* __restrict__ dM, double* tr,
-                          int64_t base, int64_t t0, int len, int64_t T) {
+                          int64_t base, int64_t t0, int len, int64_t T, const ScanCarry& cy) {
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NT = F::NT;
@@ -527,7 +616,19 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
         }
         if constexpr (GRAD) {
             float* out = dM + (base + pos) * NN;
-            if (pos >= lo_p) {
+            const int64_t s0 = base - t0;  // token index of the sequence's first token
+            if (pos < lo_p && cy.carry) {
+                // t = 0 with a carried-in state: P_{-1} = carry (B operand layout)
+                const float* cs = cy.carry + (s0 / T) * NN;
+#pragma unroll
+                for (int K = 0; K < NT; ++K)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            bv.t[K][J][b] = double(cs[(16 * K + trow(l, b)) * N + 16 * J + c]);
+            }
+            if (pos >= lo_p || cy.carry) {
                 // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
                 __syncthreads();
 #pragma unroll
@@ -551,6 +652,12 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
             } else {
                 store_acc_rows<N, float>(out, G);  // t = 0: P_{-1} = I
             }
+            if (pos < lo_p && cy.dcarry) {
+                // dL/dP_{-1} = Q_0 M_0^T, i.e. its transpose is M_0 G_0
+                typename F::aop_t am;
+                load_a_direct<N, float>(am, Mb + int64_t(pos) * NN);
+                store_acc_rows<N, float>(cy.dcarry + (s0 / T) * NN, chain_step<N>(am, G, vzero<N>()));
+            }
         }
     };
 #pragma unroll
@@ -571,7 +678,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
                                                       const float* __restrict__ dP,
                                                       float* __restrict__ dM, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
-                                                      unsigned char* __restrict__ ws) {
+                                                      unsigned char* __restrict__ ws, ScanCarry cy) {
     using F = Mf<N>;
     using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
@@ -590,7 +697,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     vec_t G = vzero<N>();
     vec_t W = videntity<N>(l);
     if (!multi) {
-        bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T);
+        bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
         return;
     }
     // Chunks run in reverse token order (position r = 0 is the sequence's last
@@ -607,7 +714,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     const bool later = r >= Z;
 
     // 1. affine aggregate
-    bwd_sweep<N, PF, false>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T);
+    bwd_sweep<N, PF, false>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
     ws_store_acc_rows<N>(sbl + c * NN, G);
     ws_store_acc_rows<N>(swt + c * NN, W);
     fence_release();
@@ -655,22 +762,27 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     }
 
     // 4. re-run from the carry, writing dM
-    bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T);
+    bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
 }
 
 template <int N, int PF, int KR>
 hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
-                   int64_t Z, void* ws, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR>), dim3(unsigned(S * nch)), dim3(64), 0, stream,
-                       M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+                   int64_t Z, void* ws, hipStream_t stream, const ScanCarry& cy) {
+    if (cy.out_exp)
+        hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR, true>), dim3(unsigned(S * nch)), dim3(64), 0,
+                           stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
+    else
+        hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR, false>), dim3(unsigned(S * nch)), dim3(64), 0,
+                           stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
 template <int N, int PF>
 hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
-                   int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
+                   int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream,
+                   const ScanCarry& cy) {
     hipLaunchKernelGGL((bwd_mfma_kernel<N, PF>), dim3(unsigned(S * nch)), dim3(64), 0, stream, M,
-                       P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+                       P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
@@ -684,24 +796,26 @@ constexpr int kRetain16 = MRU_RETAIN16;
 
 int mfma_retain_tokens(int n) { return n == 16 ? kRetain16 : 0; }
 
-bool mfma_from_x_supported(int n) { return false; }
+bool mfma_from_x_supported(int) { return false; }
 
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x) {
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
+                           const ScanCarry& cy) {
     if (from_x) return hipErrorInvalidValue;
     if (n == 16) {
-        if (nch > 1 && K <= kRetain16) return run_fwd<16, 16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream);
-        return run_fwd<16, 16, 0>(M, P, S, T, K, nch, Z, ws, stream);
+        if (nch > 1 && K <= kRetain16)
+            return run_fwd<16, 16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd<16, 16, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
-    if (n == 32) return run_fwd<32, 4, 0>(M, P, S, T, K, nch, Z, ws, stream);
+    if (n == 32) return run_fwd<32, 4, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream) {
-    if (n == 16) return run_bwd<16, 8>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
-    if (n == 32) return run_bwd<32, 2>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+                           hipStream_t stream, const ScanCarry& cy) {
+    if (n == 16) return run_bwd<16, 8>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+    if (n == 32) return run_bwd<32, 2>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     return hipErrorInvalidValue;
 }
 

@@ -269,10 +269,9 @@ __device__ inline void load_vec(float (&v)[N], const float* src) {
 
 // st <- st * (L diag(e) U), in place per row.
 template <int N, int R>
-__device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const float* e) {
-    float x[N * N], ev[N];
+__device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const float (&ev)[N]) {
+    float x[N * N];
     load_matrix<N>(x, X);
-    load_vec<N>(ev, e);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         // times L: r_j += sum_{i > j} r_i X_ij, ascending j reads only untouched r_i
@@ -292,10 +291,9 @@ __device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const f
 
 // st <- st * (L diag(e) U)^T = st * U^T diag(e) L^T, in place per row.
 template <int N, int R>
-__device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X, const float* e) {
-    float x[N * N], ev[N];
+__device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X, const float (&ev)[N]) {
+    float x[N * N];
     load_matrix<N>(x, X);
-    load_vec<N>(ev, e);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         // times U^T: r_j += sum_{k > j} r_k X_jk, ascending j
@@ -313,13 +311,56 @@ __device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X, const
     }
 }
 
+// Scaled state (scaled forward scan): a chain's rows hold S with P = 2^ex S.
+// renorm_rows multiplies S by a power of two (exact) so that its largest entry
+// has magnitude in [0.5, 1) and adds the shift to ex; ex is the same in every
+// lane of the chain.  An all-zero S is left as it is.
+template <int N, int R>
+__device__ inline void renorm_rows(float (&st)[R][N], int& ex) {
+    int e = kNoExp;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) e = max_exp(e, st[r][j]);
+    e = group_max<N / R>(e);
+    if (e == kNoExp) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[r][j] = ldexpf(st[r][j], -e);
+    ex += e;
+}
+
+// The lane's rows of a sequence's carried-in state (2^carry_exp * carry, or I).
+template <int N, int R, bool SC>
+__device__ inline void init_rows(float (&st)[R][N], int& ex, const ScanCarry& cy, int64_t s,
+                                 int li) {
+    ex = 0;
+    if (!cy.carry) {
+        set_identity_rows<N, R>(st, li * R);
+        if constexpr (SC) renorm_rows<N, R>(st, ex);
+        return;
+    }
+    load_rows<N, R>(st, cy.carry + s * N * N + li * R * N);
+    const int ce = cy.carry_exp ? cy.carry_exp[s] : 0;
+    if constexpr (SC) {
+        ex = ce;
+        renorm_rows<N, R>(st, ex);
+    } else if (ce != 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < N; ++j) st[r][j] = ldexpf(st[r][j], ce);
+    }
+}
+
 // One sweep of a forward chain over its chunk: st <- st * M_t for each token,
 // optionally storing the rows of every P_t.  With FX the input is x and each
 // step multiplies by M_t's factors (se holds the staged tokens' e).
-template <int N, int R, int TB, bool WRITE, bool FX>
-__device__ void fwd_sweep(float (&st)[R][N], const float* __restrict__ M, float* __restrict__ P,
-                          float* lds, float* se, const ChainInfo* info, int g, int li, int maxlen,
-                          int64_t T) {
+template <int N, int R, int TB, bool WRITE, bool FX, bool SC>
+__device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ M,
+                          float* __restrict__ P, int32_t* __restrict__ pexp, float* lds, float* se,
+                          const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
     float4 reg[V::LD];
@@ -339,23 +380,29 @@ __device__ void fwd_sweep(float (&st)[R][N], const float* __restrict__ M, float*
             if (pos < me.len) {
                 const float* slot = lds + g * V::CH_STRIDE + tau * V::NN;
                 if constexpr (FX) {
-                    rows_times_ldu<N, R>(st, slot, se + (g * TB + tau) * N);
+                    float ev[N];
+                    load_vec<N>(ev, se + (g * TB + tau) * N);
+                    rows_times_ldu<N, R>(st, slot, ev);
                 } else {
                     float m[V::NN];
                     load_matrix<N>(m, slot);
                     rows_times<N, R>(st, m);
                 }
-                if (WRITE) store_rows<N, R>(P + (me.base + pos) * V::NN + li * R * N, st);
+                if constexpr (SC) renorm_rows<N, R>(st, ex);
+                if (WRITE) {
+                    store_rows<N, R>(P + (me.base + pos) * V::NN + li * R * N, st);
+                    if (SC && li == 0) pexp[me.base + pos] = ex;
+                }
             }
         }
     }
 }
 
-template <int N, int R, int TB, bool FX>
+template <int N, int R, int TB, bool FX, bool SC>
 __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
-                                                      unsigned char* __restrict__ ws) {
+                                                      unsigned char* __restrict__ ws, ScanCarry cy) {
     using V = Valu<N, R, TB>;
     __shared__ float lds[V::G * V::CH_STRIDE];
     __shared__ float se[FX ? V::G * TB * N : 4];
@@ -377,9 +424,12 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     for (int i = 0; i < V::G; ++i) maxlen = max(maxlen, info[i].len);
 
     float st[R][N];
-    set_identity_rows<N, R>(st, li * R);
+    int ex = 0;
+    const int64_t c = cbase + g;
+    const int64_t seq = c < nchunks ? c / nch : 0;  // idle chains read sequence 0, write nothing
     if (!multi) {
-        fwd_sweep<N, R, TB, true, FX>(st, M, P, lds, se, info, g, li, maxlen, T);
+        init_rows<N, R, SC>(st, ex, cy, seq, li);
+        fwd_sweep<N, R, TB, true, FX, SC>(st, ex, M, P, cy.out_exp, lds, se, info, g, li, maxlen, T);
         return;
     }
 
@@ -389,14 +439,18 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags_off);
     float* agg = reinterpret_cast<float*>(ws + L.slot_off[0]);
     float* incl = reinterpret_cast<float*>(ws + L.slot_off[1]);
-    const int64_t c = cbase + g;
+    int32_t* agg_exp = reinterpret_cast<int32_t*>(ws + L.exp_off);
+    int32_t* incl_exp = agg_exp + nchunks;
     const int64_t k = c - (c / nch) * nch;
     const int64_t first = c - k % Z;  // first chunk of the super (same for the whole wave)
     const bool later_super = k >= Z;  // wave-uniform
 
-    // 1. chunk aggregate
-    fwd_sweep<N, R, TB, false, FX>(st, M, P, lds, se, info, g, li, maxlen, T);
+    // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised rows)
+    set_identity_rows<N, R>(st, li * R);
+    fwd_sweep<N, R, TB, false, FX, SC>(st, ex, M, P, cy.out_exp, lds, se, info, g, li, maxlen, T);
+    const int a_ex = ex;
     ws_store_rows<N, R>(agg + c * V::NN + li * R * N, st);
+    if (SC && li == 0) ws_store(&agg_exp[c], int32_t(a_ex));
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
 
@@ -404,27 +458,44 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     wait_range_nonempty(flags, first, cbase, hdr);
     fence_acquire();
     float lrow[R][N];
+    int l_ex = 0;
     set_identity_rows<N, R>(lrow, li * R);
     float m[V::NN];
     for (int64_t j = first; j < c; ++j) {
         ws_load_matrix<N>(m, agg + j * V::NN);
         rows_times<N, R>(lrow, m);
+        if constexpr (SC) {
+            l_ex += ws_load(&agg_exp[j]);
+            renorm_rows<N, R>(lrow, l_ex);
+        }
     }
 
-    // 3. carry = (prefix of the previous super) * lrow
-    if (later_super) {
-        wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
-        fence_acquire();
+    // 3. carry = (prefix of the previous super, or the carried-in state) * lrow
+    if (later_super || cy.carry) {  // wave-uniform
         store_rows<N, R>(xch + g * V::NN + li * R * N, lrow);
+        if (later_super) {
+            wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
+            fence_acquire();
+        }
         __syncthreads();
         load_matrix<N>(m, xch + g * V::NN);
-        ws_load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
+        if (later_super) {
+            ws_load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
+            ex = SC ? ws_load(&incl_exp[first - 1]) : 0;
+        } else {
+            init_rows<N, R, SC>(st, ex, cy, seq, li);
+        }
         rows_times<N, R>(st, m);
+        if constexpr (SC) {
+            ex += l_ex;
+            renorm_rows<N, R>(st, ex);
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int q = 0; q < N; ++q) st[r][q] = lrow[r][q];
+        ex = l_ex;
     }
     const bool boundary = (k % Z == Z - 1) && (k + 1 < nch);
     if (boundary) {
@@ -435,13 +506,16 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
             for (int q = 0; q < N; ++q) inc[r][q] = st[r][q];
         ws_load_matrix<N>(m, agg + c * V::NN);
         rows_times<N, R>(inc, m);
+        int i_ex = ex + a_ex;
+        if constexpr (SC) renorm_rows<N, R>(inc, i_ex);
         ws_store_rows<N, R>(incl + c * V::NN + li * R * N, inc);
+        if (SC && li == 0) ws_store(&incl_exp[c], int32_t(i_ex));
     }
     fence_release();
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from its carry and write every prefix
-    fwd_sweep<N, R, TB, true, FX>(st, M, P, lds, se, info, g, li, maxlen, T);
+    fwd_sweep<N, R, TB, true, FX, SC>(st, ex, M, P, cy.out_exp, lds, se, info, g, li, maxlen, T);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -457,10 +531,12 @@ template <int N, int R, int TB, bool GRAD, bool FX>
 __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
                           const float* __restrict__ P, const float* __restrict__ dP,
                           float* __restrict__ dM, float* lds, float* se, float* qx,
-                          const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
+                          const ChainInfo* info, int g, int li, int maxlen, int64_t T,
+                          const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
     constexpr int ARR = GRAD ? 3 : 2;  // staged arrays: M(t+1), dP(t), [P(t-1)]
     const ChainInfo me = info[g];
+    const int64_t s0 = me.base - me.t0;  // token index of the sequence's first token
     float4 rm[V::LD], rr[V::LD], rp[V::LD];
     auto load_all = [&](int blk) {
         stage_load<N, R, TB, true>(rm, M, info, blk, +1, T);
@@ -491,8 +567,10 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
             if (live) {
                 if (tseq + 1 < T) {
                     if constexpr (FX) {
-                        rows_times_ldu_t<N, R>(q, mslot, eslot);
-                        if (!GRAD) rows_times_ldu_t<N, R>(w, mslot, eslot);
+                        float ev[N];
+                        load_vec<N>(ev, eslot);
+                        rows_times_ldu_t<N, R>(q, mslot, ev);
+                        if (!GRAD) rows_times_ldu_t<N, R>(w, mslot, ev);
                     } else {
                         float m[V::NN];
                         load_matrix<N>(m, mslot);
@@ -512,9 +590,8 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                 __syncthreads();
                 if (live) {
                     float d[R][N];
-                    if (tseq > 0) {
-                        const float* pslot =
-                            lds + 2 * V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN;
+                    // d = Pprev^T Q_t for the lane's rows, Pprev row-major at src
+                    auto times_prev = [&](const float* src) {
                         float qa[V::NN];
                         load_matrix<N>(qa, qx + g * V::NN);
                         set_zero_rows<N, R>(d);
@@ -522,12 +599,17 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                         for (int ii = 0; ii < N; ++ii) {
                             float pc[R];
 #pragma unroll
-                            for (int r = 0; r < R; ++r) pc[r] = pslot[ii * N + li * R + r];
+                            for (int r = 0; r < R; ++r) pc[r] = src[ii * N + li * R + r];
 #pragma unroll
                             for (int r = 0; r < R; ++r)
 #pragma unroll
                                 for (int j = 0; j < N; ++j) d[r][j] = fmaf(pc[r], qa[ii * N + j], d[r][j]);
                         }
+                    };
+                    if (tseq > 0) {
+                        times_prev(lds + 2 * V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN);
+                    } else if (cy.carry) {
+                        times_prev(cy.carry + (s0 / T) * V::NN);  // P_0 = carried-in state
                     } else {
 #pragma unroll
                         for (int r = 0; r < R; ++r)
@@ -535,6 +617,27 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                             for (int j = 0; j < N; ++j) d[r][j] = q[r][j];
                     }
                     store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
+                    if (tseq == 0 && cy.dcarry) {
+                        // dL/dP_0 = Q_1 M_1^T, M_1 this token's input
+                        float dc[R][N];
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int j = 0; j < N; ++j) dc[r][j] = q[r][j];
+                        const float* m1 = M + s0 * V::NN;
+                        if constexpr (FX) {
+                            float ev[N];
+                            const float mean = ldu_mean<N>(m1);
+#pragma unroll
+                            for (int kk = 0; kk < N; ++kk) ev[kk] = expf(m1[kk * N + kk] - mean);
+                            rows_times_ldu_t<N, R>(dc, m1, ev);
+                        } else {
+                            float mm[V::NN];
+                            load_matrix<N>(mm, m1);
+                            rows_times_t<N, R>(dc, mm);
+                        }
+                        store_rows<N, R>(cy.dcarry + (s0 / T) * V::NN + li * R * N, dc);
+                    }
                 }
             }
         }
@@ -547,7 +650,8 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
                                                       const float* __restrict__ dP,
                                                       float* __restrict__ dM, int64_t S,
                                                       int64_t T, int64_t K, int64_t nch,
-                                                      int64_t Z, unsigned char* __restrict__ ws) {
+                                                      int64_t Z, unsigned char* __restrict__ ws,
+                                                      ScanCarry cy) {
     using V = Valu<N, R, TB>;
     __shared__ float lds[3 * V::G * V::CH_STRIDE];
     __shared__ float se[FX ? V::G * TB * N : 4];
@@ -572,7 +676,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     set_zero_rows<N, R>(q);
     set_identity_rows<N, R>(w, li * R);
     if (!multi) {
-        bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T);
+        bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T, cy);
         return;
     }
 
@@ -590,7 +694,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     const bool later_super = r >= Z;
 
     // 1. affine aggregate of the chunk
-    bwd_sweep<N, R, TB, false, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T);
+    bwd_sweep<N, R, TB, false, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T, cy);
     ws_store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
     ws_store_rows<N, R>(swt + c * V::NN + li * R * N, w);
     fence_release();
@@ -646,26 +750,34 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from the carry and write dM
-    bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T);
+    bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T, cy);
 }
 
-template <int N, int R, int TB, bool FX>
+template <int N, int R, int TB, bool FX, bool SC>
 hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
-                   int64_t Z, void* ws, hipStream_t stream) {
+                   int64_t Z, void* ws, hipStream_t stream, const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
     const int64_t waves = (S * nch + V::G - 1) / V::G;
-    hipLaunchKernelGGL((fwd_valu_kernel<N, R, TB, FX>), dim3(unsigned(waves)), dim3(64), 0, stream,
-                       M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+    hipLaunchKernelGGL((fwd_valu_kernel<N, R, TB, FX, SC>), dim3(unsigned(waves)), dim3(64), 0,
+                       stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
 template <int N, int R, int TB, bool FX>
+hipError_t run_fwd_any(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
+                       int64_t Z, void* ws, hipStream_t stream, const ScanCarry& cy) {
+    if (cy.out_exp) return run_fwd<N, R, TB, FX, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+    return run_fwd<N, R, TB, FX, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
+}
+
+template <int N, int R, int TB, bool FX>
 hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
-                   int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream) {
+                   int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream,
+                   const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
     const int64_t waves = (S * nch + V::G - 1) / V::G;
     hipLaunchKernelGGL((bwd_valu_kernel<N, R, TB, FX>), dim3(unsigned(waves)), dim3(64), 0, stream,
-                       M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws));
+                       M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
@@ -692,28 +804,31 @@ int valu_chains_per_wave(int n, int dir) {
 }
 
 hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x) {
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
+                           const ScanCarry& cy) {
     if (n == 4) {
-        if (from_x) return run_fwd<MRU_VALU_CFG4, true>(M, P, S, T, K, nch, Z, ws, stream);
-        return run_fwd<MRU_VALU_CFG4, false>(M, P, S, T, K, nch, Z, ws, stream);
+        if (from_x) return run_fwd_any<MRU_VALU_CFG4, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd_any<MRU_VALU_CFG4, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 8) {
-        if (from_x) return run_fwd<MRU_VALU_CFG8, true>(M, P, S, T, K, nch, Z, ws, stream);
-        return run_fwd<MRU_VALU_CFG8, false>(M, P, S, T, K, nch, Z, ws, stream);
+        if (from_x) return run_fwd_any<MRU_VALU_CFG8, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd_any<MRU_VALU_CFG8, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream, bool from_x) {
+                           hipStream_t stream, bool from_x, const ScanCarry& cy) {
     if (n == 4) {
-        if (from_x) return run_bwd<MRU_VALU_BWD_CFG4, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
-        return run_bwd<MRU_VALU_BWD_CFG4, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+        if (from_x)
+            return run_bwd<MRU_VALU_BWD_CFG4, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        return run_bwd<MRU_VALU_BWD_CFG4, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 8) {
-        if (from_x) return run_bwd<MRU_VALU_BWD_CFG8, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
-        return run_bwd<MRU_VALU_BWD_CFG8, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream);
+        if (from_x)
+            return run_bwd<MRU_VALU_BWD_CFG8, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        return run_bwd<MRU_VALU_BWD_CFG8, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     }
     return hipErrorInvalidValue;
 }

@@ -140,3 +140,26 @@ def test_fused_entries_validate_before_any_launch(mpp):
     assert lib.mru_scan_fwd_x(a, b, 1, 1, 16, 8, -1, nul, 0, nul) == 6
     assert lib.mru_scan_bwd_x(a, b, c, c, 1, 1, 8, 8, 1, nul, 0, nul) == 4
     assert lib.mru_scan_bwd_x(a, b, nul, d, 1, 1, 8, 8, 1, nul, 0, nul) == 1
+
+
+def test_extended_entries_validate_before_any_launch(mpp):
+    lib = mpp.load_library()
+    nul = ctypes.c_void_p(0)
+    a, b, c, d, e = (ctypes.c_void_p(v) for v in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000))
+    odd16 = ctypes.c_void_p(0x300004)
+    odd4 = ctypes.c_void_p(0x300002)
+    # forward: misaligned carry / exponents, exponents overlapping P, P over the carry
+    assert lib.mru_scan_fwd_ex(a, 0, odd16, nul, b, nul, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 3
+    assert lib.mru_scan_fwd_ex(a, 0, c, odd4, b, nul, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 3
+    assert lib.mru_scan_fwd_ex(a, 0, c, nul, b, ctypes.c_void_p(0x200000 + 64), 1, 1, 8, 8, 1 << 20,
+                               nul, 0, nul) == 4
+    assert lib.mru_scan_fwd_ex(a, 0, ctypes.c_void_p(0x200000 + 256), nul, b, nul, 1, 1, 8, 8,
+                               1 << 20, nul, 0, nul) == 4
+    # from_x only for n = 4, 8; empty is a no-op
+    assert lib.mru_scan_fwd_ex(a, 1, nul, nul, b, nul, 1, 1, 8, 16, 0, nul, 0, nul) == 2
+    assert lib.mru_scan_fwd_ex(nul, 0, c, nul, nul, nul, 1, 1, 0, 8, 0, nul, 0, nul) == 0
+    # backward: dcarry overlapping dM or the carry, misaligned dcarry
+    assert lib.mru_scan_bwd_ex(a, 0, c, b, d, e, ctypes.c_void_p(0x500000 + 64), 1, 1, 8, 8, 1 << 20,
+                               nul, 0, nul) == 4
+    assert lib.mru_scan_bwd_ex(a, 0, c, b, d, e, c, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 4
+    assert lib.mru_scan_bwd_ex(a, 0, c, b, d, e, odd16, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 3
