@@ -31,6 +31,12 @@
 #include "mru_device.h"
 #include "mru_kernels.h"
 
+// Prefetch depth of the retained n = 16 aggregate pass (tokens in flight; the
+// whole chunk is held in registers anyway, so depth costs no registers).
+#ifndef MRU_PFR16
+#define MRU_PFR16 16
+#endif
+
 namespace mru {
 namespace {
 
@@ -293,51 +299,122 @@ constexpr int walk_depth() { return N == 16 ? 4 : (BWD ? 1 : 2); }
 
 // ---------------------------------------------------------------------------- forward
 
-// The operand ring: the loads for token t + PF are issued right after token t's
-// operands are consumed.  Loads are unconditional (addresses clamped into the
-// chunk), and the main loop runs whole blocks of PF tokens, so every ring slot
-// stays in fixed registers and PF tokens of loads stay in flight.
-template <int N, int PF, bool WRITE, bool SC>
-__device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
-                          float* __restrict__ P, int32_t* __restrict__ pexp, int64_t base, int len) {
-    using F = Mf<N>;
-    constexpr int NT = F::NT;
-    constexpr int NN = F::NN;
-    constexpr int NA = NT * NT * 4;  // A-operand entries per token and lane
-    if (len <= 0) return;
+// Operand staging of the forward chain.  The A operand of M_t^T needs, in lane
+// l, 4 entries of one column of M_t (M_t[16K + trow(l, b)][16I + tacol(l)],
+// b = 0..3), which row-major memory holds 4*n bytes apart.  Loading them
+// directly takes 4-byte loads, and the 63 loads a wave may keep in flight then
+// cover only 16 KB.  Instead the wave reads each token with 16-byte loads
+// (row-major, n*n/256 per lane, 1 KB per wave instruction) and turns them into
+// operands through LDS: the pieces are written transposed (M^T, row stride
+// n+4), after which every lane's 4 entries are contiguous and come back in one
+// 16-byte LDS read per tile.  Two LDS buffers alternate by token parity, so a
+// single barrier per token orders both the writes before the reads and the
+// previous use of a buffer before its next writes.
+template <int N>
+struct Stage {
+    static constexpr int NV = N * N / 256;  // 16-byte pieces per lane per token
+    static constexpr int LS = N + 4;        // LDS row stride of M^T (floats)
+    static constexpr int BUF = N * LS;      // floats per LDS buffer
+};
+
+template <int N>
+__device__ inline void load_token(float (&v)[4 * Stage<N>::NV], const float* tok) {
     const int l = threadIdx.x & 63;
-    // entry (I, K, b) of M_t^T's A operand: M_t[16K + trow(l, b)][16I + tacol(l)]
-    int aoff[NA];
+#pragma unroll
+    for (int q = 0; q < Stage<N>::NV; ++q) {
+        const float4 w = reinterpret_cast<const float4*>(tok)[q * 64 + l];
+        v[4 * q] = w.x;
+        v[4 * q + 1] = w.y;
+        v[4 * q + 2] = w.z;
+        v[4 * q + 3] = w.w;
+    }
+}
+
+// Row-major pieces v of one token -> this lane's A-operand entries of M^T
+// (index (I * NT + K) * 4 + b), through the LDS buffer tb.
+template <int N>
+__device__ inline void to_operand(float (&o)[4 * Stage<N>::NV], const float (&v)[4 * Stage<N>::NV],
+                                  float* tb) {
+    constexpr int NT = N / 16;
+    constexpr int LS = Stage<N>::LS;
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < Stage<N>::NV; ++q) {
+        const int f = q * 64 + l;           // float4 index within the token
+        const int r = f / (N / 4);          // row of M
+        const int c0 = 4 * (f % (N / 4));   // first column of the piece
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tb[(c0 + j) * LS + r] = v[4 * q + j];
+    }
+    __syncthreads();
 #pragma unroll
     for (int I = 0; I < NT; ++I)
 #pragma unroll
-        for (int K = 0; K < NT; ++K)
+        for (int K = 0; K < NT; ++K) {
+            const float4 w =
+                *reinterpret_cast<const float4*>(tb + (16 * I + tacol(l)) * LS + 16 * K + trow(l, 0));
+            float* d = &o[(I * NT + K) * 4];
+            d[0] = w.x; d[1] = w.y; d[2] = w.z; d[3] = w.w;
+        }
+}
+
+template <int N>
+__device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4 * Stage<N>::NV]) {
+    constexpr int NT = N / 16;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                aoff[(I * NT + K) * 4 + b] = (16 * K + trow(l, b)) * N + 16 * I + tacol(l);
+    for (int e = 0; e < 4 * Stage<N>::NV; ++e)
+        a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(o[e]);
+}
+
+// Software pipelining of the forward chain.  Instructions issue in order, and
+// a token's four products go to the matrix core back to back; anything that
+// needs their result waits behind them, and so does everything after it.  So
+// each step first issues token t's products and only then does the work that
+// does not depend on them (storing token t-1's prefix, preparing token t+1's
+// operands), which then runs while the matrix core is busy.  Scheduling
+// barriers keep the compiler from moving that work in front of the products.
+
+template <int N, bool SC>
+__device__ inline void store_prefix(float* __restrict__ P, int32_t* __restrict__ pexp, int64_t tok,
+                                    const typename Mf<N>::vec_t& X, int ex) {
+    store_acc_rows<N, float>(P + tok * Mf<N>::NN, X);
+    if (SC && (threadIdx.x & 63) == 0) pexp[tok] = ex;
+}
+
+// The operand ring: PF tokens of loads stay in flight; a slot is refilled (with
+// the token PF further on, address clamped into the chunk) as soon as its
+// pieces have been turned into operands.  The main loop runs whole blocks of PF
+// tokens so every ring slot stays in fixed registers.
+template <int N, int PF, bool WRITE, bool SC>
+__device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
+                          float* __restrict__ P, int32_t* __restrict__ pexp, int64_t base, int len,
+                          float* tlds) {
+    using F = Mf<N>;
+    using vec_t = typename F::vec_t;
+    constexpr int NN = F::NN;
+    constexpr int NA = 4 * Stage<N>::NV;  // A-operand entries per token and lane
+    if (len <= 0) return;
     const float* Mb = M + base * NN;
     float ring[PF][NA];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        const int u = min(p, len - 1);
-#pragma unroll
-        for (int e = 0; e < NA; ++e) ring[p][e] = Mb[u * NN + aoff[e]];
-    }
+    for (int p = 0; p < PF; ++p) load_token<N>(ring[p], Mb + int64_t(min(p, len - 1)) * NN);
+    float o[NA];  // operands of the next token to multiply
+    to_operand<N>(o, ring[0], tlds);
+    load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
     auto step = [&](int p, int t, bool refill) {
         typename F::aop_t a;
-#pragma unroll
-        for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(ring[p][e]);
-        if (refill) {
-            const int u = min(t + PF, len - 1);
-#pragma unroll
-            for (int e = 0; e < NA; ++e) ring[p][e] = Mb[u * NN + aoff[e]];
+        operand_from<N>(a, o);
+        vec_t Xn = chain_step<N>(a, X, vzero<N>());
+        __builtin_amdgcn_sched_barrier(0);
+        if (WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
+        if (t + 1 < len) {
+            const int pn = (p + 1) % PF;  // ring slot of token t + 1
+            to_operand<N>(o, ring[pn], tlds + ((t + 1) & 1) * Stage<N>::BUF);
+            if (refill) load_token<N>(ring[pn], Mb + int64_t(min(t + 1 + PF, len - 1)) * NN);
         }
-        X = chain_step<N>(a, X, vzero<N>());
+        __builtin_amdgcn_sched_barrier(0);
+        X = Xn;
         if constexpr (SC) renorm_acc<N>(X, ex);
-        if (WRITE) {
-            store_acc_rows<N, float>(P + (base + t) * NN, X);
-            if (SC && l == 0) pexp[base + t] = ex;
-        }
     };
     int t0 = 0;
     for (; t0 + PF <= len; t0 += PF) {
@@ -347,47 +424,49 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __rest
 #pragma unroll
     for (int p = 0; p < PF; ++p)
         if (t0 + p < len) step(p, t0 + p, false);
+    if (WRITE) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
 }
 
-// Retained chunk (KR > 0): the aggregate pass loads the chunk's A-operand
-// entries into a register buffer of KR tokens (loads issued PF tokens ahead,
-// clamped into the chunk) and the apply pass reuses them, so each input matrix
-// is read from HBM once even when the chunk needs a carry.
+// Retained chunk (KR > 0): the aggregate pass loads the chunk's tokens into a
+// register buffer of KR tokens (loads issued PF tokens ahead, clamped into the
+// chunk), converts each to its operand entries in place, and the apply pass
+// reuses them, so each input matrix is read from HBM once even when the chunk
+// needs a carry.
 template <int N, int KR, int PF, bool SC>
 __device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
-                                int64_t base, int len, float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
+                                int64_t base, int len, float (&buf)[KR][4 * Stage<N>::NV],
+                                float* tlds) {
     using F = Mf<N>;
-    constexpr int NT = F::NT;
+    using vec_t = typename F::vec_t;
     constexpr int NN = F::NN;
-    constexpr int NA = NT * NT * 4;
-    const int l = threadIdx.x & 63;
-    int aoff[NA];
-#pragma unroll
-    for (int I = 0; I < NT; ++I)
-#pragma unroll
-        for (int K = 0; K < NT; ++K)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                aoff[(I * NT + K) * 4 + b] = (16 * K + trow(l, b)) * N + 16 * I + tacol(l);
+    constexpr int NA = 4 * Stage<N>::NV;
+    if (len <= 0) return;
     const float* Mb = M + base * NN;
 #pragma unroll
-    for (int p = 0; p < PF && p < KR; ++p) {
-        const int u = min(p, len - 1);
+    for (int p = 0; p < PF && p < KR; ++p) load_token<N>(buf[p], Mb + int64_t(min(p, len - 1)) * NN);
+    {
+        float o[NA];
+        to_operand<N>(o, buf[0], tlds);
 #pragma unroll
-        for (int e = 0; e < NA; ++e) buf[p][e] = Mb[u * NN + aoff[e]];
+        for (int e = 0; e < NA; ++e) buf[0][e] = o[e];
     }
 #pragma unroll
     for (int t = 0; t < KR; ++t) {
-        if (t + PF < KR) {
-            const int u = min(t + PF, len - 1);
-#pragma unroll
-            for (int e = 0; e < NA; ++e) buf[t + PF][e] = Mb[u * NN + aoff[e]];
-        }
+        if (t + PF < KR) load_token<N>(buf[t + PF], Mb + int64_t(min(t + PF, len - 1)) * NN);
+        __builtin_amdgcn_sched_barrier(0);
         if (t < len) {
             typename F::aop_t a;
+            operand_from<N>(a, buf[t]);
+            vec_t Xn = chain_step<N>(a, X, vzero<N>());
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < KR && t + 1 < len) {
+                float o[NA];
+                to_operand<N>(o, buf[t + 1], tlds + ((t + 1) & 1) * Stage<N>::BUF);
 #pragma unroll
-            for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(buf[t][e]);
-            X = chain_step<N>(a, X, vzero<N>());
+                for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            X = Xn;
             if constexpr (SC) renorm_acc<N>(X, ex);
         }
     }
@@ -396,26 +475,33 @@ __device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* 
 template <int N, int KR, bool SC>
 __device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __restrict__ P,
                                  int32_t* __restrict__ pexp, int64_t base, int len,
-                                 const float (&buf)[KR][Mf<N>::NT * Mf<N>::NT * 4]) {
+                                 const float (&buf)[KR][4 * Stage<N>::NV]) {
     using F = Mf<N>;
-    constexpr int NT = F::NT;
-    constexpr int NA = NT * NT * 4;
+    using vec_t = typename F::vec_t;
 #pragma unroll
     for (int t = 0; t < KR; ++t) {
         if (t < len) {
             typename F::aop_t a;
-#pragma unroll
-            for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(buf[t][e]);
-            X = chain_step<N>(a, X, vzero<N>());
+            operand_from<N>(a, buf[t]);
+            vec_t Xn = chain_step<N>(a, X, vzero<N>());
+            __builtin_amdgcn_sched_barrier(0);
+            if (t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
+            __builtin_amdgcn_sched_barrier(0);
+            X = Xn;
             if constexpr (SC) renorm_acc<N>(X, ex);
-            store_acc_rows<N, float>(P + (base + t) * F::NN, X);
-            if (SC && (threadIdx.x & 63) == 0) pexp[base + t] = ex;
         }
     }
+    if (len > 0) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
 }
 
+// Waves per SIMD the forward kernel is register-budgeted for (tuning knob).
+#ifndef MRU_MFMA_FWD_WAVES
+#define MRU_MFMA_FWD_WAVES 1
+#endif
+
 template <int N, int PF, int KR, bool SC>
-__global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ M,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MRU_MFMA_FWD_WAVES)))
+void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
                                                       unsigned char* __restrict__ ws, ScanCarry cy) {
@@ -424,6 +510,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     using vec_t = typename F::vec_t;
     constexpr int NN = N * N;
     __shared__ double xl[NN];
+    __shared__ __align__(16) float tlds[2 * Stage<N>::BUF];
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -437,7 +524,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     int ex = 0;
     if (!multi) {
         vec_t X = init_acc<N, SC>(ex, cy, seq);
-        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len);
+        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
         return;
     }
     const WsLayout L = ws_layout(nchunks, N, sizeof(acc_t), 2);
@@ -454,9 +541,9 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0)
-        fwd_pass_retain<N, KR, PF, SC>(X, ex, M, ch.base, ch.len, buf);
+        fwd_pass_retain<N, KR, (N == 16 ? MRU_PFR16 : PF), SC>(X, ex, M, ch.base, ch.len, buf, tlds);
     else
-        fwd_sweep<N, PF, false, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len);
+        fwd_sweep<N, PF, false, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
     const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
     if (SC && l == 0) ws_store(&agg_exp[c], int32_t(a_ex));
@@ -525,7 +612,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(const float* __restrict__ 
     if constexpr (KR > 0)
         fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf);
     else
-        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len);
+        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -791,6 +878,9 @@ hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, i
 #ifndef MRU_RETAIN16
 #define MRU_RETAIN16 64
 #endif
+#ifndef MRU_PF16
+#define MRU_PF16 16
+#endif
 // Tokens of one chunk kept in registers by the n = 16 forward kernel.
 constexpr int kRetain16 = MRU_RETAIN16;
 
@@ -803,9 +893,9 @@ hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n
                            const ScanCarry& cy) {
     if (from_x) return hipErrorInvalidValue;
     if (n == 16) {
-        if (nch > 1 && K <= kRetain16)
-            return run_fwd<16, 16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream, cy);
-        return run_fwd<16, 16, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        if (kRetain16 > 0 && nch > 1 && K <= kRetain16)
+            return run_fwd<16, MRU_PF16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd<16, MRU_PF16, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 32) return run_fwd<32, 4, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
     return hipErrorInvalidValue;
