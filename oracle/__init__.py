@@ -5,6 +5,8 @@ by the product path.  See ``mru_oracle`` for the definitions and citations.
 """
 from .mru_oracle import (  # noqa: F401
     FP32_DOMAIN_LIMIT,
+    ORTHO_METHODS,
+    build_orthogonal_ref,
     build_ref,
     build_vjp_ref,
     bwd_ref,

@@ -32,6 +32,9 @@ Readings taken where the pages are silent:
   continuation), and the scaled form writes each P_t as 2^E times a matrix
   whose largest entry lies in [0.5, 1).
 * Flattening is the row-major reshape of P_t to an n*n vector, per head.
+* The orthogonal variant builds A = (X - X^T) / 2 (the skew-symmetric part of
+  the row-major view) and maps it to an orthogonal matrix by the Cayley map
+  or the matrix exponential.
 * The backward pass is the vector-Jacobian product of L = sum_t <R_t, P_t>_F
   with respect to every M_t (the pages describe training through the product
   but give no formula; the chain rule fixes it), and build_vjp_ref carries a
@@ -46,7 +49,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "build_ref", "build_vjp_ref", "scan_ref", "bwd_ref", "scaled_ref", "flatten_ref", "loss_ref",
+    "build_ref", "build_orthogonal_ref", "ORTHO_METHODS", "build_vjp_ref", "scan_ref", "bwd_ref", "scaled_ref", "flatten_ref", "loss_ref",
     "rel_fro_err", "representable", "FP32_DOMAIN_LIMIT",
 ]
 
@@ -83,6 +86,39 @@ def build_ref(x: np.ndarray, n: int) -> np.ndarray:
     det = np.linalg.det(LDU)
     c = np.abs(det) ** (-1.0 / n)
     return c[..., None, None] * LDU
+
+
+ORTHO_METHODS = ("cayley", "expm")
+
+
+def build_orthogonal_ref(x: np.ndarray, n: int, method: str) -> np.ndarray:
+    """Orthogonal input state matrices from raw token vectors.
+
+    ``x``: ``[..., n*n]``; returns float64 ``M``: ``[..., n, n]``.  With X the
+    row-major n-by-n view and A = (X - X^T) / 2 its skew-symmetric part,
+    ``method`` = "cayley" gives M = (I - A)^{-1} (I + A) and "expm" gives
+    M = exp(A); both are orthogonal with det(M) = 1.
+
+    Follows "Improving Matrix Recurrent Units as an Attention Alternative",
+    Key Points, which names orthogonal constraints through the Cayley map and
+    the matrix exponential (the variant it reports hindered learning).  How
+    the n*n entries become A is not stated; the skew-symmetric part of X is
+    the reading taken.  The steps use library routines: a linear solve for
+    the Cayley map and scipy's scaling-and-squaring Pade exponential.
+    """
+    X = _as_matrices(x, n)
+    A = 0.5 * (X - np.swapaxes(X, -1, -2))
+    eye = np.broadcast_to(np.eye(n), A.shape)
+    if method == "cayley":
+        return np.linalg.solve(eye - A, eye + A)
+    if method == "expm":
+        from scipy.linalg import expm
+        flat = A.reshape(-1, n, n)
+        out = np.empty_like(flat)
+        for i in range(flat.shape[0]):
+            out[i] = expm(flat[i])
+        return out.reshape(A.shape)
+    raise ValueError(f"method must be one of {ORTHO_METHODS}")
 
 
 def build_vjp_ref(x: np.ndarray, dM: np.ndarray, n: int) -> np.ndarray:

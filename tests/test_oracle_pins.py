@@ -539,3 +539,67 @@ def test_scaled_ref_values():
         assert np.array_equal(np.ldexp(Pm[k], int(E[k])), P[k])       # exact
         big = np.abs(Pm[k]).max()
         assert big == 0 or 0.5 <= big < 1.0
+
+
+# ----------------------------------------------------------------------------- orthogonal inputs
+
+from oracle import ORTHO_METHODS, build_orthogonal_ref  # noqa: E402
+
+
+def test_orthogonal_two_by_two_closed_forms():
+    # n = 2: A = [[0, a], [-a, 0]] with a = (x01 - x10) / 2; the diagonal of X is ignored
+    for x01, x10, d in [(0.3, -0.1, 0.7), (-1.2, 0.4, -2.0), (2.5, 2.5, 0.0)]:
+        x = np.array([d, x01, x10, -d])
+        a = (x01 - x10) / 2
+        E = build_orthogonal_ref(x, 2, "expm")
+        np.testing.assert_allclose(E, [[math.cos(a), math.sin(a)], [-math.sin(a), math.cos(a)]],
+                                   rtol=0, atol=1e-14)
+        C = build_orthogonal_ref(x, 2, "cayley")
+        q = 1 + a * a
+        np.testing.assert_allclose(C, [[(1 - a * a) / q, 2 * a / q], [-2 * a / q, (1 - a * a) / q]],
+                                   rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("method", ORTHO_METHODS)
+@pytest.mark.parametrize("n", [4, 8, 16, 32])
+def test_orthogonal_is_orthogonal_with_det_one(method, n):
+    x = RNG.normal(0, 0.4, size=(5, n * n))
+    M = build_orthogonal_ref(x, n, method)
+    I = np.broadcast_to(np.eye(n), M.shape)
+    np.testing.assert_allclose(np.swapaxes(M, -1, -2) @ M, I, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.det(M), 1.0, rtol=0, atol=1e-11)
+    # symmetric X gives A = 0 and M = I; negating A transposes M
+    xs = RNG.normal(size=(n, n)); xs = (xs + xs.T).reshape(-1)
+    np.testing.assert_allclose(build_orthogonal_ref(xs, n, method), np.eye(n), rtol=0, atol=1e-14)
+    Xm = x.reshape(5, n, n)
+    np.testing.assert_allclose(build_orthogonal_ref(np.swapaxes(Xm, -1, -2).reshape(5, -1), n, method),
+                               np.swapaxes(M, -1, -2), rtol=0, atol=1e-12)
+
+
+def test_orthogonal_methods_against_series_and_each_other():
+    # exp(A) against a plain truncated Taylor series; the Cayley map of the
+    # generator of a plane rotation, a times [[0, 1], [-1, 0]], rotates that
+    # plane by 2 atan(a) and leaves the rest fixed
+    n = 6
+    x = RNG.normal(0, 0.2, size=(n * n,))
+    X = x.reshape(n, n)
+    A = (X - X.T) / 2
+    series, term = np.eye(n), np.eye(n)
+    for k in range(1, 30):
+        term = term @ A / k
+        series = series + term
+    np.testing.assert_allclose(build_orthogonal_ref(x, n, "expm"), series, rtol=0, atol=1e-14)
+    a = 0.37
+    x2 = np.zeros((4, 4)); x2[1, 2] = 2 * a     # A = rotation generator in plane (1, 2)
+    C = build_orthogonal_ref(x2.reshape(-1), 4, "cayley")
+    th = 2 * math.atan(a)
+    assert abs(C[1, 1] - math.cos(th)) < 1e-14 and abs(C[1, 2] - math.sin(th)) < 1e-14
+    assert np.allclose(C[[0, 3]][:, [0, 3]], np.eye(2), atol=1e-15)
+
+
+def test_orthogonal_scan_keeps_the_norm():
+    n, T = 8, 500
+    x = RNG.normal(0, 0.3, size=(T, n * n))
+    for method in ORTHO_METHODS:
+        P = scan_ref(build_orthogonal_ref(x, n, method))
+        np.testing.assert_allclose(np.linalg.norm(P, axis=(-1, -2)), math.sqrt(n), rtol=1e-11)
