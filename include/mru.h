@@ -66,6 +66,10 @@ typedef enum mru_status {
 #define MRU_DIR_FWD 0
 #define MRU_DIR_BWD 1
 
+/* Orthogonal input constructions (mru_build_orthogonal). */
+#define MRU_ORTHO_CAYLEY 0
+#define MRU_ORTHO_EXPM 1
+
 /* MRU_ABI_VERSION of the loaded library. */
 int32_t mru_abi_version(void);
 
@@ -87,6 +91,24 @@ const char* mru_status_string(int32_t status);
  */
 mru_status mru_build_inputs(const float* x, float* M, int64_t B, int64_t H, int64_t T,
                             int32_t n, void* stream);
+
+/*
+ * Orthogonal input state matrices, the variant "Improving Matrix Recurrent
+ * Units as an Attention Alternative" (Key Points) describes as orthogonal
+ * constraints via the Cayley map or the matrix exponential.  For each token,
+ * with X the row-major n-by-n view of x and A = (X - X^T) / 2 its
+ * skew-symmetric part (the pages do not say how the entries fill A; this is
+ * the reading taken):
+ *   method MRU_ORTHO_CAYLEY:  M = (I - A)^{-1} (I + A)
+ *   method MRU_ORTHO_EXPM:    M = exp(A)
+ * Both are orthogonal with det M = 1, so every prefix product has
+ * |P_t|_F = sqrt(n) and a scan of them never leaves the fp32 range.
+ * Computed in fp64 and rounded once to fp32 (relative error per matrix below
+ * 1e-7).  x, M as for mru_build_inputs; any other method returns
+ * MRU_ERR_SHAPE.
+ */
+mru_status mru_build_orthogonal(const float* x, float* M, int64_t B, int64_t H, int64_t T,
+                                int32_t n, int32_t method, void* stream);
 
 /*
  * Gradient through the input construction: dx = d<dM, build(x)>/dx, i.e. the

@@ -73,6 +73,8 @@ def load_library():
     lib.mru_status_string.argtypes = [i32]
     lib.mru_build_inputs.restype = i32
     lib.mru_build_inputs.argtypes = [vp, vp, i64, i64, i64, i32, vp]
+    lib.mru_build_orthogonal.restype = i32
+    lib.mru_build_orthogonal.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp]
     lib.mru_build_inputs_bwd.restype = i32
     lib.mru_build_inputs_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
     lib.mru_scan_chunk.restype = i32
@@ -182,6 +184,34 @@ def build_inputs(x: torch.Tensor, n: int, out: torch.Tensor | None = None) -> to
     with torch.cuda.device(x.device):
         st = lib.mru_build_inputs(_ptr(x), _ptr(M), B, H, T, n, _stream_handle(x.device))
     _check(st, "mru_build_inputs")
+    return M
+
+
+ORTHO_METHODS = {"cayley": 0, "expm": 1}
+
+
+def build_orthogonal(x: torch.Tensor, n: int, method: str = "cayley",
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """[B,H,T,n*n] raw token vectors -> [B,H,T,n,n] orthogonal input matrices:
+    the Cayley map or the exponential of A = (X - X^T)/2."""
+    if method not in ORTHO_METHODS:
+        raise ValueError(f"method must be one of {tuple(ORTHO_METHODS)}")
+    _require(x, "x", 4)
+    B, H, T, nn = x.shape
+    if n not in SUPPORTED_N or nn != n * n:
+        raise ValueError(f"x must be [B,H,T,n*n] with n in {SUPPORTED_N}, got {tuple(x.shape)}, n={n}")
+    if out is None:
+        M = torch.empty((B, H, T, n, n), dtype=torch.float32, device=x.device)
+    else:
+        _require(out, "out", 5)
+        if tuple(out.shape) != (B, H, T, n, n) or out.device != x.device:
+            raise ValueError("out must be [B,H,T,n,n] on x's device")
+        M = out
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.mru_build_orthogonal(_ptr(x), _ptr(M), B, H, T, n, ORTHO_METHODS[method],
+                                      _stream_handle(x.device))
+    _check(st, "mru_build_orthogonal")
     return M
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmru.so")
-SOURCES = ["mru_api.hip", "build_inputs.hip", "scan_valu.hip", "scan_mfma.hip"]
+SOURCES = ["mru_api.hip", "build_inputs.hip", "build_orth.hip", "scan_valu.hip", "scan_mfma.hip"]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

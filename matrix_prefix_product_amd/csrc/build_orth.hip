@@ -1,0 +1,197 @@
+// Orthogonal input state matrices ("Improving Matrix Recurrent Units as an
+// Attention Alternative", Key Points: orthogonal constraints through the Cayley
+// map or the matrix exponential).  With X the row-major n-by-n view of a token
+// vector and A = (X - X^T) / 2 its skew-symmetric part:
+//   Cayley:       M = (I - A)^{-1} (I + A)
+//   exponential:  M = exp(A)
+// Both are orthogonal with det M = 1, so a scan of them keeps |P_t|_F = sqrt(n).
+//
+// A chain of n lanes works on one token, lane i owning row i, in fp64 (the
+// vector fp64 rate equals the fp32 one on CDNA4, and fp64 keeps the only
+// rounding of the result the final one to fp32).  Rows of the other lanes come
+// through LDS.
+//   Cayley: Gauss-Jordan elimination on [I - A | I + A].  No pivoting is needed:
+//     the symmetric part of I - A is I, so every leading block is nonsingular.
+//   Exponential: scaling and squaring.  A is scaled by 2^-s (exact) so that its
+//     largest row sum is at most 1/2, exp of the scaled matrix is summed by
+//     Horner's rule to degree 12 (remainder below 1e-14), then squared s times.
+//     s is the token's own; the wave runs the largest s among its tokens with
+//     each token's squarings gated to its own count, so a token's result never
+//     depends on the tokens it shares a wave with.
+#include "mru_device.h"
+#include "mru_kernels.h"
+
+namespace mru {
+namespace {
+
+constexpr int kTaylorDegree = 12;
+
+template <int N>
+struct Orth {
+    static constexpr int NN = N * N;
+    static constexpr int TPW = 64 / N;          // tokens per wave
+    static constexpr int XS = TPW * NN;         // staged floats per wave
+    static constexpr int ES = N + 1;            // LDS row stride of a token's matrix (doubles)
+};
+
+template <int N>
+__device__ inline double group_max_d(double v) {
+#pragma unroll
+    for (int m = 1; m < N; m <<= 1) v = fmax(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+template <int N, int METHOD>
+__global__ __launch_bounds__(64) void build_orth_kernel(const float* __restrict__ x,
+                                                        float* __restrict__ M, int64_t ntok) {
+    using O = Orth<N>;
+    __shared__ __align__(16) float xs[O::XS];
+    __shared__ double ms[O::TPW * N * O::ES];
+    __shared__ double as[METHOD == 1 ? O::TPW * N * O::ES : 2];  // rows of the scaled A
+    const int lane = threadIdx.x & 63;
+    const int tk = lane / N;  // token of the wave
+    const int i = lane % N;   // row
+    double* mine = ms + tk * N * O::ES;
+    const int64_t groups = (ntok + O::TPW - 1) / O::TPW;
+    for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+        const int64_t tok0 = grp * O::TPW;
+        const int64_t tok = tok0 + tk;
+        const bool live = tok < ntok;
+        // stage the wave's tokens (float4 per lane per step; zeros past the end)
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < O::XS / 256; ++q) {
+            const int f = q * 64 + lane;  // float4 index within the wave's tokens
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (tok0 + (f * 4) / O::NN < ntok)
+                v = reinterpret_cast<const float4*>(x + tok0 * O::NN)[f];
+            reinterpret_cast<float4*>(xs)[f] = v;
+        }
+        __syncthreads();
+        const float* X = xs + tk * O::NN;
+        double a[N];  // row i of A
+#pragma unroll
+        for (int j = 0; j < N; ++j) a[j] = 0.5 * (double(X[i * N + j]) - double(X[j * N + i]));
+
+        double r[N];  // row i of the result
+        if constexpr (METHOD == 0) {
+            double lft[N];
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                lft[j] = (j == i ? 1.0 : 0.0) - a[j];
+                r[j] = (j == i ? 1.0 : 0.0) + a[j];
+            }
+            // pivot row k (normalised) goes to the token's LDS rows 0 (left) and 1 (right)
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                __syncthreads();
+                if (i == k) {
+                    const double inv = 1.0 / lft[k];
+#pragma unroll
+                    for (int j = 0; j < N; ++j) {
+                        lft[j] *= inv;
+                        r[j] *= inv;
+                        mine[j] = lft[j];
+                        mine[O::ES + j] = r[j];
+                    }
+                }
+                __syncthreads();
+                if (i != k) {
+                    const double f = lft[k];
+#pragma unroll
+                    for (int j = 0; j < N; ++j) {
+                        lft[j] = fma(-f, mine[j], lft[j]);
+                        r[j] = fma(-f, mine[O::ES + j], r[j]);
+                    }
+                }
+            }
+        } else {
+            // scale: largest absolute row sum of A to at most 1/2
+            double rs = 0.0;
+#pragma unroll
+            for (int j = 0; j < N; ++j) rs += fabs(a[j]);
+            const double nrm = group_max_d<N>(rs);
+            const int s = nrm > 0.5 ? frexp_exp(nrm) + 1 : 0;  // nrm < 2^e, so nrm 2^-s <= 1/2
+            const int s_wave = __builtin_amdgcn_readfirstlane(group_max<64>(s));
+            double* arow = as + (tk * N + i) * O::ES;  // the lane's row of A, read back per k
+#pragma unroll
+            for (int j = 0; j < N; ++j) arow[j] = ldexp(a[j], -s);
+            // Horner: E = I + (A E) / d, ..., E = I + (A E) / 1, starting from E = I
+#pragma unroll
+            for (int j = 0; j < N; ++j) r[j] = (j == i) ? 1.0 : 0.0;
+#pragma unroll 1
+            for (int d = kTaylorDegree; d >= 1; --d) {
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < N; ++j) mine[i * O::ES + j] = r[j];
+                __syncthreads();
+                // row i of A E, accumulated in place of r (already in LDS)
+#pragma unroll
+                for (int j = 0; j < N; ++j) r[j] = 0.0;
+#pragma unroll
+                for (int k = 0; k < N; ++k) {
+                    const double c = arow[k];
+#pragma unroll
+                    for (int j = 0; j < N; ++j) r[j] = fma(c, mine[k * O::ES + j], r[j]);
+                }
+                const double inv = 1.0 / double(d);
+#pragma unroll
+                for (int j = 0; j < N; ++j) r[j] = fma(r[j], inv, (j == i) ? 1.0 : 0.0);
+            }
+#pragma unroll 1
+            for (int q = 0; q < s_wave; ++q) {
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < N; ++j) mine[i * O::ES + j] = r[j];
+                __syncthreads();
+                if (q < s) {  // row i of E E; the coefficients are this lane's row, in LDS
+#pragma unroll
+                    for (int j = 0; j < N; ++j) r[j] = 0.0;
+#pragma unroll
+                    for (int k = 0; k < N; ++k) {
+                        const double c = mine[i * O::ES + k];
+#pragma unroll
+                        for (int j = 0; j < N; ++j) r[j] = fma(c, mine[k * O::ES + j], r[j]);
+                    }
+                }
+            }
+        }
+        if (live) {
+            float4* out = reinterpret_cast<float4*>(M + tok * O::NN + i * N);
+#pragma unroll
+            for (int c = 0; c < N / 4; ++c)
+                out[c] = make_float4(float(r[4 * c]), float(r[4 * c + 1]), float(r[4 * c + 2]),
+                                     float(r[4 * c + 3]));
+        }
+    }
+}
+
+template <int N, int METHOD>
+hipError_t run_orth(const float* x, float* M, int64_t ntok, hipStream_t stream) {
+    const int64_t groups = (ntok + Orth<N>::TPW - 1) / Orth<N>::TPW;
+    const unsigned blocks = unsigned(groups < 16384 ? groups : 16384);
+    hipLaunchKernelGGL((build_orth_kernel<N, METHOD>), dim3(blocks), dim3(64), 0, stream, x, M, ntok);
+    return hipGetLastError();
+}
+
+template <int METHOD>
+hipError_t run_orth_n(const float* x, float* M, int64_t ntok, int n, hipStream_t stream) {
+    switch (n) {
+        case 4: return run_orth<4, METHOD>(x, M, ntok, stream);
+        case 8: return run_orth<8, METHOD>(x, M, ntok, stream);
+        case 16: return run_orth<16, METHOD>(x, M, ntok, stream);
+        case 32: return run_orth<32, METHOD>(x, M, ntok, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_build_orth(const float* x, float* M, int64_t ntok, int n, int method,
+                             hipStream_t stream) {
+    if (method == 0) return run_orth_n<0>(x, M, ntok, n, stream);
+    if (method == 1) return run_orth_n<1>(x, M, ntok, n, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mru

@@ -163,6 +163,20 @@ mru_status mru_build_inputs(const float* x, float* M, int64_t B, int64_t H, int6
     return launched(launch_build(x, M, S * T, n, static_cast<hipStream_t>(stream)));
 }
 
+mru_status mru_build_orthogonal(const float* x, float* M, int64_t B, int64_t H, int64_t T,
+                                int32_t n, int32_t method, void* stream) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (method != MRU_ORTHO_CAYLEY && method != MRU_ORTHO_EXPM) return MRU_ERR_SHAPE;
+    if (elems == 0) return MRU_OK;
+    if (!x || !M) return MRU_ERR_NULL;
+    if (!aligned16(x) || !aligned16(M)) return MRU_ERR_ALIGN;
+    const size_t bytes = size_t(elems) * sizeof(float);
+    if (overlap(x, bytes, M, bytes)) return MRU_ERR_ALIAS;
+    (void)hipGetLastError();
+    return launched(launch_build_orth(x, M, S * T, n, method, static_cast<hipStream_t>(stream)));
+}
+
 mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int64_t B, int64_t H,
                                 int64_t T, int32_t n, void* stream) {
     int64_t S, elems;

@@ -10,6 +10,10 @@ namespace mru {
 
 // LDU fill + determinant correction for ntok = B*H*T token matrices.
 hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream);
+// Orthogonal inputs from the skew-symmetric part of each token: method 0 the
+// Cayley map, 1 the matrix exponential.
+hipError_t launch_build_orth(const float* x, float* M, int64_t ntok, int n, int method,
+                             hipStream_t stream);
 // Its gradient: dx from x and dL/dM.
 hipError_t launch_build_bwd(const float* x, const float* dM, float* dx, int64_t ntok, int n,
                             hipStream_t stream);

@@ -163,3 +163,14 @@ def test_extended_entries_validate_before_any_launch(mpp):
                                nul, 0, nul) == 4
     assert lib.mru_scan_bwd_ex(a, 0, c, b, d, e, c, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 4
     assert lib.mru_scan_bwd_ex(a, 0, c, b, d, e, odd16, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 3
+
+
+def test_orthogonal_build_validates(mpp):
+    lib = mpp.load_library()
+    nul = ctypes.c_void_p(0)
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert lib.mru_build_orthogonal(a, b, 1, 1, 4, 8, 2, nul) == 2     # unknown method
+    assert lib.mru_build_orthogonal(a, b, 1, 1, 4, 6, 0, nul) == 2     # bad n
+    assert lib.mru_build_orthogonal(a, a, 1, 1, 4, 8, 1, nul) == 4     # alias
+    assert lib.mru_build_orthogonal(nul, b, 1, 1, 4, 8, 0, nul) == 1
+    assert lib.mru_build_orthogonal(nul, nul, 0, 1, 4, 8, 0, nul) == 0
