@@ -37,7 +37,9 @@
  * Arithmetic  inputs and outputs are IEEE fp32.  The running product is kept
  *             in fp32 for n = 4, 8 and in fp64 for n = 16, 32.  Values beyond
  *             the fp32 range become +-inf / nan exactly as IEEE arithmetic
- *             gives them: nothing is clamped or renormalised.
+ *             gives them: nothing is clamped or renormalised, except in the
+ *             scaled form of mru_scan_fwd_ex, which writes each P_t as a power
+ *             of two times a normalised matrix.
  */
 #ifndef MRU_H
 #define MRU_H
@@ -54,8 +56,10 @@ extern "C" {
 typedef enum mru_status {
     MRU_OK = 0,
     MRU_ERR_NULL = 1,       /* a required pointer is NULL                         */
-    MRU_ERR_SHAPE = 2,      /* B, H or T negative, n not in {4,8,16,32}, overflow */
-    MRU_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                   */
+    MRU_ERR_SHAPE = 2,      /* B, H or T negative, n not in {4,8,16,32}, overflow,
+                               or an option the entry point does not support     */
+    MRU_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned (exponent arrays:
+                               4-byte)                                            */
     MRU_ERR_ALIAS = 4,      /* an output overlaps an input or another output      */
     MRU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required            */
     MRU_ERR_CHUNK = 6,      /* chunk < 0                                          */

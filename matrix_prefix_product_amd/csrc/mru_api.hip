@@ -140,8 +140,8 @@ const char* mru_status_string(int32_t status) {
     switch (status) {
         case MRU_OK: return "MRU_OK";
         case MRU_ERR_NULL: return "MRU_ERR_NULL: a required pointer is NULL";
-        case MRU_ERR_SHAPE: return "MRU_ERR_SHAPE: bad B/H/T or n not in {4,8,16,32}";
-        case MRU_ERR_ALIGN: return "MRU_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case MRU_ERR_SHAPE: return "MRU_ERR_SHAPE: bad B/H/T, n not in {4,8,16,32}, or an unsupported option";
+        case MRU_ERR_ALIGN: return "MRU_ERR_ALIGN: a pointer is misaligned (16 bytes; exponent arrays 4)";
         case MRU_ERR_ALIAS: return "MRU_ERR_ALIAS: an output overlaps an input";
         case MRU_ERR_WORKSPACE: return "MRU_ERR_WORKSPACE: workspace missing or too small";
         case MRU_ERR_CHUNK: return "MRU_ERR_CHUNK: chunk must be >= 0";
@@ -228,7 +228,7 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
                          const ScanCarry& cy) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
-    if (from_x && n > 8 && !mfma_from_x_supported(n)) return MRU_ERR_SHAPE;
+    if (from_x && n > 8) return MRU_ERR_SHAPE;  // the matrix-core scans read M
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P) return MRU_ERR_NULL;
@@ -264,7 +264,7 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
         if (st != MRU_OK) return st;
     }
     if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
-    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
+    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, cy));
 }
 
 mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float* dM, int64_t B,

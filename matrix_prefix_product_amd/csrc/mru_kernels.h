@@ -43,10 +43,8 @@ hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, floa
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
                            hipStream_t stream, bool from_x, const ScanCarry& cy);
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream,
                            const ScanCarry& cy);
-// Whether the matrix-core forward can start from raw token vectors for this n.
-bool mfma_from_x_supported(int n);
 hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
                            hipStream_t stream, const ScanCarry& cy);

@@ -886,12 +886,9 @@ constexpr int kRetain16 = MRU_RETAIN16;
 
 int mfma_retain_tokens(int n) { return n == 16 ? kRetain16 : 0; }
 
-bool mfma_from_x_supported(int) { return false; }
-
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream,
                            const ScanCarry& cy) {
-    if (from_x) return hipErrorInvalidValue;
     if (n == 16) {
         if (kRetain16 > 0 && nch > 1 && K <= kRetain16)
             return run_fwd<16, MRU_PF16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream, cy);

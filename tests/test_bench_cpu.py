@@ -1,0 +1,35 @@
+"""Host-side checks of bench.py's contract (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                           capture_output=True, text=True, env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU" in r.stderr
+        assert r.stdout == ""
+
+
+def test_algorithmic_bytes_per_kernel():
+    import bench
+    S, T, n = 8192, 256, 8
+    per_entry = {"fwd_x": 8, "bwd_x": 16, "build": 8, "fwd": 8, "bwd": 16, "build_bwd": 12}
+    for kind, b in per_entry.items():
+        assert bench.algorithmic_bytes(kind, S, T, n) == b * n * n * S * T
+    # one C2L forward launch moves exactly 1 GiB, the backward 2 GiB
+    assert bench.algorithmic_bytes("fwd_x", S, T, n) == 2 ** 30
+    assert bench.algorithmic_bytes("bwd_x", S, T, n) == 2 ** 31
+
+
+def test_traffic_record_is_tied_to_the_sources():
+    import bench
+    h = bench.source_hash()
+    assert len(h) == 16 and h == bench.source_hash()
+    # a record taken on other sources is ignored
+    assert bench.load_traffic("c2l", "no_such_kernel") is None
