@@ -19,6 +19,8 @@ never stored.  Prints ONE JSON line:
   unfused       the separate kernels (build x -> M, scan M -> P, backward from M,
                 and the build's own backward x, dM -> dx) timed alone
   n16, n32      forward-scan throughput on the n=16 and n=32 workloads
+  next          the scaled forward, the orthogonal input builds and a
+                token-by-token decode step with a carried state
   cpu_baseline  the fp64 oracle (oracle/) timed on the host on a bounded sample
                 of the same workload
 
@@ -200,6 +202,61 @@ def unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, workload, reps: int = 
     return rec
 
 
+def _time(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    return t[len(t) // 2] * 1e3  # median, microseconds
+
+
+def next_rows(mpp, torch):
+    """Figures for the rows beyond the core path: the scaled forward, the
+    orthogonal input builds and token-by-token streaming with a carried state."""
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    # scaled vs plain forward on the n = 32, 64K-token workload
+    B, H, T, n = 1, 8, 65536, 32
+    x = (torch.randn((B, H, T, n * n), generator=g, device="cuda") * 0.02).contiguous()
+    M = mpp.build_inputs(x, n)
+    ws = torch.empty(max(mpp.workspace_bytes(B, H, T, n), 256), dtype=torch.uint8, device="cuda")
+    plain = _time(torch, lambda: mpp.scan_fwd(M, workspace=ws), 5)
+    scaled = _time(torch, lambda: mpp.scan_fwd_ex(M, scaled=True, workspace=ws), 5)
+    out["scaled_fwd"] = {"workload": "c4 shape (1x8x65536, n=32): every P_t as 2^E times a normalised matrix",
+                         "median_us": round(scaled, 1), "plain_median_us": round(plain, 1),
+                         "achieved_GBs": round((8 * n * n + 4) * B * H * T / (scaled * 1e-6) / 1e9, 1)}
+    # orthogonal builds: fp64 arithmetic per token, Cayley 2n^3 and exp about (12 + s) * n^3 multiply-adds
+    orth = {}
+    for name, (B, H, T, n) in {"c2l shape, n=8": (1024, 8, 256, 8), "c4 shape, n=32": (1, 8, 65536, 32)}.items():
+        x = (torch.randn((B, H, T, n * n), generator=g, device="cuda") * 0.1).contiguous()
+        M = torch.empty((B, H, T, n, n), device="cuda")
+        for method in ("cayley", "expm"):
+            us = _time(torch, lambda: mpp.build_orthogonal(x, n, method, out=M), 5)
+            fma = (2 if method == "cayley" else 12) * n ** 3 * B * H * T
+            orth[f"{method}, {name}"] = {
+                "median_us": round(us, 1),
+                "achieved_GBs": round(8 * n * n * B * H * T / (us * 1e-6) / 1e9, 1),
+                "fp64_tflops_lower_bound": round(2 * fma / (us * 1e-6) / 1e12, 2),
+                "fp64_vector_peak_tflops": FP64_PEAK_TFLOPS}
+        del x, M
+    out["orthogonal_build"] = orth
+    # streaming: one token per call for 8192 sequences of 8x8 states (a decode step)
+    B, H, n = 1024, 8, 8
+    xs = (torch.randn((B, H, 1, n * n), generator=g, device="cuda") * 0.1).contiguous()
+    state = mpp.scan_fwd_x(xs, n)[:, :, 0].contiguous()
+    us = _time(torch, lambda: mpp.scan_fwd_ex(xs, carry=state, from_x=True, n=n), 20)
+    out["decode_step"] = {"workload": "8192 sequences (1024x8), n=8, one token from x with the carried state",
+                          "median_us": round(us, 1), "tokens_per_s": B / (us * 1e-6)}
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_reference(torch, gib: int = 1, reps: int = 10):
     """A plain device-to-device copy of known size on the same GPU: the practical
     streaming bandwidth this machine reaches, and the known-size kernel that scales
@@ -346,6 +403,7 @@ def main():
         c3, c4 = WORKLOADS["c3"], WORKLOADS["c4"]
         out["n16"] = fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3)
         out["n32"] = fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4)
+        out["next"] = next_rows(mpp, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = time_cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
