@@ -293,6 +293,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the n=16 / n=32 forward figures")
+    ap.add_argument("--extra-only", action="store_true",
+                    help="only the n=16 / n=32 and next-row figures (for profiling those kernels)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -313,6 +315,15 @@ def main():
     S = B * H
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.extra_only:
+        c3, c4 = WORKLOADS["c3"], WORKLOADS["c4"]
+        extra = {
+            "n16": fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3),
+            "n32": fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4),
+            "next": next_rows(mpp, torch),
+        }
+        print(json.dumps(extra), flush=True)
+        return
 
     x = torch.from_numpy(gen_x(B, H, T, n, w.sigma_off, w.sigma_diag, w.seed)).to(dev)
     R = torch.from_numpy(gen_R(B, H, T, n, w.seed)).to(dev)

@@ -84,9 +84,13 @@ __global__ __launch_bounds__(64) void build_orth_kernel(const float* __restrict_
             // pivot row k (normalised) goes to the token's LDS rows 0 (left) and 1 (right)
 #pragma unroll
             for (int k = 0; k < N; ++k) {
+                // read column k before branching: inside "i == k" the compiler
+                // would rewrite lft[k] as lft[i], a lane-dependent index that
+                // moves the whole row to scratch memory
+                const double lk = lft[k];
                 __syncthreads();
                 if (i == k) {
-                    const double inv = 1.0 / lft[k];
+                    const double inv = 1.0 / lk;
 #pragma unroll
                     for (int j = 0; j < N; ++j) {
                         lft[j] *= inv;
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(64) void build_orth_kernel(const float* __restrict_
                 }
                 __syncthreads();
                 if (i != k) {
-                    const double f = lft[k];
+                    const double f = lk;
 #pragma unroll
                     for (int j = 0; j < N; ++j) {
                         lft[j] = fma(-f, mine[j], lft[j]);
