@@ -35,6 +35,11 @@ struct Valu {
     static constexpr int F4_BLK = TB * F4_TOK;    // float4 per chain per staged block
     static constexpr int LD = (G * F4_BLK) / 64;  // float4 loads per lane per staged array
     static constexpr int CH_STRIDE = TB * NN + 4; // floats per chain in LDS (16 B skew)
+    // floats per chain in the LDS buffers through which a chain's lanes swap
+    // rows; every lane then reads its chain's whole matrix, and the 16 B skew
+    // puts the chains in different banks (an unskewed n*n-float stride sends
+    // all chains of a wave to the same banks)
+    static constexpr int QX_STRIDE = NN + 4;
     static_assert((G * F4_BLK) % 64 == 0, "staging must tile the wave");
     static_assert(N % R == 0 && 64 % LPC == 0, "bad row split");
 };
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     using V = Valu<N, R, TB>;
     __shared__ float lds[V::G * V::CH_STRIDE];
     __shared__ float se[FX ? V::G * TB * N : 4];
-    __shared__ float xch[V::G * V::NN];
+    __shared__ __align__(16) float xch[V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
     const int g = lane / V::LPC;
@@ -472,13 +477,13 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
 
     // 3. carry = (prefix of the previous super, or the carried-in state) * lrow
     if (later_super || cy.carry) {  // wave-uniform
-        store_rows<N, R>(xch + g * V::NN + li * R * N, lrow);
+        store_rows<N, R>(xch + g * V::QX_STRIDE + li * R * N, lrow);
         if (later_super) {
             wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
             fence_acquire();
         }
         __syncthreads();
-        load_matrix<N>(m, xch + g * V::NN);
+        load_matrix<N>(m, xch + g * V::QX_STRIDE);
         if (later_super) {
             ws_load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
             ex = SC ? ws_load(&incl_exp[first - 1]) : 0;
@@ -586,14 +591,14 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                 // exchange Q_t rows within the chain, then dM rows a = own rows:
                 // dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
                 __syncthreads();
-                if (live) store_rows<N, R>(qx + g * V::NN + li * R * N, q);
+                if (live) store_rows<N, R>(qx + g * V::QX_STRIDE + li * R * N, q);
                 __syncthreads();
                 if (live) {
                     float d[R][N];
                     // d = Pprev^T Q_t for the lane's rows, Pprev row-major at src
                     auto times_prev = [&](const float* src) {
                         float qa[V::NN];
-                        load_matrix<N>(qa, qx + g * V::NN);
+                        load_matrix<N>(qa, qx + g * V::QX_STRIDE);
                         set_zero_rows<N, R>(d);
 #pragma unroll
                         for (int ii = 0; ii < N; ++ii) {
@@ -655,7 +660,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     using V = Valu<N, R, TB>;
     __shared__ float lds[3 * V::G * V::CH_STRIDE];
     __shared__ float se[FX ? V::G * TB * N : 4];
-    __shared__ float qx[V::G * V::NN];
+    __shared__ __align__(16) float qx[V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
     const int g = lane / V::LPC;
@@ -718,9 +723,9 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     if (later_super) {
         wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
         fence_acquire();
-        store_rows<N, R>(qx + g * V::NN + li * R * N, wc);
+        store_rows<N, R>(qx + g * V::QX_STRIDE + li * R * N, wc);
         __syncthreads();
-        load_matrix<N>(m, qx + g * V::NN);
+        load_matrix<N>(m, qx + g * V::QX_STRIDE);
         ws_load_rows<N, R>(q, sinc + (first - 1) * V::NN + li * R * N);
         rows_times<N, R>(q, m);
 #pragma unroll

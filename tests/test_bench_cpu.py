@@ -33,3 +33,10 @@ def test_traffic_record_is_tied_to_the_sources():
     assert len(h) == 16 and h == bench.source_hash()
     # a record taken on other sources is ignored
     assert bench.load_traffic("c2l", "no_such_kernel") is None
+
+
+def test_counted_sources_exist():
+    import bench
+    csrc = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
+    for f in bench.COUNTED_SOURCES:
+        assert os.path.isfile(os.path.join(csrc, f)), f
