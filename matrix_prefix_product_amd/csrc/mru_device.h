@@ -139,7 +139,8 @@ __device__ inline void fence_acquire() {
 // time then come from many sequences, and every chunk's predecessors were handed
 // out at least S tickets earlier, which keeps the carry chains short.  A chunk
 // only ever waits on earlier chunks of its own sequence, which have smaller
-// tickets.  Returns the first chunk index of the group (groups of G chunks).
+// tickets.  Returns the first chunk index of the group (groups of G chunks);
+// t must be below S * groups_per_seq (larger tickets map back into range).
 __device__ inline int64_t ticket_to_chunk(int64_t t, int64_t S, int64_t groups_per_seq, int G) {
     const int64_t s = t % S;
     return (s * groups_per_seq + t / S) * G;
