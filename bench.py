@@ -19,10 +19,14 @@ never stored.  Prints ONE JSON line:
   unfused       the separate kernels (build x -> M, scan M -> P, backward from M,
                 and the build's own backward x, dM -> dx) timed alone
   n16, n32      forward-scan throughput on the n=16 and n=32 workloads
+  n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload
   next          the scaled forward, the orthogonal input builds and a
                 token-by-token decode step with a carried state
   cpu_baseline  the fp64 oracle (oracle/) timed on the host on a bounded sample
-                of the same workload
+                of the same workload, on one thread and split over worker
+                processes; and the GPU step's outputs on the first batch rows
+                checked against the oracle's (relative Frobenius error per
+                matrix, with the 2e-4 / 5e-4 bounds)
 
 Only one GPU is used: --gpus N with N > 1 exits with an explanation.
 """
@@ -87,41 +91,108 @@ def load_traffic(workload: str, kernel: str):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
-def time_cpu_baseline(w, budget_s: float):
-    """The oracle's build + forward + backward on a bounded sample, 1 thread."""
+# Batch rows of the timed workload whose GPU outputs the host leg checks
+# against the oracle (all heads, all tokens).
+PARITY_ROWS = 16
+_POOL = {}  # inputs of the parallel oracle run, inherited by the forked workers
+
+
+def _oracle_rows(bounds):
+    """One worker's share of the parallel oracle run: batch rows [lo, hi)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import build_ref, bwd_ref, scan_ref
+    lo, hi = bounds
+    x, R, n = _POOL["x"][lo:hi], _POOL["R"][lo:hi], _POOL["n"]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        M = build_ref(x, n)
+        scan_ref(M)
+        bwd_ref(M, R)
+        return time.perf_counter() - t0
+
+
+def cpu_leg(w, budget_s: float, max_workers: int = 16):
+    """The fp64 oracle's build + forward + backward on the host, on a bounded
+    sample of the workload (whole sequences, batch rows 0..nb-1, all heads):
+    (i) in this process with BLAS on one thread, (ii) split over batch rows
+    across forked worker processes, one thread each.  Runs before the GPU is
+    touched (the workers are forked).  Returns the baseline record and the
+    oracle's outputs for the first PARITY_ROWS batch rows."""
+    import multiprocessing as mp
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import build_ref, bwd_ref, scan_ref
     from workloads import gen_R, gen_x
 
-    def run(b_rows, h_rows, T):
-        x = gen_x(w.B, w.H, T, w.n, w.sigma_off, w.sigma_diag, w.seed, b_idx=b_rows, h_idx=h_rows)
-        R = gen_R(w.B, w.H, T, w.n, w.seed, b_idx=b_rows, h_idx=h_rows)
+    T = min(w.T, 4096)
+
+    def gen(rows):
+        return (gen_x(w.B, w.H, T, w.n, w.sigma_off, w.sigma_diag, w.seed, b_idx=rows),
+                gen_R(w.B, w.H, T, w.n, w.seed, b_idx=rows))
+
+    def run(x, R):
         t0 = time.perf_counter()
         M = build_ref(x, w.n)
-        scan_ref(M)
-        bwd_ref(M, R)
-        return time.perf_counter() - t0
+        P = scan_ref(M)
+        dM = bwd_ref(M, R)
+        return time.perf_counter() - t0, P, dM
 
     with threadpool_limits(limits=1):
-        T = min(w.T, 4096)
-        dt1 = run([0], [0], T)  # one sequence, to size the sample
-        seqs = max(1, min(w.B * w.H, int(budget_s / max(dt1, 1e-4))))
-        nh = min(w.H, seqs)
-        nb = max(1, min(w.B, seqs // nh))
-        dt = run(list(range(nb)), list(range(nh)), T)
-    head_tokens = nb * nh * T
-    tokens = head_tokens / w.H
-    return {
-        "value": tokens / dt,
+        probe = min(w.B, 4)
+        dt, _, _ = run(*gen(range(probe)))
+        nb = int(min(w.B, max(probe, budget_s / max(dt / probe, 1e-9))))
+        x, R = gen(range(nb))
+        dt, P, dM = run(x, R)
+    keep = min(nb, PARITY_ROWS)
+    ref = (P[:keep].copy(), dM[:keep].copy())
+    del P, dM
+
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0)), nb))
+    _POOL.update(x=x, R=R, n=w.n)
+    cuts = [nb * k // workers for k in range(workers + 1)]
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_oracle_rows, [(0, 1)] * workers)  # start every worker
+        t0 = time.perf_counter()
+        pool.map(_oracle_rows, list(zip(cuts[:-1], cuts[1:])))
+        dt_par = time.perf_counter() - t0
+    _POOL.clear()
+
+    head_tokens = nb * w.H * T
+    rec = {
+        "value": head_tokens / w.H / dt,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{nb} batch rows x {nh} heads x {T} tokens of {w.name} (fp64 numpy build_ref + "
+        "sample": f"{nb} batch rows x {w.H} heads x {T} tokens of {w.name} (fp64 numpy build_ref + "
                   f"scan_ref + bwd_ref, {dt:.1f} s, BLAS limited to 1 thread)",
         "head_tokens_per_s": head_tokens / dt,
+        "parallel": {
+            "value": head_tokens / w.H / dt_par,
+            "unit": "tokens/s",
+            "cores": workers,
+            "sample": f"the same sample split over {workers} forked processes by batch rows, "
+                      f"one BLAS thread each, {dt_par:.2f} s wall",
+        },
     }
+    return rec, ref
+
+
+def cpu_parity(ref, gpu):
+    """Relative Frobenius error per matrix of the GPU's P and dM rows against
+    the oracle's (fp64 build from the same x), with the forward and backward
+    bounds (2e-4, 5e-4)."""
+    import numpy as np
+
+    from oracle import rel_fro_err
+    out = {"rows": f"batch rows 0..{ref[0].shape[0] - 1}, all heads and tokens"}
+    for name, r, g, tol in (("P", ref[0], gpu[0], 2e-4), ("dM", ref[1], gpu[1], 5e-4)):
+        e = rel_fro_err(g[: r.shape[0]].astype(np.float64), r)
+        out[name] = {"max": float(e.max()), "median": float(np.median(e)),
+                     "over_bound": int(np.sum(e > tol)), "bound": tol}
+    return out
 
 
 def kernel_record(kind, avg_ms, S, T, n, workload):
@@ -180,6 +251,51 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
         "matrix_util": round(impl_flops / (med * 1e-3) / 1e12 / peak, 4),
         "data": "synthetic, seeded on the GPU (torch.Generator), same scales as the workload",
     }
+
+
+def fwd_bwd(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
+    """Forward and backward scans (M -> P, then M, P, dL/dP -> dL/dM) on the
+    n = 16 forward+backward workload; inputs generated on the GPU from a seed,
+    dL/dP drawn N(0, 1)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    scale = torch.full((n, n), so, device="cuda")
+    scale.fill_diagonal_(sd)
+    x = (torch.randn((B, H, T, n, n), generator=g, device="cuda") * scale).reshape(B, H, T, n * n)
+    M = mpp.build_inputs(x.contiguous(), n)
+    del x
+    R = torch.randn((B, H, T, n, n), generator=g, device="cuda")
+    P = torch.empty_like(M)
+    dM = torch.empty_like(M)
+    ws_f = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_FWD), 256), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_BWD), 256), dtype=torch.uint8, device="cuda")
+    t_f = _time(torch, lambda: mpp.scan_fwd(M, out=P, workspace=ws_f), reps)
+    t_b = _time(torch, lambda: mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b), reps)
+    S = B * H
+    out = {"workload": f"{name}: B={B},H={H},T={T},n={n}, forward scan then backward scan"}
+    for kind, us in (("fwd", t_f), ("bwd", t_b)):
+        K, nch, Z, _ = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD if kind == "fwd" else mpp.DIR_BWD)
+        # products per token: forward 1, backward 2 (state and dM); multi-chunk
+        # plans run every token twice (aggregate, then from the carry), except
+        # the forward's first chunk of each sequence
+        per = 1 if kind == "fwd" else 2
+        prod = per * S * T * (2.0 if nch > 1 else 1.0) - (S * K if kind == "fwd" and nch > 1 else 0)
+        flops = prod * 2 * n ** 3
+        b = algorithmic_bytes(kind, S, T, n)
+        out[kind] = {
+            "median_us": round(us, 1),
+            "achieved_GBs": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "plan": {"chunk": K, "chunks_per_seq": nch, "super": Z},
+            "matrix_tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "matrix_peak_tflops": FP64_PEAK_TFLOPS,
+            "matrix_util": round(flops / (us * 1e-6) / 1e12 / FP64_PEAK_TFLOPS, 4),
+        }
+    out["tokens_per_s"] = B * T / ((t_f + t_b) * 1e-6)
+    out["data"] = "synthetic, seeded on the GPU (torch.Generator), same scales as the workload"
+    del M, R, P, dM, ws_f, ws_b
+    torch.cuda.empty_cache()
+    return out
 
 
 def unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, workload, reps: int = 10):
@@ -311,22 +427,28 @@ def main():
               f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
         sys.exit(2)
 
+    from workloads import WORKLOADS, gen_R, gen_x
+
+    w = WORKLOADS[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline and not args.extra_only:
+        cpu, cpu_ref = cpu_leg(w, args.cpu_seconds)  # before anything touches the GPU
+
     import numpy as np
     import torch
 
     import matrix_prefix_product_amd as mpp
-    from workloads import WORKLOADS, gen_R, gen_x
 
-    w = WORKLOADS[args.workload]
     B, H, T, n = w.B, w.H, w.T, w.n
     S = B * H
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.extra_only:
-        c3, c4 = WORKLOADS["c3"], WORKLOADS["c4"]
+        c3, c4, c5 = WORKLOADS["c3"], WORKLOADS["c4"], WORKLOADS["c5"]
         extra = {
             "n16": fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3),
             "n32": fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4),
+            "n16_fwd_bwd": fwd_bwd(mpp, torch, "c5", c5.B, c5.H, c5.T, c5.n, c5.sigma_off, c5.sigma_diag, 10, 5),
             "next": next_rows(mpp, torch),
         }
         print(json.dumps(extra), flush=True)
@@ -366,6 +488,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
+    if cpu is not None:
+        rows = cpu_ref[0].shape[0]
+        gpu_rows = (P[:rows].cpu().numpy(), dM[:rows].cpu().numpy())
     ms_per_step = total_ms / args.steps
     per = {k: [] for k in ("fwd_x", "bwd_x")}
     for e in evs:
@@ -418,12 +543,15 @@ def main():
     out["copy_reference"] = copy_reference(torch)
 
     if not args.no_extra:
-        c3, c4 = WORKLOADS["c3"], WORKLOADS["c4"]
+        c3, c4, c5 = WORKLOADS["c3"], WORKLOADS["c4"], WORKLOADS["c5"]
         out["n16"] = fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3)
         out["n32"] = fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4)
+        out["n16_fwd_bwd"] = fwd_bwd(mpp, torch, "c5", c5.B, c5.H, c5.T, c5.n, c5.sigma_off,
+                                     c5.sigma_diag, 10, 5)
         out["next"] = next_rows(mpp, torch)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = time_cpu_baseline(w, args.cpu_seconds)
+    if cpu is not None:
+        cpu["parity_sample"] = cpu_parity(cpu_ref, gpu_rows)
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

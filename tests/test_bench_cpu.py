@@ -40,3 +40,25 @@ def test_counted_sources_exist():
     csrc = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
     for f in bench.COUNTED_SOURCES:
         assert os.path.isfile(os.path.join(csrc, f)), f
+
+
+def test_cpu_leg_and_parity_sample():
+    import numpy as np
+
+    import bench
+    from workloads import WORKLOADS
+    w = WORKLOADS["c2"].with_(T=32)
+    rec, ref = bench.cpu_leg(w, 0.0, max_workers=2)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["value"] > 0
+    assert rec["parallel"]["cores"] >= 1 and rec["parallel"]["value"] > 0
+    P, dM = ref
+    assert 1 <= P.shape[0] <= bench.PARITY_ROWS and P.shape[1:] == (w.H, 32, w.n, w.n)
+    assert dM.shape == P.shape
+    same = bench.cpu_parity(ref, (P.astype(np.float32), dM.astype(np.float32)))
+    assert same["P"]["over_bound"] == 0 and same["dM"]["over_bound"] == 0
+    assert same["P"]["max"] < 1e-6
+    # a wrong row is flagged
+    bad = P.astype(np.float32).copy()
+    bad[0, 0, 5] *= 1.01
+    flagged = bench.cpu_parity(ref, (bad, dM.astype(np.float32)))
+    assert flagged["P"]["over_bound"] == 1 and flagged["P"]["max"] > 5e-3
