@@ -146,7 +146,8 @@ def test_scaled_beyond_fp32_range(mpp, n):
 
 
 BWD_CASES = [(4, 2, 3, 203, 0), (4, 1, 1, 1024, 0), (8, 2, 2, 300, 7), (8, 3, 1, 64, SINGLE),
-             (16, 1, 3, 500, 0), (16, 2, 1, 130, 9), (32, 1, 2, 300, 0), (32, 1, 1, 70, 1)]
+             (16, 1, 3, 500, 0), (16, 2, 1, 130, 9), (16, 1, 2, 512, 32), (32, 1, 2, 300, 0),
+             (32, 1, 1, 70, 1)]
 
 
 @pytest.mark.parametrize("n,B,H,T,chunk", BWD_CASES)

@@ -78,6 +78,7 @@ FWD_CASES = [
     (4, 1, 1, 1024, 0), (4, 3, 2, 203, 3), (4, 5, 1, 300, 300), (4, 2, 2, 97, 1),
     (8, 8, 8, 256, 0), (8, 2, 3, 203, 5), (8, 1, 2, 203, 1), (8, 33, 1, 64, 64), (8, 2, 2, 500, 16),
     (16, 1, 6, 1000, 0), (16, 2, 3, 1000, 7), (16, 3, 1, 257, 257), (16, 1, 2, 130, 1),
+    (16, 2, 3, 1024, 32), (16, 1, 2, 96, 32), (16, 3, 1, 4096, 32),  # chunks dividing T
     (32, 1, 3, 600, 0), (32, 1, 2, 600, 13), (32, 2, 1, 150, 150), (32, 1, 1, 70, 1),
 ]
 
@@ -202,6 +203,7 @@ BWD_CASES = [
     (4, 1, 1, 1024, 0), (4, 3, 2, 203, 3), (4, 2, 2, 97, 1), (4, 5, 1, 120, 120),
     (8, 8, 8, 256, 0), (8, 2, 3, 203, 5), (8, 1, 2, 203, 1), (8, 33, 1, 64, 64), (8, 2, 2, 500, 16),
     (16, 1, 6, 1000, 0), (16, 2, 3, 1000, 7), (16, 3, 1, 257, 257), (16, 1, 2, 130, 1),
+    (16, 2, 3, 1024, 32), (16, 1, 2, 96, 32), (16, 3, 1, 4096, 32),  # chunks dividing T
     (32, 1, 3, 600, 0), (32, 1, 2, 600, 13), (32, 2, 1, 150, 150), (32, 1, 1, 70, 1),
 ]
 
