@@ -60,8 +60,13 @@ int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir) {
         if (S * lanes_per_chain >= 32768) return T;  // >= 512 waves
         target = 16384;                              // 1024 waves of chains
     } else {
-        if (S >= 2048) return T;  // one wave per chain
-        target = 2048;
+        // one wave per chain, one wave per SIMD (1024 SIMDs on MI355X).  Chains
+        // wanted (measured, C3-C5 shapes): n = 32 runs best with one round of
+        // waves (its chunks are long enough to hide the look-back), the n = 16
+        // backward with four, the n = 16 forward with two (then capped by the
+        // register buffer below).
+        target = n == 32 ? 1024 : (dir == 1 ? 4096 : 2048);
+        if (S >= target) return T;
     }
     const int64_t nch = (target + S - 1) / S;
     int64_t K = (T + nch - 1) / nch;
