@@ -423,7 +423,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the MRU scan shards over independent "
-              "sequences with no communication, so this build measures one GPU's share; "
+              "sequences with no communication, so the benchmark measures one GPU's share; "
               f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported.", file=sys.stderr)
         sys.exit(2)
 
