@@ -20,6 +20,8 @@ never stored.  Prints ONE JSON line:
                 and the build's own backward x, dM -> dx) timed alone
   n16, n32      forward-scan throughput on the n=16 and n=32 workloads
   n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload
+  small         the two small workloads (one 1024-token n=4 sequence; the 8x8x256
+                n=8 step): launch-bound latencies
   next          the scaled forward, the orthogonal input builds and a
                 token-by-token decode step with a carried state
   cpu_baseline  the fp64 oracle (oracle/) timed on the host on a bounded sample
@@ -298,6 +300,39 @@ def fwd_bwd(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
     return out
 
 
+def small_configs(mpp, torch, WORKLOADS, gen_R, gen_x, reps: int = 50):
+    """The two small workloads as specified: C1 (one 1024-token sequence, n=4,
+    forward) and C2 (8x8 heads x 256 tokens, n=8, the step: forward from x then
+    backward).  Both are launch-bound and cache-resident (128 KiB / 8 MiB), so
+    they report latency, not bandwidth."""
+    out = {}
+    for name in ("c1", "c2"):
+        w = WORKLOADS[name]
+        x = torch.from_numpy(gen_x(w.B, w.H, w.T, w.n, w.sigma_off, w.sigma_diag, w.seed)).cuda()
+        R = torch.from_numpy(gen_R(w.B, w.H, w.T, w.n, w.seed)).cuda()
+        P = torch.empty((w.B, w.H, w.T, w.n, w.n), device="cuda")
+        dM = torch.empty_like(P)
+        ws_f = torch.empty(max(mpp.workspace_bytes(w.B, w.H, w.T, w.n, mpp.DIR_FWD), 256),
+                           dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(max(mpp.workspace_bytes(w.B, w.H, w.T, w.n, mpp.DIR_BWD), 256),
+                           dtype=torch.uint8, device="cuda")
+        fwd = _time(torch, lambda: mpp.scan_fwd_x(x, w.n, out=P, workspace=ws_f), reps)
+        rec = {"workload": f"{name}: B={w.B},H={w.H},T={w.T},n={w.n}",
+               "plan": dict(zip(("chunk", "chunks_per_seq", "super", "ws_bytes"),
+                                mpp.scan_plan(w.B, w.H, w.T, w.n, mpp.DIR_FWD))),
+               "fwd_x_median_us": round(fwd, 2),
+               "fwd_tokens_per_s": w.B * w.T / (fwd * 1e-6)}
+        if name == "c2":
+            def step():
+                mpp.scan_fwd_x(x, w.n, out=P, workspace=ws_f)
+                mpp.scan_bwd_x(x, P, R, out=dM, workspace=ws_b)
+            st = _time(torch, step, reps)
+            rec["step_median_us"] = round(st, 2)
+            rec["step_tokens_per_s"] = w.B * w.T / (st * 1e-6)
+        out[name] = rec
+    return out
+
+
 def unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, workload, reps: int = 10):
     """The separate kernels on the same inputs: build x -> M, scan M -> P,
     backward from M, and the build's backward (x, dM -> dx)."""
@@ -548,6 +583,7 @@ def main():
         out["n32"] = fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4)
         out["n16_fwd_bwd"] = fwd_bwd(mpp, torch, "c5", c5.B, c5.H, c5.T, c5.n, c5.sigma_off,
                                      c5.sigma_diag, 10, 5)
+        out["small"] = small_configs(mpp, torch, WORKLOADS, gen_R, gen_x)
         out["next"] = next_rows(mpp, torch)
     if cpu is not None:
         cpu["parity_sample"] = cpu_parity(cpu_ref, gpu_rows)
