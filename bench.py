@@ -484,6 +484,7 @@ def main():
             "n16": fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3),
             "n32": fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4),
             "n16_fwd_bwd": fwd_bwd(mpp, torch, "c5", c5.B, c5.H, c5.T, c5.n, c5.sigma_off, c5.sigma_diag, 10, 5),
+            "small": small_configs(mpp, torch, WORKLOADS, gen_R, gen_x),
             "next": next_rows(mpp, torch),
         }
         print(json.dumps(extra), flush=True)
