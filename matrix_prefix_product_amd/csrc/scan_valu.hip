@@ -40,6 +40,10 @@ struct Valu {
     // puts the chains in different banks (an unskewed n*n-float stride sends
     // all chains of a wave to the same banks)
     static constexpr int QX_STRIDE = NN + 4;
+    // floats per chain of the staged e values (fused scans): every lane of a
+    // chain reads its token's n values, and the 16 B skew again keeps the
+    // wave's chains in different banks
+    static constexpr int SE_STRIDE = TB * N + 4;
     static_assert((G * F4_BLK) % 64 == 0, "staging must tile the wave");
     static_assert(N % R == 0 && 64 % LPC == 0, "bad row split");
 };
@@ -243,7 +247,8 @@ __device__ inline void stage_store(float* lds, const float4* reg) {
 // times a dense M, so the fused scans do the same work as the plain ones and
 // move x in place of M.
 //
-// stage_e: e for every staged token (chain-major, TB tokens per chain).
+// stage_e: e for every staged token (chain-major, TB tokens per chain, chains
+// SE_STRIDE floats apart).
 template <int N, int R, int TB>
 __device__ inline void stage_e(const float* lds, float* se) {
     using V = Valu<N, R, TB>;
@@ -256,7 +261,7 @@ __device__ inline void stage_e(const float* lds, float* se) {
         const int tok = f / N;
         const int k = f % N;
         const float* X = lds + (tok / TB) * V::CH_STRIDE + (tok % TB) * V::NN;
-        se[f] = expf(X[k * N + k] - ldu_mean<N>(X));
+        se[(tok / TB) * V::SE_STRIDE + (tok % TB) * N + k] = expf(X[k * N + k] - ldu_mean<N>(X));
     }
 }
 
@@ -386,7 +391,7 @@ __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ 
                 const float* slot = lds + g * V::CH_STRIDE + tau * V::NN;
                 if constexpr (FX) {
                     float ev[N];
-                    load_vec<N>(ev, se + (g * TB + tau) * N);
+                    load_vec<N>(ev, se + g * V::SE_STRIDE + tau * N);
                     rows_times_ldu<N, R>(st, slot, ev);
                 } else {
                     float m[V::NN];
@@ -409,8 +414,8 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
                                                       int64_t K, int64_t nch, int64_t Z,
                                                       unsigned char* __restrict__ ws, ScanCarry cy) {
     using V = Valu<N, R, TB>;
-    __shared__ float lds[V::G * V::CH_STRIDE];
-    __shared__ float se[FX ? V::G * TB * N : 4];
+    __shared__ __align__(16) float lds[V::G * V::CH_STRIDE];
+    __shared__ __align__(16) float se[FX ? V::G * V::SE_STRIDE : 4];
     __shared__ __align__(16) float xch[V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
@@ -567,7 +572,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
             const bool live = i < me.len;
             const int64_t tseq = int64_t(me.t0) + pos;
             const float* mslot = lds + g * V::CH_STRIDE + tau * V::NN;
-            const float* eslot = se + (g * TB + tau) * N;
+            const float* eslot = se + g * V::SE_STRIDE + tau * N;
             const float* rslot = lds + V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN;
             if (live) {
                 if (tseq + 1 < T) {
@@ -658,8 +663,8 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
                                                       int64_t Z, unsigned char* __restrict__ ws,
                                                       ScanCarry cy) {
     using V = Valu<N, R, TB>;
-    __shared__ float lds[3 * V::G * V::CH_STRIDE];
-    __shared__ float se[FX ? V::G * TB * N : 4];
+    __shared__ __align__(16) float lds[3 * V::G * V::CH_STRIDE];
+    __shared__ __align__(16) float se[FX ? V::G * V::SE_STRIDE : 4];
     __shared__ __align__(16) float qx[V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
