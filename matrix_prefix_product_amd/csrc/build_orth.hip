@@ -6,10 +6,12 @@
 //   exponential:  M = exp(A)
 // Both are orthogonal with det M = 1, so a scan of them keeps |P_t|_F = sqrt(n).
 //
-// A chain of n lanes works on one token, lane i owning row i, in fp64 (the
+// On the vector ALUs (Cayley for every n, the exponential for n = 4, 8) a
+// chain of n lanes works on one token, lane i owning row i, in fp64 (the
 // vector fp64 rate equals the fp32 one on CDNA4, and fp64 keeps the only
 // rounding of the result the final one to fp32).  Rows of the other lanes come
-// through LDS.
+// through LDS.  The exponential for n = 16, 32 runs on the matrix cores
+// (build_expm_mfma_kernel below), also in fp64.
 //   Cayley: Gauss-Jordan elimination on [I - A | I + A].  No pivoting is needed:
 //     the symmetric part of I - A is I, so every leading block is nonsingular.
 //   Exponential: scaling and squaring.  A is scaled by 2^-s (exact) so that its
@@ -20,6 +22,7 @@
 //     depends on the tokens it shares a wave with.
 #include "mru_device.h"
 #include "mru_kernels.h"
+#include "mru_mfma.h"
 
 namespace mru {
 namespace {
@@ -170,6 +173,85 @@ __global__ __launch_bounds__(64) void build_orth_kernel(const float* __restrict_
     }
 }
 
+// Exponential for n = 16 and 32 on the matrix cores: the same scaling and
+// squaring (Horner's rule to degree 12, then s squarings), one token per wave,
+// every product a chain of fp64 16x16x4 MFMAs in the tile layout of
+// mru_mfma.h.  The accumulator holds E = exp(-A), which is exp(A)^T because A
+// is skew-symmetric, so that writing the accumulator's rows the way the scans
+// write P stores exp(A) row-major.  The Horner products take -A as their left
+// operand (formed once per token from the staged X); a squaring takes E
+// itself, through one LDS transpose.
+template <int N>
+__global__ __launch_bounds__(64) void build_expm_mfma_kernel(const float* __restrict__ x,
+                                                             float* __restrict__ M, int64_t ntok) {
+    using F = Mf<N>;
+    using vec_t = typename F::vec_t;
+    constexpr int NT = F::NT;
+    constexpr int NN = N * N;
+    __shared__ __align__(16) float xs[NN];
+    __shared__ __align__(16) double es[NN];
+    const int l = threadIdx.x & 63;
+    for (int64_t tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NN / 256; ++q)
+            reinterpret_cast<float4*>(xs)[q * 64 + l] =
+                reinterpret_cast<const float4*>(x + tok * NN)[q * 64 + l];
+        __syncthreads();
+        // s from the largest absolute row sum of A (lane i < n sums row i)
+        double rs = 0.0;
+        if (l < N) {
+#pragma unroll
+            for (int j = 0; j < N; ++j) rs += fabs(0.5 * (double(xs[l * N + j]) - double(xs[j * N + l])));
+        }
+        const double nrm = group_max_d<64>(rs);
+        const int s = nrm > 0.5 ? frexp_exp(nrm) + 1 : 0;  // nrm < 2^e, so nrm 2^-s <= 1/2
+        // left operand: -A 2^-s, entry (16I + tacol, 16K + trow(b)) of tile (I, K)
+        typename F::aop_t a;
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int K = 0; K < NT; ++K)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int r = 16 * I + tacol(l), c = 16 * K + trow(l, b);
+                    a.v[I][K][b] = ldexp(0.5 * (double(xs[c * N + r]) - double(xs[r * N + c])), -s);
+                }
+        // Horner: E = I + (-A E) / d for d = 12 .. 1, from E = I
+        vec_t E = videntity<N>(l);
+#pragma unroll 1
+        for (int d = kTaylorDegree; d >= 1; --d) {
+            const vec_t AE = chain_step<N>(a, E, vzero<N>());
+            const double inv = 1.0 / double(d);
+#pragma unroll
+            for (int I = 0; I < NT; ++I)
+#pragma unroll
+                for (int J = 0; J < NT; ++J)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        E.t[I][J][r] = fma(AE.t[I][J][r], inv,
+                                           (16 * I + trow(l, r) == 16 * J + tcol(l)) ? 1.0 : 0.0);
+        }
+#pragma unroll 1
+        for (int q = 0; q < s; ++q) {
+            typename F::aop_t ae;
+            __syncthreads();
+            store_acc_rows<N, double>(es, E);  // E^T row-major
+            __syncthreads();
+            load_a_transposed<N, double>(ae, es);  // E as the left operand
+            E = chain_step<N>(ae, E, vzero<N>());
+        }
+        store_acc_rows<N, float>(M + tok * NN, E);  // E^T = exp(A), row-major
+    }
+}
+
+template <int N>
+hipError_t run_expm_mfma(const float* x, float* M, int64_t ntok, hipStream_t stream) {
+    const unsigned blocks = unsigned(ntok < 16384 ? ntok : 16384);
+    hipLaunchKernelGGL((build_expm_mfma_kernel<N>), dim3(blocks), dim3(64), 0, stream, x, M, ntok);
+    return hipGetLastError();
+}
+
 template <int N, int METHOD>
 hipError_t run_orth(const float* x, float* M, int64_t ntok, hipStream_t stream) {
     const int64_t groups = (ntok + Orth<N>::TPW - 1) / Orth<N>::TPW;
@@ -183,8 +265,12 @@ hipError_t run_orth_n(const float* x, float* M, int64_t ntok, int n, hipStream_t
     switch (n) {
         case 4: return run_orth<4, METHOD>(x, M, ntok, stream);
         case 8: return run_orth<8, METHOD>(x, M, ntok, stream);
-        case 16: return run_orth<16, METHOD>(x, M, ntok, stream);
-        case 32: return run_orth<32, METHOD>(x, M, ntok, stream);
+        case 16:
+            if constexpr (METHOD == 1) return run_expm_mfma<16>(x, M, ntok, stream);
+            else return run_orth<16, METHOD>(x, M, ntok, stream);
+        case 32:
+            if constexpr (METHOD == 1) return run_expm_mfma<32>(x, M, ntok, stream);
+            else return run_orth<32, METHOD>(x, M, ntok, stream);
         default: return hipErrorInvalidValue;
     }
 }
