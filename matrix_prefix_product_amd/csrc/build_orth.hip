@@ -173,6 +173,104 @@ __global__ __launch_bounds__(64) void build_orth_kernel(const float* __restrict_
     }
 }
 
+// Cayley map by columns (n = 8, 16, 32): lane j of a token's 2n lanes owns
+// column j of the augmented matrix [I - A | I + A].  Gauss-Jordan without
+// pivoting, as above, with the same arithmetic on every entry (the pivot row
+// scaled by the reciprocal of the pivot, then one fused multiply-add per entry
+// and step, steps in order), so the result is bitwise that of the row kernel.
+// But a step needs only the pivot column (n values held by one lane; each
+// lane's own pivot-row entry is in its registers), and it reaches the other
+// lanes without LDS: for n = 8 a token is one 16-lane row and a DPP row
+// broadcast moves each value; for n = 16, 32 a wave works on one token (for
+// n = 16 the upper 32 lanes idle) and readlane puts the pivot column in scalar
+// registers, which the multiply-adds read directly.  Lanes n..2n-1 end up
+// holding the columns of M.  (n = 4 keeps the row kernel: two 8-lane tokens
+// per row need two masked broadcasts per value, which measured slower.)
+template <int B, int E, class F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Value of v in lane k of the lane's token (k a compile-time constant).
+template <int N, int k>
+__device__ inline double bcast_col(double v) {
+    const int lo = __double2loint(v), hi = __double2hiint(v);
+    int rlo, rhi;
+    if constexpr (N == 8) {
+        rlo = __builtin_amdgcn_update_dpp(0, lo, 0x150 + k, 0xF, 0xF, false);  // row_newbcast:k
+        rhi = __builtin_amdgcn_update_dpp(0, hi, 0x150 + k, 0xF, 0xF, false);
+    } else {  // one token per wave, starting at lane 0
+        rlo = __builtin_amdgcn_readlane(lo, k);
+        rhi = __builtin_amdgcn_readlane(hi, k);
+    }
+    return __hiloint2double(rhi, rlo);
+}
+
+template <int N>
+__global__ __launch_bounds__(64) void build_cayley_cols_kernel(const float* __restrict__ x,
+                                                               float* __restrict__ M, int64_t ntok) {
+    static_assert(N == 8 || N == 16 || N == 32, "column kernel for n = 8, 16, 32");
+    constexpr int NN = N * N;
+    constexpr int W = 2 * N;                    // lanes per token
+    constexpr int TPW = N == 8 ? 64 / W : 1;    // tokens per wave
+    constexpr int XS = TPW * NN;                // staged floats per wave
+    __shared__ __align__(16) float xs[XS];
+    const int lane = threadIdx.x & 63;
+    const int tk = TPW > 1 ? lane / W : 0;      // token of the wave
+    const int j = lane % W;                     // column of [I - A | I + A]
+    const int jc = j % N;                       // column of A
+    const double sgn = j < N ? -1.0 : 1.0;
+    const bool owner = TPW > 1 || lane < W;     // lanes 32-63 idle for n = 16
+    const int64_t groups = (ntok + TPW - 1) / TPW;
+    for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+        const int64_t tok0 = grp * TPW;
+        const int64_t tok = tok0 + tk;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < XS / 256; ++q) {
+            const int f = q * 64 + lane;  // float4 index within the wave's tokens
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (tok0 + (f * 4) / NN < ntok) v = reinterpret_cast<const float4*>(x + tok0 * NN)[f];
+            reinterpret_cast<float4*>(xs)[f] = v;
+        }
+        __syncthreads();
+        const float* X = xs + tk * NN;
+        double col[N];  // column j: I -/+ A
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            col[i] = (i == jc ? 1.0 : 0.0) + sgn * (0.5 * (double(X[i * N + jc]) - double(X[jc * N + i])));
+        static_for<0, N>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            const double piv = bcast_col<N, k>(col[k]);  // pivot, from column k
+            const double r = col[k] * (1.0 / piv);       // this column's pivot-row entry
+            static_for<0, N>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i != k) {
+                    const double m = bcast_col<N, k>(col[i]);  // pivot column, row i
+                    col[i] = fma(-m, r, col[i]);
+                }
+            });
+            col[k] = r;
+        });
+        if (owner && j >= N && tok < ntok) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) M[tok * NN + i * N + jc] = float(col[i]);
+        }
+    }
+}
+
+template <int N>
+hipError_t run_cayley_cols(const float* x, float* M, int64_t ntok, hipStream_t stream) {
+    constexpr int TPW = N == 8 ? 64 / (2 * N) : 1;
+    const int64_t groups = (ntok + TPW - 1) / TPW;
+    const unsigned blocks = unsigned(groups < 16384 ? groups : 16384);
+    hipLaunchKernelGGL((build_cayley_cols_kernel<N>), dim3(blocks), dim3(64), 0, stream, x, M, ntok);
+    return hipGetLastError();
+}
+
 // Exponential for n = 16 and 32 on the matrix cores: the same scaling and
 // squaring (Horner's rule to degree 12, then s squarings), one token per wave,
 // every product a chain of fp64 16x16x4 MFMAs in the tile layout of
@@ -262,16 +360,22 @@ hipError_t run_orth(const float* x, float* M, int64_t ntok, hipStream_t stream) 
 
 template <int METHOD>
 hipError_t run_orth_n(const float* x, float* M, int64_t ntok, int n, hipStream_t stream) {
-    switch (n) {
-        case 4: return run_orth<4, METHOD>(x, M, ntok, stream);
-        case 8: return run_orth<8, METHOD>(x, M, ntok, stream);
-        case 16:
-            if constexpr (METHOD == 1) return run_expm_mfma<16>(x, M, ntok, stream);
-            else return run_orth<16, METHOD>(x, M, ntok, stream);
-        case 32:
-            if constexpr (METHOD == 1) return run_expm_mfma<32>(x, M, ntok, stream);
-            else return run_orth<32, METHOD>(x, M, ntok, stream);
-        default: return hipErrorInvalidValue;
+    if constexpr (METHOD == 0) {  // Cayley
+        switch (n) {
+            case 4: return run_orth<4, 0>(x, M, ntok, stream);
+            case 8: return run_cayley_cols<8>(x, M, ntok, stream);
+            case 16: return run_cayley_cols<16>(x, M, ntok, stream);
+            case 32: return run_cayley_cols<32>(x, M, ntok, stream);
+            default: return hipErrorInvalidValue;
+        }
+    } else {  // exponential
+        switch (n) {
+            case 4: return run_orth<4, 1>(x, M, ntok, stream);
+            case 8: return run_orth<8, 1>(x, M, ntok, stream);
+            case 16: return run_expm_mfma<16>(x, M, ntok, stream);
+            case 32: return run_expm_mfma<32>(x, M, ntok, stream);
+            default: return hipErrorInvalidValue;
+        }
     }
 }
 
