@@ -69,8 +69,14 @@ def source_hash() -> str:
 
 
 def algorithmic_bytes(kind: str, S: int, T: int, n: int) -> int:
-    # bytes per matrix entry per token-head
+    # bytes per matrix entry per token-head (4-byte entries): build reads x and
+    # writes M, forward reads M (or x) and writes P, build backward reads x and
+    # dM and writes dx.  The backward reads M (or x) and dP and writes dM; for
+    # n <= 8 it reads one stored prefix per 4 tokens (recomputing the others),
+    # 13 bytes in all, for n = 16, 32 every prefix, 16.
     per = {"build": 8, "fwd": 8, "bwd": 16, "fwd_x": 8, "bwd_x": 16, "build_bwd": 12}[kind]
+    if kind in ("bwd", "bwd_x") and n <= 8:
+        per = 13
     return per * n * n * S * T
 
 

@@ -198,6 +198,10 @@ mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_
  *
  * M   [B][H][T][n][n] fp32, read (the forward inputs).
  * P   [B][H][T][n][n] fp32, read (the forward outputs of mru_scan_fwd on M).
+ *     For n in {4, 8} only one prefix in four is read (the one before each
+ *     block of four tokens, counted from a chunk's end) and the prefixes in
+ *     between are recomputed from it and M, so P must be the forward's output
+ *     on this M (up to rounding); n in {16, 32} reads every prefix.
  * dP  [B][H][T][n][n] fp32, read.
  * dM  [B][H][T][n][n] fp32, written.
  * chunk, ws, ws_bytes as for mru_scan_fwd with direction MRU_DIR_BWD.

@@ -24,6 +24,17 @@ __device__ inline float ldu_mean(const float* X) {
     return sum * (1.0f / N);
 }
 
+// The same mean from the diagonal already gathered, d[k] = X_kk: the same sum
+// in the same order, so the same rounded value.
+template <int N>
+__device__ inline float ldu_mean_diag(const float (&d)[N]) {
+#pragma clang fp contract(off)
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) sum += d[k];
+    return sum * (1.0f / N);
+}
+
 // acc[j] = M_ij for j = 0..N-1, given e[k] = exp(X_kk - mean).  The k loop is
 // fully unrolled for N <= 16 (U's zero pattern resolved at compile time) and
 // kept rolled with U's zeros masked for N = 32 (register pressure); both add

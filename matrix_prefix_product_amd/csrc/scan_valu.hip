@@ -12,7 +12,9 @@
 // state is R rows of P_t = P_{t-1} M_t.
 // Backward (gradient of sum_t <dP_t, P_t>): the chain state is R rows of
 // Q_t = dP_t + Q_{t+1} M_{t+1}^T, swept from the last token to the first, and
-// dM_t = P_{t-1}^T Q_t needs all rows of Q_t, exchanged through LDS.
+// dM_t = P_{t-1}^T Q_t needs all rows of Q_t and of P_{t-1}, exchanged through
+// LDS.  The backward reads one stored prefix per TB tokens and recomputes the
+// others from it (VALU work is cheap here, HBM bytes are not).
 #include "mru_build.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
@@ -40,10 +42,8 @@ struct Valu {
     // puts the chains in different banks (an unskewed n*n-float stride sends
     // all chains of a wave to the same banks)
     static constexpr int QX_STRIDE = NN + 4;
-    // floats per chain of the staged e values (fused scans): every lane of a
-    // chain reads its token's n values, and the 16 B skew again keeps the
-    // wave's chains in different banks
-    static constexpr int SE_STRIDE = TB * N + 4;
+    // floats per chain of the backward's kept input matrix (16 B skew, as above)
+    static constexpr int NX_STRIDE = NN + 4;
     static_assert((G * F4_BLK) % 64 == 0, "staging must tile the wave");
     static_assert(N % R == 0 && 64 % LPC == 0, "bad row split");
 };
@@ -247,41 +247,46 @@ __device__ inline void stage_store(float* lds, const float4* reg) {
 // times a dense M, so the fused scans do the same work as the plain ones and
 // move x in place of M.
 //
-// stage_e: e for every staged token (chain-major, TB tokens per chain, chains
-// SE_STRIDE floats apart).
+// stage_e: replaces the diagonal of every staged token by its e values (the
+// diagonal of X is needed for nothing else), so a product reads the token's
+// factors as one n-by-n block with full 16-byte loads.  A token's e values are
+// shared out over 64/(G*TB) lanes (or a lane takes G*TB/64 whole tokens); each
+// lane reads its token's diagonal once and forms the mean from it.  All of a
+// token's reads precede its writes in the one wave's program order.
 template <int N, int R, int TB>
-__device__ inline void stage_e(const float* lds, float* se) {
+__device__ inline void stage_e(float* lds) {
     using V = Valu<N, R, TB>;
-    constexpr int VALS = V::G * TB * N;
-    static_assert(VALS % 64 == 0, "e values must tile the wave");
+    constexpr int TOKS = V::G * TB;                  // staged tokens of the wave
+    constexpr int LPT = TOKS >= 64 ? 1 : 64 / TOKS;  // lanes per token
+    constexpr int TPL = TOKS >= 64 ? TOKS / 64 : 1;  // tokens per lane
+    constexpr int KPL = N / LPT;                     // e values per lane and token
+    static_assert(TOKS % 64 == 0 || 64 % TOKS == 0, "tokens must tile the wave");
+    static_assert(N % LPT == 0, "e values must split evenly over a token's lanes");
     const int lane = threadIdx.x & 63;
+    const int part = lane % LPT;
 #pragma unroll
-    for (int q = 0; q < VALS / 64; ++q) {
-        const int f = q * 64 + lane;
-        const int tok = f / N;
-        const int k = f % N;
-        const float* X = lds + (tok / TB) * V::CH_STRIDE + (tok % TB) * V::NN;
-        se[(tok / TB) * V::SE_STRIDE + (tok % TB) * N + k] = expf(X[k * N + k] - ldu_mean<N>(X));
+    for (int u = 0; u < TPL; ++u) {
+        const int tok = u * 64 + lane / LPT;
+        float* X = lds + (tok / TB) * V::CH_STRIDE + (tok % TB) * V::NN;
+        float d[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) d[k] = X[k * N + k];
+        const float mean = ldu_mean_diag<N>(d);
+#pragma unroll
+        for (int kk = 0; kk < KPL; ++kk) {
+            float v = d[kk];
+#pragma unroll
+            for (int h = 1; h < LPT; ++h) v = part == h ? d[h * KPL + kk] : v;
+            const int k = part * KPL + kk;
+            X[k * N + k] = expf(v - mean);
+        }
     }
 }
 
-template <int N>
-__device__ inline void load_vec(float (&v)[N], const float* src) {
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-        const float4 t = reinterpret_cast<const float4*>(src)[q];
-        v[4 * q] = t.x;
-        v[4 * q + 1] = t.y;
-        v[4 * q + 2] = t.z;
-        v[4 * q + 3] = t.w;
-    }
-}
-
-// st <- st * (L diag(e) U), in place per row.
+// st <- st * (L diag(e) U), in place per row; x holds L below, e on and U
+// above the diagonal.
 template <int N, int R>
-__device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const float (&ev)[N]) {
-    float x[N * N];
-    load_matrix<N>(x, X);
+__device__ inline void rows_times_ldu(float (&st)[R][N], const float (&x)[N * N]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         // times L: r_j += sum_{i > j} r_i X_ij, ascending j reads only untouched r_i
@@ -290,7 +295,7 @@ __device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const f
 #pragma unroll
             for (int i = j + 1; i < N; ++i) st[r][j] = fmaf(st[r][i], x[i * N + j], st[r][j]);
 #pragma unroll
-        for (int j = 0; j < N; ++j) st[r][j] *= ev[j];
+        for (int j = 0; j < N; ++j) st[r][j] *= x[j * N + j];
         // times U: r_j += sum_{k < j} r_k X_kj, descending j reads only untouched r_k
 #pragma unroll
         for (int j = N - 1; j > 0; --j)
@@ -299,11 +304,17 @@ __device__ inline void rows_times_ldu(float (&st)[R][N], const float* X, const f
     }
 }
 
-// st <- st * (L diag(e) U)^T = st * U^T diag(e) L^T, in place per row.
 template <int N, int R>
-__device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X, const float (&ev)[N]) {
+__device__ inline void rows_times_ldu(float (&st)[R][N], const float* X) {
     float x[N * N];
     load_matrix<N>(x, X);
+    rows_times_ldu<N, R>(st, x);
+}
+
+// st <- st * (L diag(e) U)^T = st * U^T diag(e) L^T, in place per row (x as
+// for rows_times_ldu).
+template <int N, int R>
+__device__ inline void rows_times_ldu_t(float (&st)[R][N], const float (&x)[N * N]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         // times U^T: r_j += sum_{k > j} r_k X_jk, ascending j
@@ -312,13 +323,20 @@ __device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X, const
 #pragma unroll
             for (int k = j + 1; k < N; ++k) st[r][j] = fmaf(st[r][k], x[j * N + k], st[r][j]);
 #pragma unroll
-        for (int j = 0; j < N; ++j) st[r][j] *= ev[j];
+        for (int j = 0; j < N; ++j) st[r][j] *= x[j * N + j];
         // times L^T: r_j += sum_{k < j} r_k X_jk, descending j
 #pragma unroll
         for (int j = N - 1; j > 0; --j)
 #pragma unroll
             for (int k = 0; k < j; ++k) st[r][j] = fmaf(st[r][k], x[j * N + k], st[r][j]);
     }
+}
+
+template <int N, int R>
+__device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X) {
+    float x[N * N];
+    load_matrix<N>(x, X);
+    rows_times_ldu_t<N, R>(st, x);
 }
 
 // Scaled state (scaled forward scan): a chain's rows hold S with P = 2^ex S.
@@ -366,10 +384,11 @@ __device__ inline void init_rows(float (&st)[R][N], int& ex, const ScanCarry& cy
 
 // One sweep of a forward chain over its chunk: st <- st * M_t for each token,
 // optionally storing the rows of every P_t.  With FX the input is x and each
-// step multiplies by M_t's factors (se holds the staged tokens' e).
+// step multiplies by M_t's factors (stage_e puts each staged token's e on its
+// diagonal).
 template <int N, int R, int TB, bool WRITE, bool FX, bool SC>
 __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ M,
-                          float* __restrict__ P, int32_t* __restrict__ pexp, float* lds, float* se,
+                          float* __restrict__ P, int32_t* __restrict__ pexp, float* lds,
                           const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
@@ -381,7 +400,7 @@ __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ 
         __syncthreads();
         if (blk + TB < maxlen) stage_load<N, R, TB, false>(reg, M, info, blk + TB, 0, T);
         if constexpr (FX) {
-            stage_e<N, R, TB>(lds, se);
+            stage_e<N, R, TB>(lds);
             __syncthreads();
         }
 #pragma unroll
@@ -390,9 +409,7 @@ __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ 
             if (pos < me.len) {
                 const float* slot = lds + g * V::CH_STRIDE + tau * V::NN;
                 if constexpr (FX) {
-                    float ev[N];
-                    load_vec<N>(ev, se + g * V::SE_STRIDE + tau * N);
-                    rows_times_ldu<N, R>(st, slot, ev);
+                    rows_times_ldu<N, R>(st, slot);
                 } else {
                     float m[V::NN];
                     load_matrix<N>(m, slot);
@@ -415,7 +432,6 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
                                                       unsigned char* __restrict__ ws, ScanCarry cy) {
     using V = Valu<N, R, TB>;
     __shared__ __align__(16) float lds[V::G * V::CH_STRIDE];
-    __shared__ __align__(16) float se[FX ? V::G * V::SE_STRIDE : 4];
     __shared__ __align__(16) float xch[V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
@@ -439,7 +455,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     const int64_t seq = c < nchunks ? c / nch : 0;  // idle chains read sequence 0, write nothing
     if (!multi) {
         init_rows<N, R, SC>(st, ex, cy, seq, li);
-        fwd_sweep<N, R, TB, true, FX, SC>(st, ex, M, P, cy.out_exp, lds, se, info, g, li, maxlen, T);
+        fwd_sweep<N, R, TB, true, FX, SC>(st, ex, M, P, cy.out_exp, lds, info, g, li, maxlen, T);
         return;
     }
 
@@ -457,7 +473,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
 
     // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised rows)
     set_identity_rows<N, R>(st, li * R);
-    fwd_sweep<N, R, TB, false, FX, SC>(st, ex, M, P, cy.out_exp, lds, se, info, g, li, maxlen, T);
+    fwd_sweep<N, R, TB, false, FX, SC>(st, ex, M, P, cy.out_exp, lds, info, g, li, maxlen, T);
     const int a_ex = ex;
     ws_store_rows<N, R>(agg + c * V::NN + li * R * N, st);
     if (SC && li == 0) ws_store(&agg_exp[c], int32_t(a_ex));
@@ -525,45 +541,131 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from its carry and write every prefix
-    fwd_sweep<N, R, TB, true, FX, SC>(st, ex, M, P, cy.out_exp, lds, se, info, g, li, maxlen, T);
+    fwd_sweep<N, R, TB, true, FX, SC>(st, ex, M, P, cy.out_exp, lds, info, g, li, maxlen, T);
 }
 
 // ---------------------------------------------------------------------------- backward
 
-// One reverse sweep over the chunk.
+// One reverse sweep over the chunk, from its last token down, TB tokens per
+// staged block.  A block stages M_t (x_t) and dP_t of its own tokens; M_{t+1}
+// of a token is the slot staged before it, and for the block's first token the
+// previous block's last slot, kept per chain in nx (before the first block: the
+// token after the chunk, when the sequence has one).
 //   AGG pass  (GRAD = false): q <- dP_t + q M_{t+1}^T and w <- w M_{t+1}^T, from
 //             q = 0, w = I; afterwards q is the chunk's local adjoint at its first
 //             token and w the rows of (M_{a+1} ... M_{b+1})^T.
 //   GRAD pass (GRAD = true):  q <- dP_t + q M_{t+1}^T from the carry, and
-//             dM_t = P_{t-1}^T Q_t written for the lane's rows.
+//             dM_t = P_{t-1}^T Q_t written for the lane's rows.  Of P only the
+//             prefix just before each block's lowest token is read; the block's
+//             other P_{t-1} are recomputed from it by the forward recurrence
+//             P_t = P_{t-1} M_t, with the same products as the forward scan (so
+//             bit for bit the stored prefixes when P came from the matching
+//             forward scan).  This reads n^2 floats per block instead of per token.
 // At the last token of a sequence there is no M_{t+1}: q <- dP_t.
 template <int N, int R, int TB, bool GRAD, bool FX>
 __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
                           const float* __restrict__ P, const float* __restrict__ dP,
-                          float* __restrict__ dM, float* lds, float* se, float* qx,
+                          float* __restrict__ dM, float* lds, float* nx, float* qx,
                           const ChainInfo* info, int g, int li, int maxlen, int64_t T,
                           const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
-    constexpr int ARR = GRAD ? 3 : 2;  // staged arrays: M(t+1), dP(t), [P(t-1)]
     const ChainInfo me = info[g];
     const int64_t s0 = me.base - me.t0;  // token index of the sequence's first token
-    float4 rm[V::LD], rr[V::LD], rp[V::LD];
-    auto load_all = [&](int blk) {
-        stage_load<N, R, TB, true>(rm, M, info, blk, +1, T);
-        stage_load<N, R, TB, true>(rr, dP, info, blk, 0, T);
-        if (GRAD) stage_load<N, R, TB, true>(rp, P, info, blk, -1, T);
+    float* const xl = lds + g * V::CH_STRIDE;                          // staged M_t
+    float* const rl = lds + V::G * V::CH_STRIDE + g * V::CH_STRIDE;    // staged dP_t
+    float* const nxg = nx + g * V::NX_STRIDE;                          // M_{t+1}
+    float* const qxg = qx + g * V::QX_STRIDE;                          // Q_t rows
+    float* const pxg = qx + (V::G + g) * V::QX_STRIDE;                 // P_{t-1} rows
+    float4 rm[V::LD], rr[V::LD];
+    float ck[R][N];  // rows of P just before the lowest token of the next block
+    bool ck_id = false;
+    // Rows of that prefix: P itself inside the sequence, else P_0 (the carried-in
+    // state, or I).  The load is unconditional from a valid address.
+    auto load_checkpoint = [&](int blk) {
+        const int lo = max(me.len - blk - TB, 0);
+        const int64_t tc = int64_t(me.t0) + lo - 1;
+        const float* src = P;  // idle chains (a padding chunk may lie past the array)
+        if (me.len > 0) {
+            if (tc >= 0) src = P + (me.base + lo - 1) * V::NN;
+            else if (cy.carry) src = cy.carry + (s0 / T) * V::NN;
+        }
+        ck_id = tc < 0 && !cy.carry;
+        load_rows<N, R>(ck, src + li * R * N);
     };
-    if (maxlen > 0) load_all(0);
+    auto load_block = [&](int blk) {
+        stage_load<N, R, TB, true>(rm, M, info, blk, 0, T);
+        stage_load<N, R, TB, true>(rr, dP, info, blk, 0, T);
+        if constexpr (GRAD) load_checkpoint(blk);
+    };
+    {
+        // M_{t+1} of the chunk's last token
+        float t[R][N];
+        if (me.len > 0 && int64_t(me.t0) + me.len < T)
+            load_rows<N, R>(t, M + (me.base + me.len) * V::NN + li * R * N);
+        else
+            set_zero_rows<N, R>(t);
+        store_rows<N, R>(nxg + li * R * N, t);
+        if constexpr (FX) {
+            // its e on the diagonal, as stage_e does for staged tokens
+            __syncthreads();
+            const float mean = ldu_mean<N>(nxg);
+            float e[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) e[r] = expf(nxg[(li * R + r) * (N + 1)] - mean);
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < R; ++r) nxg[(li * R + r) * (N + 1)] = e[r];
+        }
+    }
+    if (maxlen > 0) load_block(0);
     for (int blk = 0; blk < maxlen; blk += TB) {
         __syncthreads();
         stage_store<N, R, TB>(lds, rm);
         stage_store<N, R, TB>(lds + V::G * V::CH_STRIDE, rr);
-        if (GRAD) stage_store<N, R, TB>(lds + 2 * V::G * V::CH_STRIDE, rp);
+        float cur[R][N];
+        if constexpr (GRAD) {
+            if (ck_id)
+                set_identity_rows<N, R>(cur, li * R);
+            else
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < N; ++j) cur[r][j] = ck[r][j];
+        }
         __syncthreads();
-        if (blk + TB < maxlen) load_all(blk + TB);
+        if (blk + TB < maxlen) load_block(blk + TB);
         if constexpr (FX) {
-            stage_e<N, R, TB>(lds, se);  // factors of M_{t+1} from x_{t+1}
+            stage_e<N, R, TB>(lds);
             __syncthreads();
+        }
+        // rp[tau]: the lane's rows of P_{t-1} for the block's token tau, from the
+        // block's lowest live token (tau = min(TB-1, hi)) upward
+        float rp[GRAD ? TB : 1][R][N];
+        if constexpr (GRAD) {
+            const int hi = me.len - 1 - blk;
+#pragma unroll
+            for (int tau = TB - 1; tau >= 0; --tau) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < N; ++j) rp[tau][r][j] = tau == TB - 1 ? cur[r][j] : rp[tau + 1][r][j];
+                if (tau < TB - 1) {
+                    // P_{t-1} of token tau = P_{t-1} of token tau+1 times M_t of token tau+1
+                    const float* slot = xl + (tau + 1) * V::NN;
+                    if constexpr (FX) {
+                        rows_times_ldu<N, R>(rp[tau], slot);
+                    } else {
+                        float m[V::NN];
+                        load_matrix<N>(m, slot);
+                        rows_times<N, R>(rp[tau], m);
+                    }
+                    if (tau >= hi)
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int j = 0; j < N; ++j) rp[tau][r][j] = cur[r][j];
+                }
+            }
         }
 #pragma unroll
         for (int tau = 0; tau < TB; ++tau) {
@@ -571,16 +673,14 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
             const int pos = me.len - 1 - i;
             const bool live = i < me.len;
             const int64_t tseq = int64_t(me.t0) + pos;
-            const float* mslot = lds + g * V::CH_STRIDE + tau * V::NN;
-            const float* eslot = se + g * V::SE_STRIDE + tau * N;
-            const float* rslot = lds + V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN;
+            const float* mslot = tau == 0 ? nxg : xl + (tau - 1) * V::NN;
             if (live) {
                 if (tseq + 1 < T) {
                     if constexpr (FX) {
-                        float ev[N];
-                        load_vec<N>(ev, eslot);
-                        rows_times_ldu_t<N, R>(q, mslot, ev);
-                        if (!GRAD) rows_times_ldu_t<N, R>(w, mslot, ev);
+                        float x[V::NN];
+                        load_matrix<N>(x, mslot);
+                        rows_times_ldu_t<N, R>(q, x);
+                        if (!GRAD) rows_times_ldu_t<N, R>(w, x);
                     } else {
                         float m[V::NN];
                         load_matrix<N>(m, mslot);
@@ -590,37 +690,35 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                 } else {
                     set_zero_rows<N, R>(q);
                 }
-                add_rows<N, R>(q, rslot + li * R * N);
+                add_rows<N, R>(q, rl + tau * V::NN + li * R * N);
             }
-            if (GRAD) {
-                // exchange Q_t rows within the chain, then dM rows a = own rows:
-                // dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
+            if constexpr (GRAD) {
+                // exchange the rows of Q_t and P_{t-1} within the chain, then
+                // dM rows a = own rows: dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
                 __syncthreads();
-                if (live) store_rows<N, R>(qx + g * V::QX_STRIDE + li * R * N, q);
+                if (live) {
+                    store_rows<N, R>(qxg + li * R * N, q);
+                    store_rows<N, R>(pxg + li * R * N, rp[tau]);
+                }
                 __syncthreads();
                 if (live) {
                     float d[R][N];
-                    // d = Pprev^T Q_t for the lane's rows, Pprev row-major at src
-                    auto times_prev = [&](const float* src) {
+                    if (tseq > 0 || cy.carry) {
                         float qa[V::NN];
-                        load_matrix<N>(qa, qx + g * V::QX_STRIDE);
+                        load_matrix<N>(qa, qxg);
                         set_zero_rows<N, R>(d);
 #pragma unroll
                         for (int ii = 0; ii < N; ++ii) {
                             float pc[R];
 #pragma unroll
-                            for (int r = 0; r < R; ++r) pc[r] = src[ii * N + li * R + r];
+                            for (int r = 0; r < R; ++r) pc[r] = pxg[ii * N + li * R + r];
 #pragma unroll
                             for (int r = 0; r < R; ++r)
 #pragma unroll
                                 for (int j = 0; j < N; ++j) d[r][j] = fmaf(pc[r], qa[ii * N + j], d[r][j]);
                         }
-                    };
-                    if (tseq > 0) {
-                        times_prev(lds + 2 * V::G * V::CH_STRIDE + g * V::CH_STRIDE + tau * V::NN);
-                    } else if (cy.carry) {
-                        times_prev(cy.carry + (s0 / T) * V::NN);  // P_0 = carried-in state
                     } else {
+                        // P_0 = I
 #pragma unroll
                         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -636,11 +734,12 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                             for (int j = 0; j < N; ++j) dc[r][j] = q[r][j];
                         const float* m1 = M + s0 * V::NN;
                         if constexpr (FX) {
-                            float ev[N];
+                            float x[V::NN];
+                            load_matrix<N>(x, m1);
                             const float mean = ldu_mean<N>(m1);
 #pragma unroll
-                            for (int kk = 0; kk < N; ++kk) ev[kk] = expf(m1[kk * N + kk] - mean);
-                            rows_times_ldu_t<N, R>(dc, m1, ev);
+                            for (int kk = 0; kk < N; ++kk) x[kk * (N + 1)] = expf(x[kk * (N + 1)] - mean);
+                            rows_times_ldu_t<N, R>(dc, x);
                         } else {
                             float mm[V::NN];
                             load_matrix<N>(mm, m1);
@@ -650,6 +749,13 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                     }
                 }
             }
+        }
+        // the block's last slot (e on its diagonal) is M_{t+1} of the next
+        // block's first token
+        {
+            float t[R][N];
+            load_rows<N, R>(t, xl + (TB - 1) * V::NN + li * R * N);
+            store_rows<N, R>(nxg + li * R * N, t);
         }
     }
 }
@@ -663,9 +769,9 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
                                                       int64_t Z, unsigned char* __restrict__ ws,
                                                       ScanCarry cy) {
     using V = Valu<N, R, TB>;
-    __shared__ __align__(16) float lds[3 * V::G * V::CH_STRIDE];
-    __shared__ __align__(16) float se[FX ? V::G * V::SE_STRIDE : 4];
-    __shared__ __align__(16) float qx[V::G * V::QX_STRIDE];
+    __shared__ __align__(16) float lds[2 * V::G * V::CH_STRIDE];
+    __shared__ __align__(16) float nx[V::G * V::NX_STRIDE];
+    __shared__ __align__(16) float qx[2 * V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
     const int g = lane / V::LPC;
@@ -686,7 +792,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     set_zero_rows<N, R>(q);
     set_identity_rows<N, R>(w, li * R);
     if (!multi) {
-        bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T, cy);
+        bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
         return;
     }
 
@@ -704,7 +810,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     const bool later_super = r >= Z;
 
     // 1. affine aggregate of the chunk
-    bwd_sweep<N, R, TB, false, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T, cy);
+    bwd_sweep<N, R, TB, false, FX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
     ws_store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
     ws_store_rows<N, R>(swt + c * V::NN + li * R * N, w);
     fence_release();
@@ -760,7 +866,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from the carry and write dM
-    bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, se, qx, info, g, li, maxlen, T, cy);
+    bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
 }
 
 template <int N, int R, int TB, bool FX, bool SC>

@@ -19,12 +19,15 @@ def test_more_than_one_gpu_is_refused():
 def test_algorithmic_bytes_per_kernel():
     import bench
     S, T, n = 8192, 256, 8
-    per_entry = {"fwd_x": 8, "bwd_x": 16, "build": 8, "fwd": 8, "bwd": 16, "build_bwd": 12}
+    # n <= 8 backward: x (or M), dP, dM per token plus one stored prefix per 4 tokens
+    per_entry = {"fwd_x": 8, "bwd_x": 13, "build": 8, "fwd": 8, "bwd": 13, "build_bwd": 12}
     for kind, b in per_entry.items():
         assert bench.algorithmic_bytes(kind, S, T, n) == b * n * n * S * T
-    # one C2L forward launch moves exactly 1 GiB, the backward 2 GiB
+    # one C2L forward launch moves exactly 1 GiB, the backward 1.625 GiB
     assert bench.algorithmic_bytes("fwd_x", S, T, n) == 2 ** 30
-    assert bench.algorithmic_bytes("bwd_x", S, T, n) == 2 ** 31
+    assert bench.algorithmic_bytes("bwd_x", S, T, n) == 13 * 2 ** 27
+    # the matrix-core backward (n = 16, 32) reads every prefix
+    assert bench.algorithmic_bytes("bwd", 64, 1024, 16) == 16 * 256 * 64 * 1024
 
 
 def test_traffic_record_is_tied_to_the_sources():
