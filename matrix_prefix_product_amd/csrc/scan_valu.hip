@@ -15,6 +15,8 @@
 // dM_t = P_{t-1}^T Q_t needs all rows of Q_t and of P_{t-1}, exchanged through
 // LDS.  The backward reads one stored prefix per TB tokens and recomputes the
 // others from it (VALU work is cheap here, HBM bytes are not).
+#include <type_traits>
+
 #include "mru_build.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
@@ -200,9 +202,10 @@ __device__ inline void ws_load_matrix(float (&m)[N * N], const float* src) {
 
 // Staging of one block of TB tokens for every chain of the wave.  Token slot
 // tau of chain ch holds global token  base + pos(tau) + shift, where
-// pos(tau) = blk + tau going forward and len-1-(blk+tau) going backward; it is
-// loaded only when that token lies inside the chunk (pos < len, pos >= 0) and
-// inside the sequence (0 <= t0 + pos + shift < T); other slots are zero.
+// pos(tau) = blk + tau going forward and len-1-(blk+tau) going backward, when
+// that token lies inside the chunk (pos < len, pos >= 0) and inside the
+// sequence (0 <= t0 + pos + shift < T).  Other slots hold the array's first
+// token; the sweeps read them only into results they discard.
 template <int N, int R, int TB, bool REV>
 __device__ inline void stage_load(float4* reg, const float* src,
                                   const ChainInfo* info, int blk, int shift, int64_t T) {
@@ -218,10 +221,14 @@ __device__ inline void stage_load(float4* reg, const float* src,
         const ChainInfo ci = info[ch];
         const int pos = REV ? ci.len - 1 - (blk + tau) : blk + tau;
         const int64_t tseq = int64_t(ci.t0) + pos + shift;
-        const bool ok = pos >= 0 && pos < ci.len && tseq >= 0 && tseq < T;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ok) v = reinterpret_cast<const float4*>(src + (ci.base + pos + shift) * V::NN)[q];
-        reg[i] = v;
+        const bool ok = (pos >= 0) & (pos < ci.len) & (tseq >= 0) & (tseq < T);
+        // The load is unconditional (slots outside take token 0) and its value is
+        // not touched until it is staged: a branch around the load, or a select on
+        // its value, would make the compiler wait for it right here instead of
+        // one block later.
+        const int64_t tok = ok ? ci.base + pos + shift : 0;
+        const float4 v = reinterpret_cast<const float4*>(src + tok * V::NN)[q];
+        reg[i] = make_float4(v.x, v.y, v.z, v.w);
     }
 }
 
@@ -393,12 +400,16 @@ __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ 
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
     float4 reg[V::LD];
-    if (maxlen > 0) stage_load<N, R, TB, false>(reg, M, info, 0, 0, T);
-    for (int blk = 0; blk < maxlen; blk += TB) {
+    // One block.  FULL: every chain of the wave has all TB tokens of this block
+    // and of the next, so the body has no data-dependent branches and the next
+    // block is prefetched unconditionally; the compiler then waits for the
+    // staged loads without waiting for the previous block's stores.
+    auto block = [&](int blk, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         __syncthreads();
         stage_store<N, R, TB>(lds, reg);
         __syncthreads();
-        if (blk + TB < maxlen) stage_load<N, R, TB, false>(reg, M, info, blk + TB, 0, T);
+        if (FULL || blk + TB < maxlen) stage_load<N, R, TB, false>(reg, M, info, blk + TB, 0, T);
         if constexpr (FX) {
             stage_e<N, R, TB>(lds);
             __syncthreads();
@@ -406,7 +417,7 @@ __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ 
 #pragma unroll
         for (int tau = 0; tau < TB; ++tau) {
             const int pos = blk + tau;
-            if (pos < me.len) {
+            if (FULL || pos < me.len) {
                 const float* slot = lds + g * V::CH_STRIDE + tau * V::NN;
                 if constexpr (FX) {
                     rows_times_ldu<N, R>(st, slot);
@@ -418,11 +429,25 @@ __device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ 
                 if constexpr (SC) renorm_rows<N, R>(st, ex);
                 if (WRITE) {
                     store_rows<N, R>(P + (me.base + pos) * V::NN + li * R * N, st);
-                    if (SC && li == 0) pexp[me.base + pos] = ex;
+                    if (SC) pexp[me.base + pos] = ex;  // the same value from every lane of the chain
                 }
             }
         }
+    };
+    int minlen = maxlen;
+#pragma unroll
+    for (int c = 0; c < V::G; ++c) minlen = min(minlen, info[c].len);
+    const std::integral_constant<bool, true> full;
+    const std::integral_constant<bool, false> partial;
+    if (maxlen > 0) stage_load<N, R, TB, false>(reg, M, info, 0, 0, T);
+    int blk = 0;
+    if (blk + 2 * TB <= minlen) {
+        // the first full block is peeled, so that the loop is entered only from
+        // a full block (the same memory operations in flight on every entry)
+        block(blk, full);
+        for (blk += TB; blk + 2 * TB <= minlen; blk += TB) block(blk, full);
     }
+    for (; blk < maxlen; blk += TB) block(blk, partial);
 }
 
 template <int N, int R, int TB, bool FX, bool SC>
@@ -571,6 +596,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
     const int64_t s0 = me.base - me.t0;  // token index of the sequence's first token
+    const int64_t seq = s0 / T;          // its sequence
     float* const xl = lds + g * V::CH_STRIDE;                          // staged M_t
     float* const rl = lds + V::G * V::CH_STRIDE + g * V::CH_STRIDE;    // staged dP_t
     float* const nxg = nx + g * V::NX_STRIDE;                          // M_{t+1}
@@ -587,7 +613,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
         const float* src = P;  // idle chains (a padding chunk may lie past the array)
         if (me.len > 0) {
             if (tc >= 0) src = P + (me.base + lo - 1) * V::NN;
-            else if (cy.carry) src = cy.carry + (s0 / T) * V::NN;
+            else if (cy.carry) src = cy.carry + seq * V::NN;
         }
         ck_id = tc < 0 && !cy.carry;
         load_rows<N, R>(ck, src + li * R * N);
@@ -617,8 +643,13 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
             for (int r = 0; r < R; ++r) nxg[(li * R + r) * (N + 1)] = e[r];
         }
     }
-    if (maxlen > 0) load_block(0);
-    for (int blk = 0; blk < maxlen; blk += TB) {
+    // One block.  FULL: every chain of the wave has all TB tokens and none is
+    // its sequence's first, so the body has no data-dependent branches and the
+    // next block is prefetched unconditionally; the compiler then knows how many
+    // memory operations follow each load and waits for the staged loads
+    // without waiting for the previous block's dM stores.
+    auto block = [&](int blk, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         __syncthreads();
         stage_store<N, R, TB>(lds, rm);
         stage_store<N, R, TB>(lds + V::G * V::CH_STRIDE, rr);
@@ -633,7 +664,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                     for (int j = 0; j < N; ++j) cur[r][j] = ck[r][j];
         }
         __syncthreads();
-        if (blk + TB < maxlen) load_block(blk + TB);
+        if (FULL || blk + TB < maxlen) load_block(blk + TB);
         if constexpr (FX) {
             stage_e<N, R, TB>(lds);
             __syncthreads();
@@ -659,7 +690,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                         load_matrix<N>(m, slot);
                         rows_times<N, R>(rp[tau], m);
                     }
-                    if (tau >= hi)
+                    if (!FULL && tau >= hi)
 #pragma unroll
                         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -671,11 +702,11 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
         for (int tau = 0; tau < TB; ++tau) {
             const int i = blk + tau;
             const int pos = me.len - 1 - i;
-            const bool live = i < me.len;
+            const bool live = FULL || i < me.len;
             const int64_t tseq = int64_t(me.t0) + pos;
             const float* mslot = tau == 0 ? nxg : xl + (tau - 1) * V::NN;
             if (live) {
-                if (tseq + 1 < T) {
+                if (FULL || tseq + 1 < T) {
                     if constexpr (FX) {
                         float x[V::NN];
                         load_matrix<N>(x, mslot);
@@ -687,8 +718,14 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                         rows_times_t<N, R>(q, m);
                         if (!GRAD) rows_times_t<N, R>(w, m);
                     }
-                } else {
-                    set_zero_rows<N, R>(q);
+                }
+                if (FULL || tseq + 1 >= T) {
+                    // the sequence's last token has no M_{t+1} (a select, not a branch)
+                    const bool last = tseq + 1 >= T;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int j = 0; j < N; ++j) q[r][j] = last ? 0.f : q[r][j];
                 }
                 add_rows<N, R>(q, rl + tau * V::NN + li * R * N);
             }
@@ -703,7 +740,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                 __syncthreads();
                 if (live) {
                     float d[R][N];
-                    if (tseq > 0 || cy.carry) {
+                    if (FULL || tseq > 0 || cy.carry) {
                         float qa[V::NN];
                         load_matrix<N>(qa, qxg);
                         set_zero_rows<N, R>(d);
@@ -725,7 +762,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                             for (int j = 0; j < N; ++j) d[r][j] = q[r][j];
                     }
                     store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
-                    if (tseq == 0 && cy.dcarry) {
+                    if (!FULL && tseq == 0 && cy.dcarry) {
                         // dL/dP_0 = Q_1 M_1^T, M_1 this token's input
                         float dc[R][N];
 #pragma unroll
@@ -745,7 +782,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                             load_matrix<N>(mm, m1);
                             rows_times_t<N, R>(dc, mm);
                         }
-                        store_rows<N, R>(cy.dcarry + (s0 / T) * V::NN + li * R * N, dc);
+                        store_rows<N, R>(cy.dcarry + seq * V::NN + li * R * N, dc);
                     }
                 }
             }
@@ -757,7 +794,23 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
             load_rows<N, R>(t, xl + (TB - 1) * V::NN + li * R * N);
             store_rows<N, R>(nxg + li * R * N, t);
         }
+    };
+    int minlen = maxlen;
+#pragma unroll
+    for (int c = 0; c < V::G; ++c) minlen = min(minlen, info[c].len);
+    const std::integral_constant<bool, true> full;
+    const std::integral_constant<bool, false> partial;
+    if (maxlen > 0) load_block(0);
+    int blk = 0;
+    // full blocks end one token short of the shortest chain: the first token of
+    // a sequence is handled by the partial body
+    if (blk + TB < minlen) {
+        // the first full block is peeled, so that the loop is entered only from
+        // a full block (the same memory operations in flight on every entry)
+        block(blk, full);
+        for (blk += TB; blk + TB < minlen; blk += TB) block(blk, full);
     }
+    for (; blk < maxlen; blk += TB) block(blk, partial);
 }
 
 template <int N, int R, int TB, bool FX>
