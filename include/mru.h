@@ -274,6 +274,33 @@ mru_status mru_scan_bwd_ex(const float* in, int32_t from_x, const float* carry, 
                            int64_t T, int32_t n, int32_t chunk, void* ws, size_t ws_bytes,
                            void* stream);
 
+/*
+ * Gradient of the whole layer with respect to the raw token vectors, in one
+ * pass: dx = dL/dx_t for L = sum_t <dP_t, P_t>, P_t = P_0 M_1 ... M_t with M_t
+ * built from x_t by mru_build_inputs (LDU fill and determinant-correcting
+ * scalar, "Improving Matrix Recurrent Units as an Attention Alternative", Key
+ * Points).  The same result as mru_scan_bwd_ex (from_x = 1) followed by
+ * mru_build_inputs_bwd on its dM, up to rounding, without writing dM or reading
+ * x a second time: per token it reads x, dP and one stored prefix in four and
+ * writes dx.  With G = dL/dM_t, H = G U^T and g_k = (L^T G U^T)_kk:
+ *   dX_ij = e_j H_ij (i > j),  e_i (L^T G)_ij (i < j),  e_i g_i - mean_k e_k g_k (i = j),
+ * where (L^T G) is formed from the rows of P_{t-1} L_t, as G from those of P_{t-1}.
+ *
+ * x       [B][H][T][n*n] fp32, read (the forward's inputs).
+ * carry   [B][H][n][n] fp32 (P_0) or NULL for I; 16-byte aligned.
+ * P, dP   [B][H][T][n][n] fp32, read: the forward's outputs on x (mru_scan_fwd_x
+ *         or mru_scan_fwd_ex) and dL/dP.  One prefix in four is read, as for
+ *         mru_scan_bwd.
+ * dx      [B][H][T][n*n] fp32, written.
+ * dcarry  [B][H][n][n] fp32, written (dL/dP_0), or NULL.
+ * chunk, ws, ws_bytes as for mru_scan_bwd.  n in {4, 8}; other n return
+ * MRU_ERR_SHAPE.  Errors as mru_scan_bwd_ex; dx must not overlap any input,
+ * dcarry or ws.  B*H*T = 0 writes nothing.
+ */
+mru_status mru_scan_bwd_dx(const float* x, const float* carry, const float* P, const float* dP,
+                           float* dx, float* dcarry, int64_t B, int64_t H, int64_t T, int32_t n,
+                           int32_t chunk, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

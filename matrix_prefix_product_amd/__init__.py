@@ -25,6 +25,7 @@ import torch
 
 __all__ = [
     "build_inputs", "build_inputs_bwd", "scan_fwd", "mru_layer", "MRUBuild", "scan_bwd", "flatten", "mru_scan", "MRUScan",
+    "scan_fwd_x", "scan_bwd_x", "scan_fwd_ex", "scan_bwd_ex", "scan_bwd_dx", "build_orthogonal",
     "scan_plan", "scan_chunk", "workspace_bytes", "library_path", "load_library",
     "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N",
 ]
@@ -95,6 +96,8 @@ def load_library():
     lib.mru_scan_fwd_ex.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.mru_scan_bwd_ex.restype = i32
     lib.mru_scan_bwd_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_bwd_dx.restype = i32
+    lib.mru_scan_bwd_dx.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     _LIB = lib
     return lib
 
@@ -397,6 +400,38 @@ def scan_bwd_ex(inp: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
     return (dM, dC) if want_dcarry else dM
 
 
+def scan_bwd_dx(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
+                carry: torch.Tensor | None = None, want_dcarry: bool = False, chunk: int = 0,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """dL/dx of sum_t <dP_t, P_t> for P_t = P_0 M_1 ... M_t with M_t built from
+    x_t (build_inputs), in one pass: build_inputs_bwd(x, scan_bwd_x(x, P, dP))
+    without forming dL/dM.  P is the forward's output on x (scan_fwd_x or
+    scan_fwd_ex with the same carry).  With want_dcarry also dL/dP_0."""
+    _require(P, "P", 5)
+    n = P.shape[-1]
+    B, H, T = _xshape(x, n)
+    dev = x.device
+    for name, t in (("P", P), ("dP", dP)):
+        _require(t, name, 5)
+        if tuple(t.shape) != (B, H, T, n, n) or t.device != dev:
+            raise ValueError(f"{name} must be [B,H,T,n,n] on x's device")
+    carry = _carry_arg(carry, B, H, n, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _require(out, "out", 4)
+        if out.shape != x.shape or out.device != dev:
+            raise ValueError("out must match x")
+    dC = torch.zeros((B, H, n, n), dtype=torch.float32, device=dev) if want_dcarry else None
+    ws, ws_bytes = _workspace((B, H, T), n, DIR_BWD, chunk, dev, workspace)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.mru_scan_bwd_dx(_ptr(x), _ptr(carry), _ptr(P), _ptr(dP), _ptr(out), _ptr(dC),
+                                 B, H, T, n, chunk, _ptr(ws), ws_bytes, _stream_handle(dev))
+    _check(st, "mru_scan_bwd_dx")
+    return (out, dC) if want_dcarry else out
+
+
 def flatten(P: torch.Tensor) -> torch.Tensor:
     """Row-major flatten of each output state matrix: [B,H,T,n,n] -> [B,H,T,n*n] view."""
     return P.view(*P.shape[:-2], P.shape[-2] * P.shape[-1])
@@ -439,8 +474,8 @@ class MRUBuild(torch.autograd.Function):
 
 
 class MRULayerFused(torch.autograd.Function):
-    """P = scan_fwd_x(x, n); backward rebuilds M on chip (scan_bwd_x), then
-    build_inputs_bwd.  The input matrices are never stored."""
+    """P = scan_fwd_x(x, n); the backward goes from dL/dP to dL/dx in one pass
+    (scan_bwd_dx).  Neither the input matrices nor dL/dM are ever stored."""
 
     @staticmethod
     def forward(ctx, x: torch.Tensor, n: int, chunk: int = 0):
@@ -453,8 +488,7 @@ class MRULayerFused(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dP: torch.Tensor):
         x, P = ctx.saved_tensors
-        dM = scan_bwd_x(x, P, dP.contiguous(), ctx.chunk)
-        return build_inputs_bwd(x, dM), None, None
+        return scan_bwd_dx(x, P, dP.contiguous(), chunk=ctx.chunk), None, None
 
 
 def mru_layer(x: torch.Tensor, n: int, chunk: int = 0) -> torch.Tensor:

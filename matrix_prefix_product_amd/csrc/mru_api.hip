@@ -274,10 +274,11 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
 
 mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float* dM, int64_t B,
                          int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
-                         size_t ws_bytes, void* stream, bool from_x, const ScanCarry& cy) {
+                         size_t ws_bytes, void* stream, bool from_x, const ScanCarry& cy,
+                         bool to_dx = false) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
-    if (from_x && n > 8) return MRU_ERR_SHAPE;
+    if ((from_x || to_dx) && n > 8) return MRU_ERR_SHAPE;
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P || !dP || !dM) return MRU_ERR_NULL;
@@ -311,7 +312,8 @@ mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float*
         if (st != MRU_OK) return st;
     }
     if (n <= 8)
-        return launched(launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
+        return launched(
+            launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, to_dx, cy));
     return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, cy));
 }
 
@@ -360,6 +362,15 @@ mru_status mru_scan_bwd_ex(const float* in, int32_t from_x, const float* carry, 
     cy.carry = carry;
     cy.dcarry = dcarry;
     return scan_bwd_impl(in, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, from_x != 0, cy);
+}
+
+mru_status mru_scan_bwd_dx(const float* x, const float* carry, const float* P, const float* dP,
+                           float* dx, float* dcarry, int64_t B, int64_t H, int64_t T, int32_t n,
+                           int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+    ScanCarry cy;
+    cy.carry = carry;
+    cy.dcarry = dcarry;
+    return scan_bwd_impl(x, P, dP, dx, B, H, T, n, chunk, ws, ws_bytes, stream, true, cy, true);
 }
 
 }  // extern "C"

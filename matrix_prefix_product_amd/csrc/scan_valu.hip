@@ -94,6 +94,18 @@ __device__ inline void load_matrix(float (&m)[N * N], const float* src) {
     }
 }
 
+template <int N>
+__device__ inline void load_vec_lds(float (&v)[N], const float* src) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        const float4 t = reinterpret_cast<const float4*>(src)[q];
+        v[4 * q] = t.x;
+        v[4 * q + 1] = t.y;
+        v[4 * q + 2] = t.z;
+        v[4 * q + 3] = t.w;
+    }
+}
+
 // st <- st * m   (m row-major n-by-n in registers)
 template <int N, int R>
 __device__ inline void rows_times(float (&st)[R][N], const float (&m)[N * N]) {
@@ -290,17 +302,25 @@ __device__ inline void stage_e(float* lds) {
     }
 }
 
-// st <- st * (L diag(e) U), in place per row; x holds L below, e on and U
-// above the diagonal.
+// st <- st * L, in place per row (L the unit lower factor held below x's
+// diagonal): r_j += sum_{i > j} r_i X_ij, ascending j reads only untouched r_i.
 template <int N, int R>
-__device__ inline void rows_times_ldu(float (&st)[R][N], const float (&x)[N * N]) {
+__device__ inline void rows_times_l(float (&st)[R][N], const float (&x)[N * N]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        // times L: r_j += sum_{i > j} r_i X_ij, ascending j reads only untouched r_i
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < N; ++j)
 #pragma unroll
             for (int i = j + 1; i < N; ++i) st[r][j] = fmaf(st[r][i], x[i * N + j], st[r][j]);
+}
+
+// st <- st * (L diag(e) U), in place per row; x holds L below, e on and U
+// above the diagonal.
+template <int N, int R>
+__device__ inline void rows_times_ldu(float (&st)[R][N], const float (&x)[N * N]) {
+    rows_times_l<N, R>(st, x);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int j = 0; j < N; ++j) st[r][j] *= x[j * N + j];
         // times U: r_j += sum_{k < j} r_k X_kj, descending j reads only untouched r_k
@@ -394,7 +414,7 @@ __device__ inline void init_rows(float (&st)[R][N], int& ex, const ScanCarry& cy
 // step multiplies by M_t's factors (stage_e puts each staged token's e on its
 // diagonal).
 template <int N, int R, int TB, bool WRITE, bool FX, bool SC>
-__device__ void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ M,
+__device__ __attribute__((always_inline)) void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ M,
                           float* __restrict__ P, int32_t* __restrict__ pexp, float* lds,
                           const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
     using V = Valu<N, R, TB>;
@@ -571,6 +591,64 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------- backward
 
+// Sum over aligned groups of W (1, 2, 4 or 8) lanes with DPP moves: swap
+// neighbours, swap pairs, then mirror the halves of each 8-lane group.  Every
+// lane of a group gets the same value (each step adds two values in either
+// order, and a + b == b + a).
+template <int W>
+__device__ inline float group_sum(float v) {
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8, "groups of at most 8 lanes");
+    if constexpr (W >= 2)  // quad_perm [1, 0, 3, 2]
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if constexpr (W >= 4)  // quad_perm [2, 3, 0, 1]
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    if constexpr (W >= 8)  // row_half_mirror
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+// The lane's rows a = a0 .. a0+R-1 of dL/dX_t, the gradient through the LDU
+// build of M_t ("Improving Matrix Recurrent Units as an Attention
+// Alternative", Key Points: LDU fill, determinant-correcting scalar), from its
+// rows of G = dL/dM_t (d) and of L^T G (u).  x holds the token's factors (L
+// below, e on and U above the diagonal); xa points at row a0 of the same
+// matrix in LDS.  With H = G U^T and g_k = (L^T G U^T)_kk:
+//   dX_aj = e_j H_aj (j < a),  e_a (L^T G)_aj (j > a),  e_a g_a - mean_k e_k g_k (j = a);
+// the mean's derivative is the determinant correction's.  W = lanes per chain.
+template <int N, int R, int W>
+__device__ inline void dx_rows(float (&out)[R][N], const float (&d)[R][N], const float (&u)[R][N],
+                               const float (&x)[N * N], const float* xa, int a0) {
+    float seg[R], part = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int a = a0 + r;
+        float xr[N];
+        load_vec_lds<N>(xr, xa + r * N);  // row a of x: U_aj above, e_a on the diagonal
+        float ea = 0.f, g = 0.f;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            ea = j == a ? xr[j] : ea;
+            const float uj = j > a ? xr[j] : (j == a ? 1.f : 0.f);  // U_aj
+            g = fmaf(uj, u[r][j], g);
+        }
+        seg[r] = ea * g;
+        part += seg[r];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            // H_aj = G_aj + sum_{m > j} G_am U_jm
+            float h = d[r][j];
+#pragma unroll
+            for (int m = j + 1; m < N; ++m) h = fmaf(d[r][m], x[j * N + m], h);
+            out[r][j] = j < a ? x[j * N + j] * h : ea * u[r][j];
+        }
+    }
+    const float mean = group_sum<W>(part) * (1.0f / N);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < N; ++j) out[r][j] = j == a0 + r ? seg[r] - mean : out[r][j];
+}
+
 // One reverse sweep over the chunk, from its last token down, TB tokens per
 // staged block.  A block stages M_t (x_t) and dP_t of its own tokens; M_{t+1}
 // of a token is the slot staged before it, and for the block's first token the
@@ -587,8 +665,8 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
 //             bit for bit the stored prefixes when P came from the matching
 //             forward scan).  This reads n^2 floats per block instead of per token.
 // At the last token of a sequence there is no M_{t+1}: q <- dP_t.
-template <int N, int R, int TB, bool GRAD, bool FX>
-__device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
+template <int N, int R, int TB, bool GRAD, bool FX, bool DX>
+__device__ __attribute__((always_inline)) void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
                           const float* __restrict__ P, const float* __restrict__ dP,
                           float* __restrict__ dM, float* lds, float* nx, float* qx,
                           const ChainInfo* info, int g, int li, int maxlen, int64_t T,
@@ -602,6 +680,7 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
     float* const nxg = nx + g * V::NX_STRIDE;                          // M_{t+1}
     float* const qxg = qx + g * V::QX_STRIDE;                          // Q_t rows
     float* const pxg = qx + (V::G + g) * V::QX_STRIDE;                 // P_{t-1} rows
+    float* const lxg = qx + (2 * V::G + g) * V::QX_STRIDE;             // DX: P_{t-1} L_t rows
     float4 rm[V::LD], rr[V::LD];
     float ck[R][N];  // rows of P just before the lowest token of the next block
     bool ck_id = false;
@@ -730,29 +809,52 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
                 add_rows<N, R>(q, rl + tau * V::NN + li * R * N);
             }
             if constexpr (GRAD) {
+                // DX: the rows of P_{t-1} L_t (L_t the unit lower factor of M_t)
+                // as well; (L^T G)[a][:] = sum_i (P_{t-1} L_t)[i][a] Q_t[i][:]
+                // comes from them as G's rows come from P_{t-1}'s.
+                float pl[DX ? R : 1][N];
+                float xt[DX ? V::NN : 1];  // DX: M_t's factors (its lower part dies here)
+                if constexpr (DX) {
+                    if (live) {
+                        load_matrix<N>(xt, xl + tau * V::NN);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int j = 0; j < N; ++j) pl[r][j] = rp[tau][r][j];
+                        rows_times_l<N, R>(pl, xt);
+                    }
+                }
                 // exchange the rows of Q_t and P_{t-1} within the chain, then
                 // dM rows a = own rows: dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
                 __syncthreads();
                 if (live) {
                     store_rows<N, R>(qxg + li * R * N, q);
                     store_rows<N, R>(pxg + li * R * N, rp[tau]);
+                    if constexpr (DX) store_rows<N, R>(lxg + li * R * N, pl);
                 }
                 __syncthreads();
                 if (live) {
-                    float d[R][N];
-                    if (FULL || tseq > 0 || cy.carry) {
+                    float d[R][N], u[DX ? R : 1][N];
+                    if (DX || FULL || tseq > 0 || cy.carry) {
                         float qa[V::NN];
                         load_matrix<N>(qa, qxg);
                         set_zero_rows<N, R>(d);
+                        if constexpr (DX) set_zero_rows<N, R>(u);
 #pragma unroll
                         for (int ii = 0; ii < N; ++ii) {
-                            float pc[R];
+                            float pc[R], lc[R];
 #pragma unroll
                             for (int r = 0; r < R; ++r) pc[r] = pxg[ii * N + li * R + r];
+                            if constexpr (DX)
+#pragma unroll
+                                for (int r = 0; r < R; ++r) lc[r] = lxg[ii * N + li * R + r];
 #pragma unroll
                             for (int r = 0; r < R; ++r)
 #pragma unroll
-                                for (int j = 0; j < N; ++j) d[r][j] = fmaf(pc[r], qa[ii * N + j], d[r][j]);
+                                for (int j = 0; j < N; ++j) {
+                                    d[r][j] = fmaf(pc[r], qa[ii * N + j], d[r][j]);
+                                    if constexpr (DX) u[r][j] = fmaf(lc[r], qa[ii * N + j], u[r][j]);
+                                }
                         }
                     } else {
                         // P_0 = I
@@ -761,7 +863,13 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
 #pragma unroll
                             for (int j = 0; j < N; ++j) d[r][j] = q[r][j];
                     }
-                    store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
+                    if constexpr (DX) {
+                        float o[R][N];
+                        dx_rows<N, R, V::LPC>(o, d, u, xt, xl + tau * V::NN + li * R * N, li * R);
+                        store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, o);
+                    } else {
+                        store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
+                    }
                     if (!FULL && tseq == 0 && cy.dcarry) {
                         // dL/dP_0 = Q_1 M_1^T, M_1 this token's input
                         float dc[R][N];
@@ -813,8 +921,10 @@ __device__ void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __res
     for (; blk < maxlen; blk += TB) block(blk, partial);
 }
 
-template <int N, int R, int TB, bool FX>
-__global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ M,
+// DX runs alone on its SIMD at the shapes it is for (one chain per sequence),
+// so it may use the whole register file (AGPRs included) instead of spilling.
+template <int N, int R, int TB, bool FX, bool DX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, DX ? 1 : 2))) void bwd_valu_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ P,
                                                       const float* __restrict__ dP,
                                                       float* __restrict__ dM, int64_t S,
@@ -824,7 +934,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     using V = Valu<N, R, TB>;
     __shared__ __align__(16) float lds[2 * V::G * V::CH_STRIDE];
     __shared__ __align__(16) float nx[V::G * V::NX_STRIDE];
-    __shared__ __align__(16) float qx[2 * V::G * V::QX_STRIDE];
+    __shared__ __align__(16) float qx[(DX ? 3 : 2) * V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
     const int lane = threadIdx.x;
     const int g = lane / V::LPC;
@@ -845,7 +955,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     set_zero_rows<N, R>(q);
     set_identity_rows<N, R>(w, li * R);
     if (!multi) {
-        bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
+        bwd_sweep<N, R, TB, true, FX, DX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
         return;
     }
 
@@ -863,7 +973,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     const bool later_super = r >= Z;
 
     // 1. affine aggregate of the chunk
-    bwd_sweep<N, R, TB, false, FX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
+    bwd_sweep<N, R, TB, false, FX, DX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
     ws_store_rows<N, R>(sbl + c * V::NN + li * R * N, q);
     ws_store_rows<N, R>(swt + c * V::NN + li * R * N, w);
     fence_release();
@@ -919,7 +1029,7 @@ __global__ __launch_bounds__(64) void bwd_valu_kernel(const float* __restrict__ 
     if (boundary && li == 0) store_flag(&flags[c], kFlagPrefix);
 
     // 4. re-run the chunk from the carry and write dM
-    bwd_sweep<N, R, TB, true, FX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
+    bwd_sweep<N, R, TB, true, FX, DX>(q, w, M, P, dP, dM, lds, nx, qx, info, g, li, maxlen, T, cy);
 }
 
 template <int N, int R, int TB, bool FX, bool SC>
@@ -939,14 +1049,14 @@ hipError_t run_fwd_any(const float* M, float* P, int64_t S, int64_t T, int64_t K
     return run_fwd<N, R, TB, FX, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
 }
 
-template <int N, int R, int TB, bool FX>
+template <int N, int R, int TB, bool FX, bool DX>
 hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                    int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream,
                    const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
     const int64_t waves = (S * nch + V::G - 1) / V::G;
-    hipLaunchKernelGGL((bwd_valu_kernel<N, R, TB, FX>), dim3(unsigned(waves)), dim3(64), 0, stream,
-                       M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
+    hipLaunchKernelGGL((bwd_valu_kernel<N, R, TB, FX, DX>), dim3(unsigned(waves)), dim3(64), 0,
+                       stream, M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
@@ -988,16 +1098,21 @@ hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n
 
 hipError_t launch_bwd_valu(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream, bool from_x, const ScanCarry& cy) {
+                           hipStream_t stream, bool from_x, bool to_dx, const ScanCarry& cy) {
+    if (to_dx && !from_x) return hipErrorInvalidValue;
     if (n == 4) {
+        if (to_dx)
+            return run_bwd<MRU_VALU_BWD_CFG4, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
         if (from_x)
-            return run_bwd<MRU_VALU_BWD_CFG4, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
-        return run_bwd<MRU_VALU_BWD_CFG4, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+            return run_bwd<MRU_VALU_BWD_CFG4, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        return run_bwd<MRU_VALU_BWD_CFG4, false, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 8) {
+        if (to_dx)
+            return run_bwd<MRU_VALU_BWD_CFG8, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
         if (from_x)
-            return run_bwd<MRU_VALU_BWD_CFG8, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
-        return run_bwd<MRU_VALU_BWD_CFG8, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+            return run_bwd<MRU_VALU_BWD_CFG8, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        return run_bwd<MRU_VALU_BWD_CFG8, false, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     }
     return hipErrorInvalidValue;
 }

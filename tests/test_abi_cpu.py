@@ -165,6 +165,24 @@ def test_extended_entries_validate_before_any_launch(mpp):
     assert lib.mru_scan_bwd_ex(a, 0, c, b, d, e, odd16, 1, 1, 8, 8, 1 << 20, nul, 0, nul) == 3
 
 
+def test_layer_backward_entry_validates_before_any_launch(mpp):
+    lib = mpp.load_library()
+    nul = ctypes.c_void_p(0)
+    x, C, P, R, dx, dC = (ctypes.c_void_p(v) for v in
+                          (0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000))
+    # arguments: x, carry, P, dP, dx, dcarry, B, H, T, n, chunk, ws, ws_bytes, stream
+    assert lib.mru_scan_bwd_dx(x, nul, P, R, dx, nul, 1, 1, 8, 16, 0, nul, 0, nul) == 2   # n = 16
+    assert lib.mru_scan_bwd_dx(x, nul, P, R, dx, nul, 1, 1, 8, 6, 0, nul, 0, nul) == 2    # bad n
+    assert lib.mru_scan_bwd_dx(nul, nul, nul, nul, nul, nul, 1, 1, 0, 8, 0, nul, 0, nul) == 0  # empty
+    assert lib.mru_scan_bwd_dx(x, nul, P, nul, dx, nul, 1, 1, 8, 8, 0, nul, 0, nul) == 1  # null dP
+    assert lib.mru_scan_bwd_dx(x, nul, P, R, x, nul, 1, 1, 8, 8, 0, nul, 0, nul) == 4     # dx over x
+    assert lib.mru_scan_bwd_dx(x, ctypes.c_void_p(0x200004), P, R, dx, nul, 1, 1, 8, 8, 0, nul, 0,
+                               nul) == 3                                                   # carry misaligned
+    assert lib.mru_scan_bwd_dx(x, C, P, R, dx, ctypes.c_void_p(0x500000 + 64), 1, 1, 8, 8, 0, nul, 0,
+                               nul) == 4                                                   # dcarry over dx
+    assert lib.mru_scan_bwd_dx(x, nul, P, R, dx, nul, 1, 1, 8, 8, -1, nul, 0, nul) == 6   # chunk
+
+
 def test_orthogonal_build_validates(mpp):
     lib = mpp.load_library()
     nul = ctypes.c_void_p(0)

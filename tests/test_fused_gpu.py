@@ -4,7 +4,8 @@ mru_scan_fwd_x / mru_scan_bwd_x multiply by the LDU factors of each input
 state matrix instead of forming it, so they agree with build-then-scan up to
 rounding order; both are graded against the fp64 oracle
 (scan_ref(build_ref(x)), bwd_ref(build_ref(x), R)) with the forward / backward
-tolerances, and must be deterministic run to run.
+tolerances, and must be deterministic run to run.  mru_scan_bwd_dx goes on to
+dL/dx in the same pass, graded against build_vjp_ref of the oracle's backward.
 """
 import numpy as np
 import pytest
@@ -105,6 +106,80 @@ def test_fused_edges(mpp, n):
     R = gen_R(3, 2, 1, n, seed=6)
     dM = host(mpp.scan_bwd_x(dev(x), dev(P), dev(R)))
     assert np.array_equal(dM, R)
+
+
+@pytest.mark.parametrize("n,B,H,T,chunk", CASES)
+def test_layer_bwd_dx(mpp, n, B, H, T, chunk):
+    # x, P, dL/dP -> dL/dx in one pass, against the oracle's build VJP of its
+    # backward scan; and against the two-kernel path (backward to dM, then the
+    # build's gradient), which it equals up to rounding order
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_BWD, chunk)
+    say(f"[layer bwd dx] n={n} B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    x = _x(B, H, T, n, seed=T + 5 * n)
+    R = gen_R(B, H, T, n, seed=T + 2)
+    xd, Rd = dev(x), dev(R)
+    P = mpp.scan_fwd_x(xd, n)
+    ws = torch.empty(max(plan[3], 256), dtype=torch.uint8, device="cuda")
+    dx = mpp.scan_bwd_dx(xd, P, Rd, chunk=chunk, workspace=ws)
+    again = mpp.scan_bwd_dx(xd, P, Rd, chunk=chunk)
+    assert torch.equal(dx.view(torch.int32), again.view(torch.int32)), "not deterministic"
+    ref = build_vjp_ref(x, bwd_ref(build_ref(x, n), R), n)
+    shape = (B, H, T, n, n)
+    err = rel_fro_err(host(dx).reshape(shape), ref.reshape(shape))
+    two = build_vjp_ref(x, host(mpp.scan_bwd_x(xd, P, Rd, chunk)), n)  # fp64 build VJP of the GPU dM
+    two_gpu = host(mpp.build_inputs_bwd(xd, mpp.scan_bwd_x(xd, P, Rd, chunk)))
+    d2 = rel_fro_err(host(dx).reshape(shape), two_gpu.reshape(shape))
+    say(f"  max {err.max():.3e} median {np.median(err):.3e}; vs two kernels max {d2.max():.3e}")
+    assert err.max() <= BWD_TOL
+    assert rel_fro_err(host(dx).reshape(shape), two.reshape(shape)).max() <= 1e-4
+    if plan[3] > 0:
+        assert int(host(ws[4:8].view(torch.int32))[0]) == 0, "a flag wait timed out"
+
+
+@pytest.mark.parametrize("n,chunk", [(4, 0), (8, 0), (8, 7), (4, 16)])
+def test_layer_bwd_dx_carry(mpp, n, chunk):
+    # a carried-in state and its gradient: dx against the oracle with C0, and
+    # dL/dP_0 bitwise as the backward to dM computes it
+    B, H, T = 2, 3, 150
+    say(f"[layer bwd dx carry] n={n} chunk={chunk}")
+    x = _x(B, H, T, n, seed=77 + n)
+    R = gen_R(B, H, T, n, seed=78)
+    C = gen_R(B, H, 1, n, seed=79)[:, :, 0] * 0.5 + np.eye(n, dtype=np.float32)
+    xd, Rd, Cd = dev(x), dev(R), dev(np.ascontiguousarray(C))
+    P = mpp.scan_fwd_ex(xd, carry=Cd, from_x=True, n=n)
+    dx, dC = mpp.scan_bwd_dx(xd, P, Rd, carry=Cd, want_dcarry=True, chunk=chunk)
+    dM_ref, dC_ref = bwd_ref(build_ref(x, n), R, C0=C, want_dC0=True)
+    ref = build_vjp_ref(x, dM_ref, n)
+    shape = (B, H, T, n, n)
+    err = rel_fro_err(host(dx).reshape(shape), ref.reshape(shape))
+    say(f"  dx max {err.max():.3e}")
+    assert err.max() <= BWD_TOL
+    assert rel_fro_err(host(dC), dC_ref).max() <= BWD_TOL
+    _, dC_m = mpp.scan_bwd_ex(xd, P, Rd, carry=Cd, want_dcarry=True, from_x=True, chunk=chunk)
+    assert torch.equal(dC.view(torch.int32), dC_m.view(torch.int32))
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_layer_bwd_dx_edges(mpp, n):
+    # empty sequences are no-ops; one token: P_1 = M_1, so dx = build VJP of dP_1
+    e = torch.zeros(2, 3, 0, n * n, device="cuda")
+    assert mpp.scan_bwd_dx(e, torch.zeros(2, 3, 0, n, n, device="cuda"),
+                           torch.zeros(2, 3, 0, n, n, device="cuda")).shape == e.shape
+    x = _x(3, 2, 1, n, seed=15)
+    R = gen_R(3, 2, 1, n, seed=16)
+    xd = dev(x)
+    dx = host(mpp.scan_bwd_dx(xd, mpp.scan_fwd_x(xd, n), dev(R)))
+    ref = build_vjp_ref(x, R, n)
+    assert rel_fro_err(dx.reshape(3, 2, 1, n, n), ref.reshape(3, 2, 1, n, n)).max() <= BWD_TOL
+    # x = 0: every M_t = I and every e = 1, so dx is the build VJP at 0 of the
+    # reverse cumulative sum of dL/dP
+    T = 64
+    z = torch.zeros(1, 2, T, n * n, device="cuda")
+    R = gen_R(1, 2, T, n, seed=17)
+    G = np.cumsum(R[:, :, ::-1].astype(np.float64), axis=2)[:, :, ::-1]
+    dx = host(mpp.scan_bwd_dx(z, mpp.scan_fwd_x(z, n), dev(R)))
+    ref = build_vjp_ref(np.zeros((1, 2, T, n * n)), G, n)
+    assert rel_fro_err(dx.reshape(1, 2, T, n, n), ref.reshape(1, 2, T, n, n)).max() <= BWD_TOL
 
 
 @pytest.mark.parametrize("n", [4, 8])
