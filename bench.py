@@ -17,7 +17,8 @@ never stored.  Prints ONE JSON line:
                 current kernel sources, else null
   kernels       the same figures for every kernel of the step
   unfused       the separate kernels (build x -> M, scan M -> P, backward from M,
-                and the build's own backward x, dM -> dx) timed alone
+                and the build's own backward x, dM -> dx) timed alone, and the
+                layer backward x, P, dL/dP -> dL/dx in one pass (bwd_dx)
   n16, n32      forward-scan throughput on the n=16 and n=32 workloads
   n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload
   small         the two small workloads (one 1024-token n=4 sequence; the 8x8x256
@@ -73,8 +74,10 @@ def algorithmic_bytes(kind: str, S: int, T: int, n: int) -> int:
     # writes M, forward reads M (or x) and writes P, build backward reads x and
     # dM and writes dx.  The backward reads M (or x) and dP and writes dM; for
     # n <= 8 it reads one stored prefix per 4 tokens (recomputing the others),
-    # 13 bytes in all, for n = 16, 32 every prefix, 16.
-    per = {"build": 8, "fwd": 8, "bwd": 16, "fwd_x": 8, "bwd_x": 16, "build_bwd": 12}[kind]
+    # 13 bytes in all, for n = 16, 32 every prefix, 16.  The layer backward
+    # (bwd_dx, n <= 8) reads x, dP and one prefix in four and writes dx: 13.
+    per = {"build": 8, "fwd": 8, "bwd": 16, "fwd_x": 8, "bwd_x": 16, "build_bwd": 12,
+           "bwd_dx": 13}[kind]
     if kind in ("bwd", "bwd_x") and n <= 8:
         per = 13
     return per * n * n * S * T
@@ -341,14 +344,17 @@ def small_configs(mpp, torch, WORKLOADS, gen_R, gen_x, reps: int = 50):
 
 def unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, workload, reps: int = 10):
     """The separate kernels on the same inputs: build x -> M, scan M -> P,
-    backward from M, and the build's backward (x, dM -> dx)."""
+    backward from M, the build's backward (x, dM -> dx), and the layer
+    backward that goes from x, P, dL/dP to dL/dx in one pass (bwd_dx)."""
     M = mpp.build_inputs(x, n)
     dx = torch.empty_like(x)
+    dx1 = torch.empty_like(x)
     calls = {
         "build": lambda: mpp.build_inputs(x, n, out=M),
         "fwd": lambda: mpp.scan_fwd(M, out=P, workspace=ws_f),
         "bwd": lambda: mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b),
         "build_bwd": lambda: mpp.build_inputs_bwd(x, dM, out=dx),
+        "bwd_dx": lambda: mpp.scan_bwd_dx(x, P, R, out=dx1, workspace=ws_b),
     }
     rec = {}
     for name, fn in calls.items():
@@ -362,7 +368,7 @@ def unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, workload, reps: int = 
         torch.cuda.synchronize()
         avg = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
         rec[name] = kernel_record(name, avg, S, T, n, workload)
-    del M, dx
+    del M, dx, dx1
     return rec
 
 
