@@ -182,6 +182,33 @@ def test_layer_bwd_dx_edges(mpp, n):
     assert rel_fro_err(dx.reshape(1, 2, T, n, n), ref.reshape(1, 2, T, n, n)).max() <= BWD_TOL
 
 
+@pytest.mark.parametrize("n,chunk", [(4, 0), (8, 0), (8, 12)])
+def test_bwd_reads_one_prefix_in_four(mpp, n, chunk):
+    # The n <= 8 backward reads the stored prefix before each block of 4 tokens
+    # (blocks counted from each chunk's end) and recomputes the rest: with every
+    # other prefix replaced by NaN the results are unchanged.  Chunk lengths are
+    # multiples of 4 here and T is a multiple of the chunk, so the read prefixes
+    # are those at t = T-5, T-9, ... (0-based), i.e. t % 4 == 3.
+    B, H, T = 2, 2, 96
+    x = _x(B, H, T, n, seed=91)
+    R = gen_R(B, H, T, n, seed=92)
+    xd, Rd = dev(x), dev(R)
+    P = mpp.scan_fwd_x(xd, n)
+    poisoned = P.clone()
+    keep = torch.zeros(T, dtype=torch.bool)
+    keep[3::4] = True
+    poisoned[:, :, ~keep] = float("nan")
+    for fn in (lambda PP: mpp.scan_bwd_x(xd, PP, Rd, chunk), lambda PP: mpp.scan_bwd_dx(xd, PP, Rd, chunk=chunk)):
+        a, b = fn(P), fn(poisoned)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    M = mpp.build_inputs(xd, n)
+    Pm = mpp.scan_fwd(M)
+    pm = Pm.clone()
+    pm[:, :, ~keep] = float("nan")
+    assert torch.equal(mpp.scan_bwd(M, Pm, Rd, chunk).view(torch.int32),
+                       mpp.scan_bwd(M, pm, Rd, chunk).view(torch.int32))
+
+
 @pytest.mark.parametrize("n", [4, 8])
 def test_fused_layer_autograd(mpp, n):
     # mru_layer takes the fused path for n = 4, 8: gradient down to x against the oracle
