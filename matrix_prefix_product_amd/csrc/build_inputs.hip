@@ -9,6 +9,8 @@
 // so  M_ij = sum_{k <= min(i, j)} L_ik e_k U_kj.
 // Elementwise over tokens: a group of n/R lanes builds one token, each lane R
 // rows of M, from the token staged in LDS.  HBM-bound (8 n^2 bytes per token).
+#include <type_traits>
+
 #include "mru_build.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
@@ -92,20 +94,39 @@ __global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* _
     const float* xt = sx + tk * XS;
     const float* gt = sg + tk * XS;
     float* ct = sc + tk * XS;
-    for (int64_t tok0 = int64_t(blockIdx.x) * TPI; tok0 < ntok; tok0 += int64_t(gridDim.x) * TPI) {
+    // The next iteration's x and dM are loaded into registers while this one
+    // computes; loads are unconditional (tokens past the end read the last
+    // token and are never stored), so the compiler can wait for them without
+    // waiting for the stores issued after them.
+    constexpr int LDQ = TPI * NN / 4 / kBuildThreads;  // float4 per thread and array
+    static_assert(TPI * NN / 4 == LDQ * kBuildThreads, "tiles must cover the block");
+    float4 px[LDQ], pg[LDQ];
+    auto fetch = [&](int64_t tok0) {
+#pragma unroll
+        for (int k = 0; k < LDQ; ++k) {
+            const int f = tid + k * kBuildThreads;
+            const int64_t tok = min(tok0 + f / (NN / 4), ntok - 1);
+            const float4 vx = reinterpret_cast<const float4*>(x + tok * NN)[f % (NN / 4)];
+            const float4 vg = reinterpret_cast<const float4*>(dM + tok * NN)[f % (NN / 4)];
+            px[k] = make_float4(vx.x, vx.y, vx.z, vx.w);
+            pg[k] = make_float4(vg.x, vg.y, vg.z, vg.w);
+        }
+    };
+    const int64_t step = int64_t(gridDim.x) * TPI;
+    // FULL: all TPI tokens of the iteration exist, so the stores are unconditional.
+    auto iteration = [&](int64_t tok0, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         __syncthreads();
-        for (int f = tid; f < TPI * NN / 4; f += kBuildThreads) {
+#pragma unroll
+        for (int k = 0; k < LDQ; ++k) {
+            const int f = tid + k * kBuildThreads;
             const int t = f / (NN / 4);
             const int q = f % (NN / 4);
-            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f), vg = vx;
-            if (tok0 + t < ntok) {
-                vx = reinterpret_cast<const float4*>(x + (tok0 + t) * NN)[q];
-                vg = reinterpret_cast<const float4*>(dM + (tok0 + t) * NN)[q];
-            }
-            *reinterpret_cast<float4*>(sx + t * XS + 4 * q) = vx;
-            *reinterpret_cast<float4*>(sg + t * XS + 4 * q) = vg;
+            *reinterpret_cast<float4*>(sx + t * XS + 4 * q) = px[k];
+            *reinterpret_cast<float4*>(sg + t * XS + 4 * q) = pg[k];
         }
         __syncthreads();
+        fetch(tok0 + step);
         float sum = 0.f;
 #pragma unroll
         for (int k = 0; k < N; ++k) sum += xt[k * N + k];
@@ -170,13 +191,25 @@ __global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* _
         for (int j = 0; j < N; ++j)
             if (j == i) out[j] = seg[tk * N + i] - meaneg;
         const int64_t tok = tok0 + tk;
-        if (tok < ntok) {
+        if (FULL || tok < ntok) {
             float* dst = dx + tok * NN + i * N;
 #pragma unroll
             for (int q = 0; q < N / 4; ++q)
                 reinterpret_cast<float4*>(dst)[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
         }
+    };
+    const std::integral_constant<bool, true> full;
+    const std::integral_constant<bool, false> partial;
+    int64_t tok0 = int64_t(blockIdx.x) * TPI;
+    if (tok0 >= ntok) return;
+    fetch(tok0);
+    if (tok0 + TPI <= ntok) {
+        // the first full iteration is peeled, so that the loop is entered only
+        // from a full iteration
+        iteration(tok0, full);
+        for (tok0 += step; tok0 + TPI <= ntok; tok0 += step) iteration(tok0, full);
     }
+    if (tok0 < ntok) iteration(tok0, partial);
 }
 
 template <int N>
