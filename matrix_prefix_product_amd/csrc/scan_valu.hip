@@ -414,9 +414,10 @@ __device__ inline void init_rows(float (&st)[R][N], int& ex, const ScanCarry& cy
 // step multiplies by M_t's factors (stage_e puts each staged token's e on its
 // diagonal).
 template <int N, int R, int TB, bool WRITE, bool FX, bool SC>
-__device__ __attribute__((always_inline)) void fwd_sweep(float (&st)[R][N], int& ex, const float* __restrict__ M,
-                          float* __restrict__ P, int32_t* __restrict__ pexp, float* lds,
-                          const ChainInfo* info, int g, int li, int maxlen, int64_t T) {
+__device__ __attribute__((always_inline)) void fwd_sweep(
+    float (&st)[R][N], int& ex, const float* __restrict__ M, float* __restrict__ P,
+    int32_t* __restrict__ pexp, float* lds, const ChainInfo* info, int g, int li, int maxlen,
+    int64_t T) {
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
     float4 reg[V::LD];
@@ -661,16 +662,17 @@ __device__ inline void dx_rows(float (&out)[R][N], const float (&d)[R][N], const
 //             dM_t = P_{t-1}^T Q_t written for the lane's rows.  Of P only the
 //             prefix just before each block's lowest token is read; the block's
 //             other P_{t-1} are recomputed from it by the forward recurrence
-//             P_t = P_{t-1} M_t, with the same products as the forward scan (so
-//             bit for bit the stored prefixes when P came from the matching
-//             forward scan).  This reads n^2 floats per block instead of per token.
+//             P_t = P_{t-1} M_t, with the same products as the forward scan
+//             (bit for bit the stored prefixes when the forward ran one chunk per
+//             sequence, equal up to rounding otherwise).  This reads n^2 floats per
+//             block instead of per token.  With DX the output is dL/dx_t instead
+//             of dM_t (dx_rows), from the exchanged rows of P_{t-1} L_t as well.
 // At the last token of a sequence there is no M_{t+1}: q <- dP_t.
 template <int N, int R, int TB, bool GRAD, bool FX, bool DX>
-__device__ __attribute__((always_inline)) void bwd_sweep(float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M,
-                          const float* __restrict__ P, const float* __restrict__ dP,
-                          float* __restrict__ dM, float* lds, float* nx, float* qx,
-                          const ChainInfo* info, int g, int li, int maxlen, int64_t T,
-                          const ScanCarry& cy) {
+__device__ __attribute__((always_inline)) void bwd_sweep(
+    float (&q)[R][N], float (&w)[R][N], const float* __restrict__ M, const float* __restrict__ P,
+    const float* __restrict__ dP, float* __restrict__ dM, float* lds, float* nx, float* qx,
+    const ChainInfo* info, int g, int li, int maxlen, int64_t T, const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
     const ChainInfo me = info[g];
     const int64_t s0 = me.base - me.t0;  // token index of the sequence's first token
@@ -924,13 +926,11 @@ __device__ __attribute__((always_inline)) void bwd_sweep(float (&q)[R][N], float
 // DX runs alone on its SIMD at the shapes it is for (one chain per sequence),
 // so it may use the whole register file (AGPRs included) instead of spilling.
 template <int N, int R, int TB, bool FX, bool DX>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, DX ? 1 : 2))) void bwd_valu_kernel(const float* __restrict__ M,
-                                                      const float* __restrict__ P,
-                                                      const float* __restrict__ dP,
-                                                      float* __restrict__ dM, int64_t S,
-                                                      int64_t T, int64_t K, int64_t nch,
-                                                      int64_t Z, unsigned char* __restrict__ ws,
-                                                      ScanCarry cy) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, DX ? 1 : 2)))
+void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
+                     const float* __restrict__ dP, float* __restrict__ dM, int64_t S, int64_t T,
+                     int64_t K, int64_t nch, int64_t Z, unsigned char* __restrict__ ws,
+                     ScanCarry cy) {
     using V = Valu<N, R, TB>;
     __shared__ __align__(16) float lds[2 * V::G * V::CH_STRIDE];
     __shared__ __align__(16) float nx[V::G * V::NX_STRIDE];
