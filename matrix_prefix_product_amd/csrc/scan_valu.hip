@@ -923,10 +923,11 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
     for (; blk < maxlen; blk += TB) block(blk, partial);
 }
 
-// DX runs alone on its SIMD at the shapes it is for (one chain per sequence),
-// so it may use the whole register file (AGPRs included) instead of spilling.
+// DX at n = 8 runs alone on its SIMD at the shapes it is for (one chain per
+// sequence), so it may use the whole register file (AGPRs included) instead
+// of spilling; the other instances keep the default occupancy target.
 template <int N, int R, int TB, bool FX, bool DX>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, DX ? 1 : 2)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, DX && N == 8 ? 1 : 8)))
 void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
                      const float* __restrict__ dP, float* __restrict__ dM, int64_t S, int64_t T,
                      int64_t K, int64_t nch, int64_t Z, unsigned char* __restrict__ ws,
