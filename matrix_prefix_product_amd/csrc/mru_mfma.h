@@ -100,43 +100,6 @@ __device__ inline typename Mf<N>::vec_t chain_step_with(const typename Mf<N>::ao
     return out;
 }
 
-// Two independent products, XA <- aA XA and XB <- aB XB, with their MFMAs
-// interleaved so that each waits for its own chain's previous one while the
-// other chain's issues; between(k) runs after the k-th MFMA of the pair
-// sequence, as in chain_step_with.  Each product adds its terms in the same
-// order as chain_step.
-template <int N, class Between>
-__device__ inline void chain_step2_with(const typename Mf<N>::aop_t& aA, typename Mf<N>::vec_t& XA,
-                                        const typename Mf<N>::aop_t& aB, typename Mf<N>::vec_t& XB,
-                                        Between&& between) {
-    constexpr int NT = Mf<N>::NT;
-    typename Mf<N>::vec_t oA, oB;
-#pragma unroll
-    for (int I = 0; I < NT; ++I)
-#pragma unroll
-        for (int J = 0; J < NT; ++J) {
-            d4 accA = d4{0.0, 0.0, 0.0, 0.0}, accB = d4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int K = 0; K < NT; ++K)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int k = ((I * NT + J) * NT + K) * 4 + b;
-                    accA = mfma(aA.v[I][K][b], XA.t[K][J][b], accA);
-                    __builtin_amdgcn_sched_barrier(0);
-                    between(2 * k);
-                    __builtin_amdgcn_sched_barrier(0);
-                    accB = mfma(aB.v[I][K][b], XB.t[K][J][b], accB);
-                    __builtin_amdgcn_sched_barrier(0);
-                    between(2 * k + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            oA.t[I][J] = accA;
-            oB.t[I][J] = accB;
-        }
-    XA = oA;
-    XB = oB;
-}
-
 template <int N>
 __device__ inline typename Mf<N>::vec_t vzero() {
     typename Mf<N>::vec_t v;

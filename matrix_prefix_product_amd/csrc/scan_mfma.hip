@@ -370,105 +370,6 @@ __device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __res
     if (len > 0) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
 }
 
-// Retained chunk as two half-chunk chains.  The aggregate pass runs the chain
-// over the first KR/2 tokens (XA) and the chain over the rest (XB) side by side,
-// their products interleaved on the matrix core (each dependent product of one
-// chain waits out its predecessor while the other chain's issues); the chunk's
-// aggregate is then XB XA (transposed states: the first half's product times
-// the second's).  The apply pass likewise runs the first half from the carry
-// and the second half from carry times the first half's product.  Each
-// token's operand goes through LDS in pairs (buffers 0-1 for the first half,
-// 2-3 for the second, alternating by step).  For whole chunks (len == KR);
-// shorter ones take the single chain.
-template <int N, int KR, int PF>
-__device__ void fwd_pass_retain2(typename Mf<N>::vec_t& XA, typename Mf<N>::vec_t& XB,
-                                 const float* __restrict__ M, int64_t base,
-                                 float (&buf)[KR][4 * Stage<N>::NV], float* tlds) {
-    using F = Mf<N>;
-    using vec_t = typename F::vec_t;
-    constexpr int NN = F::NN;
-    constexpr int NA = 4 * Stage<N>::NV;
-    constexpr int H = KR / 2;
-    static_assert(KR % 2 == 0 && PF <= H, "two equal halves, prefetch within a half");
-    const float* Mb = M + base * NN;
-    const int l = threadIdx.x & 63;
-    XA = videntity<N>(l);
-    XB = videntity<N>(l);
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        load_token<N>(buf[p], Mb + int64_t(p) * NN);
-        load_token<N>(buf[H + p], Mb + int64_t(H + p) * NN);
-    }
-    {
-        operand_write<N>(buf[0], tlds);
-        operand_write<N>(buf[H], tlds + 2 * Stage<N>::BUF);
-        float o[NA];
-        __syncthreads();
-        operand_read<N>(o, tlds);
-#pragma unroll
-        for (int e = 0; e < NA; ++e) buf[0][e] = o[e];
-        operand_read<N>(o, tlds + 2 * Stage<N>::BUF);
-#pragma unroll
-        for (int e = 0; e < NA; ++e) buf[H][e] = o[e];
-    }
-#pragma unroll
-    for (int i = 0; i < H; ++i) {
-        if (i + PF < H) {
-            load_token<N>(buf[i + PF], Mb + int64_t(i + PF) * NN);
-            load_token<N>(buf[H + i + PF], Mb + int64_t(H + i + PF) * NN);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        typename F::aop_t aA, aB;
-        operand_from<N>(aA, buf[i]);
-        operand_from<N>(aB, buf[H + i]);
-        float* tbA = tlds + ((i + 1) & 1) * Stage<N>::BUF;
-        float* tbB = tlds + (2 + ((i + 1) & 1)) * Stage<N>::BUF;
-        chain_step2_with<N>(aA, XA, aB, XB, [&](int k) {
-            if (i + 1 < H) {  // compile-time: tokens i+1 and H+i+1 exist in buf
-                if (k == 0) operand_write<N>(buf[i + 1], tbA);
-                if (k == 1) operand_write<N>(buf[H + i + 1], tbB);
-                if (k == 2) {
-                    float o[NA];
-                    __syncthreads();
-                    operand_read<N>(o, tbA);
-#pragma unroll
-                    for (int e = 0; e < NA; ++e) buf[i + 1][e] = o[e];
-                }
-                if (k == 3) {
-                    float o[NA];
-                    operand_read<N>(o, tbB);
-#pragma unroll
-                    for (int e = 0; e < NA; ++e) buf[H + i + 1][e] = o[e];
-                }
-            }
-        });
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-template <int N, int KR>
-__device__ void fwd_apply_retain2(typename Mf<N>::vec_t XA, typename Mf<N>::vec_t XB,
-                                  float* __restrict__ P, int64_t base,
-                                  const float (&buf)[KR][4 * Stage<N>::NV]) {
-    using F = Mf<N>;
-    using vec_t = typename F::vec_t;
-    constexpr int H = KR / 2;
-#pragma unroll
-    for (int i = 0; i < H; ++i) {
-        typename F::aop_t aA, aB;
-        operand_from<N>(aA, buf[i]);
-        operand_from<N>(aB, buf[H + i]);
-        const vec_t pA = XA, pB = XB;
-        chain_step2_with<N>(aA, XA, aB, XB, [&](int k) {
-            if (i > 0 && k == 0) store_prefix<N, false>(P, nullptr, base + i - 1, pA, 0);
-            if (i > 0 && k == 1) store_prefix<N, false>(P, nullptr, base + H + i - 1, pB, 0);
-        });
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    store_prefix<N, false>(P, nullptr, base + H - 1, XA, 0);
-    store_prefix<N, false>(P, nullptr, base + KR - 1, XB, 0);
-}
-
 // Waves per SIMD the forward kernel is register-budgeted for (tuning knob).
 #ifndef MRU_MFMA_FWD_WAVES
 #define MRU_MFMA_FWD_WAVES 1
@@ -484,11 +385,8 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
     constexpr int NN = N * N;
-    // the retained chunk runs as two half chains (not for the scaled scan)
-    constexpr bool SPLIT = KR > 0 && !SC;
     __shared__ double xl[NN];
-    __shared__ double xa[SPLIT ? NN : 1];  // the first half's product, row-major
-    __shared__ __align__(16) float tlds[(SPLIT ? 4 : 2) * Stage<N>::BUF];
+    __shared__ __align__(16) float tlds[2 * Stage<N>::BUF];
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -518,26 +416,10 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised matrix)
     vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
-    const bool split = SPLIT && ch.len == KR;  // wave-uniform
-    if constexpr (KR > 0) {
-        if constexpr (SPLIT) {
-            if (split) {
-                vec_t XB;
-                fwd_pass_retain2<N, KR, (N == 16 ? MRU_PFR16 : PF)>(X, XB, M, ch.base, buf, tlds);
-                // aggregate^T = XB XA; the first half's product stays in xa for the apply pass
-                store_acc_rows<N, acc_t>(xa, X);
-                store_acc_rows<N, acc_t>(xl, XB);
-                __syncthreads();
-                typename F::aop_t ab;
-                load_a_transposed<N, acc_t>(ab, xl);
-                X = chain_step<N>(ab, X, vzero<N>());
-            }
-        }
-        if (!split)
-            fwd_pass_retain<N, KR, (N == 16 ? MRU_PFR16 : PF), SC>(X, ex, M, ch.base, ch.len, buf, tlds);
-    } else {
+    if constexpr (KR > 0)
+        fwd_pass_retain<N, KR, (N == 16 ? MRU_PFR16 : PF), SC>(X, ex, M, ch.base, ch.len, buf, tlds);
+    else
         fwd_sweep<N, PF, false, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
-    }
     const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
     if (SC && l == 0) ws_store(&agg_exp[c], int32_t(a_ex));
@@ -603,21 +485,10 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     }
 
     // 4. re-run from the carry
-    if constexpr (KR > 0) {
-        if constexpr (SPLIT) {
-            if (split) {
-                // the second half starts from carry times the first half's product
-                __syncthreads();
-                typename F::aop_t aa;
-                load_a_transposed<N, acc_t>(aa, xa);
-                const vec_t XB = chain_step<N>(aa, X, vzero<N>());
-                fwd_apply_retain2<N, KR>(X, XB, P, ch.base, buf);
-            }
-        }
-        if (!split) fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf);
-    } else {
+    if constexpr (KR > 0)
+        fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf);
+    else
         fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
-    }
 }
 
 // ---------------------------------------------------------------------------- backward
