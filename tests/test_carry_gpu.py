@@ -102,7 +102,8 @@ def test_segments_mfma(mpp, n):
 
 
 SCALED_CASES = [(4, 1, 1, 1024, 0), (4, 2, 2, 300, 7), (8, 2, 3, 203, 5), (8, 1, 2, 500, 0),
-                (16, 1, 2, 600, 0), (16, 2, 1, 200, SINGLE), (32, 1, 2, 300, 0), (32, 1, 1, 90, 11)]
+                (16, 1, 2, 600, 0), (16, 2, 1, 200, SINGLE), (16, 1, 1, 640, 64),  # register-retained chunks
+                (32, 1, 2, 300, 0), (32, 1, 1, 90, 11)]
 
 
 @pytest.mark.parametrize("n,B,H,T,chunk", SCALED_CASES)
