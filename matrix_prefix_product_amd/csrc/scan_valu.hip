@@ -366,6 +366,11 @@ __device__ inline void rows_times_ldu_t(float (&st)[R][N], const float* X) {
     rows_times_ldu_t<N, R>(st, x);
 }
 
+// Look-back aggregates (or backward maps) loaded per batch: their loads are in
+// flight together (bounded by registers: n*n floats each per lane).
+template <int N>
+constexpr int kLookback = N == 4 ? 4 : 2;
+
 // Scaled state (scaled forward scan): a chain's rows hold S with P = 2^ex S.
 // renorm_rows multiplies S by a power of two (exact) so that its largest entry
 // has magnitude in [0.5, 1) and adds the shift to ex; ex is the same in every
@@ -533,13 +538,26 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     int l_ex = 0;
     set_identity_rows<N, R>(lrow, li * R);
     float m[V::NN];
-    for (int64_t j = first; j < c; ++j) {
-        ws_load_matrix<N>(m, agg + j * V::NN);
-        rows_times<N, R>(lrow, m);
-        if constexpr (SC) {
-            l_ex += ws_load(&agg_exp[j]);
-            renorm_rows<N, R>(lrow, l_ex);
+    // aggregates are loaded kLookback at a time (clamped into range) so that their
+    // loads are in flight together; the products stay in order
+    for (int64_t j0 = first; j0 < c; j0 += kLookback<N>) {
+        float mb[kLookback<N>][V::NN];
+        int eb[kLookback<N>];
+#pragma unroll
+        for (int d = 0; d < kLookback<N>; ++d) {
+            const int64_t j = min(j0 + d, c - 1);
+            ws_load_matrix<N>(mb[d], agg + j * V::NN);
+            if constexpr (SC) eb[d] = ws_load(&agg_exp[j]);
         }
+#pragma unroll
+        for (int d = 0; d < kLookback<N>; ++d)
+            if (j0 + d < c) {
+                rows_times<N, R>(lrow, mb[d]);
+                if constexpr (SC) {
+                    l_ex += eb[d];
+                    renorm_rows<N, R>(lrow, l_ex);
+                }
+            }
     }
 
     // 3. carry = (prefix of the previous super, or the carried-in state) * lrow
@@ -987,11 +1005,25 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
     set_identity_rows<N, R>(wc, li * R);
     set_zero_rows<N, R>(bc);
     float m[V::NN];
-    for (int64_t j = first; j < c; ++j) {
-        ws_load_matrix<N>(m, swt + j * V::NN);
-        if (later_super) rows_times<N, R>(wc, m);
-        rows_times<N, R>(bc, m);
-        ws_add_rows<N, R>(bc, sbl + j * V::NN + li * R * N);
+    // maps loaded kLookback at a time (clamped into range), composed in order
+    for (int64_t j0 = first; j0 < c; j0 += kLookback<N>) {
+        float mb[kLookback<N>][V::NN], bb[kLookback<N>][R][N];
+#pragma unroll
+        for (int d = 0; d < kLookback<N>; ++d) {
+            const int64_t j = min(j0 + d, c - 1);
+            ws_load_matrix<N>(mb[d], swt + j * V::NN);
+            ws_load_rows<N, R>(bb[d], sbl + j * V::NN + li * R * N);
+        }
+#pragma unroll
+        for (int d = 0; d < kLookback<N>; ++d)
+            if (j0 + d < c) {
+                if (later_super) rows_times<N, R>(wc, mb[d]);
+                rows_times<N, R>(bc, mb[d]);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int q = 0; q < N; ++q) bc[r][q] += bb[d][r][q];
+            }
     }
 
     // 3. carry = Y Wc^T + Bc with Y the adjoint published by the previous super
