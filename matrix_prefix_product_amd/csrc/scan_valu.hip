@@ -485,6 +485,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     __shared__ __align__(16) float lds[V::G * V::CH_STRIDE];
     __shared__ __align__(16) float xch[V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
+    __shared__ int aex[SC ? V::G : 1];
     const int lane = threadIdx.x;
     const int g = lane / V::LPC;
     const int li = lane % V::LPC;
@@ -530,28 +531,34 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     if (SC && li == 0) ws_store(&agg_exp[c], int32_t(a_ex));
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
+    // the wave's own aggregates also go to LDS, for its later chains
+    __syncthreads();
+    store_rows<N, R>(lds + g * V::CH_STRIDE + li * R * N, st);
+    if (SC && li == 0) aex[g] = a_ex;
 
-    // 2. product of the earlier aggregates of the super, left to right
+    // 2. product of the earlier aggregates of the super, left to right: those of
+    // earlier waves (chunks first .. cbase-1) from the workspace, then those of
+    // the wave's earlier chains (cbase .. c-1) from LDS
     wait_range_nonempty(flags, first, cbase, hdr);
     fence_acquire();
     float lrow[R][N];
     int l_ex = 0;
     set_identity_rows<N, R>(lrow, li * R);
     float m[V::NN];
-    // aggregates are loaded kLookback at a time (clamped into range) so that their
-    // loads are in flight together; the products stay in order
-    for (int64_t j0 = first; j0 < c; j0 += kLookback<N>) {
+    // workspace aggregates are loaded kLookback at a time (clamped into range) so
+    // that their loads are in flight together; the products stay in order
+    for (int64_t j0 = first; j0 < cbase; j0 += kLookback<N>) {
         float mb[kLookback<N>][V::NN];
         int eb[kLookback<N>];
 #pragma unroll
         for (int d = 0; d < kLookback<N>; ++d) {
-            const int64_t j = min(j0 + d, c - 1);
+            const int64_t j = min(j0 + d, cbase - 1);
             ws_load_matrix<N>(mb[d], agg + j * V::NN);
             if constexpr (SC) eb[d] = ws_load(&agg_exp[j]);
         }
 #pragma unroll
         for (int d = 0; d < kLookback<N>; ++d)
-            if (j0 + d < c) {
+            if (j0 + d < cbase) {
                 rows_times<N, R>(lrow, mb[d]);
                 if constexpr (SC) {
                     l_ex += eb[d];
@@ -559,6 +566,18 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
                 }
             }
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < V::G - 1; ++j)
+        if (j < g) {
+            load_matrix<N>(m, lds + j * V::CH_STRIDE);
+            rows_times<N, R>(lrow, m);
+            if constexpr (SC) {
+                l_ex += aex[j];
+                renorm_rows<N, R>(lrow, l_ex);
+            }
+        }
+    __syncthreads();  // the LDS is the staging buffer again in step 4
 
     // 3. carry = (prefix of the previous super, or the carried-in state) * lrow
     if (later_super || cy.carry) {  // wave-uniform
@@ -955,6 +974,7 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
     __shared__ __align__(16) float nx[V::G * V::NX_STRIDE];
     __shared__ __align__(16) float qx[(DX ? 3 : 2) * V::G * V::QX_STRIDE];
     __shared__ ChainInfo info[V::G];
+    static_assert(V::CH_STRIDE >= 2 * V::NN, "a chain's staging slot holds its map (W^T and Bl)");
     const int lane = threadIdx.x;
     const int g = lane / V::LPC;
     const int li = lane % V::LPC;
@@ -997,26 +1017,32 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
     ws_store_rows<N, R>(swt + c * V::NN + li * R * N, w);
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
+    // the wave's own maps also go to LDS (W^T, then Bl), for its later chains
+    __syncthreads();
+    store_rows<N, R>(lds + g * V::CH_STRIDE + li * R * N, w);
+    store_rows<N, R>(lds + g * V::CH_STRIDE + V::NN + li * R * N, q);
 
-    // 2. compose the maps of the earlier chunks of the super (first applied first)
+    // 2. compose the maps of the earlier chunks of the super (first applied
+    // first): those of earlier waves from the workspace, then those of the
+    // wave's earlier chains from LDS
     wait_range_nonempty(flags, first, cbase, hdr);
     fence_acquire();
     float wc[R][N], bc[R][N];
     set_identity_rows<N, R>(wc, li * R);
     set_zero_rows<N, R>(bc);
     float m[V::NN];
-    // maps loaded kLookback at a time (clamped into range), composed in order
-    for (int64_t j0 = first; j0 < c; j0 += kLookback<N>) {
+    // workspace maps loaded kLookback at a time (clamped into range), composed in order
+    for (int64_t j0 = first; j0 < cbase; j0 += kLookback<N>) {
         float mb[kLookback<N>][V::NN], bb[kLookback<N>][R][N];
 #pragma unroll
         for (int d = 0; d < kLookback<N>; ++d) {
-            const int64_t j = min(j0 + d, c - 1);
+            const int64_t j = min(j0 + d, cbase - 1);
             ws_load_matrix<N>(mb[d], swt + j * V::NN);
             ws_load_rows<N, R>(bb[d], sbl + j * V::NN + li * R * N);
         }
 #pragma unroll
         for (int d = 0; d < kLookback<N>; ++d)
-            if (j0 + d < c) {
+            if (j0 + d < cbase) {
                 if (later_super) rows_times<N, R>(wc, mb[d]);
                 rows_times<N, R>(bc, mb[d]);
 #pragma unroll
@@ -1025,6 +1051,21 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
                     for (int q = 0; q < N; ++q) bc[r][q] += bb[d][r][q];
             }
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < V::G - 1; ++j)
+        if (j < g) {
+            float bj[R][N];
+            load_matrix<N>(m, lds + j * V::CH_STRIDE);
+            load_rows<N, R>(bj, lds + j * V::CH_STRIDE + V::NN + li * R * N);
+            if (later_super) rows_times<N, R>(wc, m);
+            rows_times<N, R>(bc, m);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int q = 0; q < N; ++q) bc[r][q] += bj[r][q];
+        }
+    __syncthreads();  // the LDS is the staging buffer again in step 4
 
     // 3. carry = Y Wc^T + Bc with Y the adjoint published by the previous super
     if (later_super) {
