@@ -70,7 +70,11 @@ int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir) {
     }
     const int64_t nch = (target + S - 1) / S;
     int64_t K = (T + nch - 1) / nch;
-    if (K < 16) K = 16;
+    // shortest chunk (measured on the C1 / C2 shapes): the vector-ALU backward does
+    // about twice the forward's work per token, so its chains gain from 8-token
+    // chunks where the forward's look-back would cost more than it saves
+    const int64_t kmin = (n <= 8 && dir == 1) ? 8 : 16;
+    if (K < kmin) K = kmin;
     // a forward chunk that fits the register buffer reads its inputs once
     const int64_t keep = dir == 0 ? mfma_retain_tokens(n) : 0;
     if (keep > 0 && K > keep) K = keep;
