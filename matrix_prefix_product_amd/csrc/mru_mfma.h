@@ -125,6 +125,23 @@ __device__ inline typename Mf<N>::vec_t videntity(int l) {
 
 // The accumulator holds X = Y^T; store / load Y row-major at p.  Lane entries
 // of tile (I, J) are Y[16J + tcol][16I + trow(l, 0..3)], 4 contiguous values.
+// The same fp32 stores, non-temporal (the nt bit): for outputs that are streamed
+// once and not read back by the kernel.
+template <int N>
+__device__ inline void store_acc_rows_nt(float* p, const typename Mf<N>::vec_t& X) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) {
+            float* q = p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0);
+            const d4 x = X.t[I][J];
+            const f4v v = {float(x[0]), float(x[1]), float(x[2]), float(x[3])};
+            __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(q));
+        }
+}
+
 template <int N, class T>
 __device__ inline void store_acc_rows(T* p, const typename Mf<N>::vec_t& X) {
     const int l = threadIdx.x & 63;
