@@ -156,19 +156,6 @@ __device__ inline void store_rows(float* dst, const float (&st)[R][N]) {
                 make_float4(st[r][4 * q], st[r][4 * q + 1], st[r][4 * q + 2], st[r][4 * q + 3]);
 }
 
-// Non-temporal stores for the backward's streamed output (see stage_load).
-template <int N, int R>
-__device__ inline void store_rows_nt(float* dst, const float (&st)[R][N]) {
-    typedef float f4v __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int q = 0; q < N / 4; ++q) {
-            const f4v v = {st[r][4 * q], st[r][4 * q + 1], st[r][4 * q + 2], st[r][4 * q + 3]};
-            __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(dst + r * N) + q);
-        }
-}
-
 template <int N, int R>
 __device__ inline void load_rows(float (&st)[R][N], const float* src) {
 #pragma unroll
@@ -252,17 +239,8 @@ __device__ inline void stage_load(float4* reg, const float* src,
         // its value, would make the compiler wait for it right here instead of
         // one block later.
         const int64_t tok = ok ? ci.base + pos + shift : 0;
-        if constexpr (REV) {
-            // The backward streams its inputs (and its output, store_rows_nt)
-            // non-temporally: measured 2-3% faster on the C2L shape, and steadier;
-            // either half alone gains nothing, and the forward is slower with them.
-            typedef float f4v __attribute__((ext_vector_type(4)));
-            const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(src + tok * V::NN) + q);
-            reg[i] = make_float4(v.x, v.y, v.z, v.w);
-        } else {
-            const float4 v = reinterpret_cast<const float4*>(src + tok * V::NN)[q];
-            reg[i] = make_float4(v.x, v.y, v.z, v.w);
-        }
+        const float4 v = reinterpret_cast<const float4*>(src + tok * V::NN)[q];
+        reg[i] = make_float4(v.x, v.y, v.z, v.w);
     }
 }
 
@@ -927,9 +905,9 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
                     if constexpr (DX) {
                         float o[R][N];
                         dx_rows<N, R, V::LPC>(o, d, u, xt, xl + tau * V::NN + li * R * N, li * R);
-                        store_rows_nt<N, R>(dM + (me.base + pos) * V::NN + li * R * N, o);
+                        store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, o);
                     } else {
-                        store_rows_nt<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
+                        store_rows<N, R>(dM + (me.base + pos) * V::NN + li * R * N, d);
                     }
                     if (!FULL && tseq == 0 && cy.dcarry) {
                         // dL/dP_0 = Q_1 M_1^T, M_1 this token's input
