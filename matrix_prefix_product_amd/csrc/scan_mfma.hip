@@ -250,8 +250,8 @@ template <int N, bool SC>
 __device__ inline void store_prefix(float* __restrict__ P, int32_t* __restrict__ pexp, int64_t tok,
                                     const typename Mf<N>::vec_t& X, int ex) {
     // n = 16: the prefixes are streamed out non-temporally, as the inputs are
-    // read (load_token): C3 forward 322-339 -> 289-303 us, C5 forward 176 -> 160
-    // us; at n = 32 either made the forward slower, so it keeps ordinary accesses
+    // read (load_token): C3 forward 321 -> 286 us, C5 forward (between backwards)
+    // 169 -> 162 us; at n = 32 either made the forward slower: ordinary accesses
     if constexpr (N == 16) store_acc_rows_nt<N>(P + tok * Mf<N>::NN, X);
     else store_acc_rows<N, float>(P + tok * Mf<N>::NN, X);
     if (SC && (threadIdx.x & 63) == 0) pexp[tok] = ex;
@@ -532,10 +532,9 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
     const float* Rb = dP + base * NN;
 
     // ring of prefetched operands per token: M_{t+1} (A operand, runs of 4),
-    // dP_t (C operand, runs of 4), P_{t-1} (B operand of the dM product).  M and
-    // dP are read, and dM written, non-temporally (the nt bit): C5 backward
-    // 362-384 -> 350-353 us, neutral at n = 32, bitwise the same results.
-    typedef float f4v __attribute__((ext_vector_type(4)));
+    // dP_t (C operand, runs of 4), P_{t-1} (B operand of the dM product).  (Read
+    // non-temporally the backward was faster launch after launch, but slower
+    // right after the forward, as in a training step: ordinary accesses.)
     float rm[PF][NA], rr[PF][NA], rp[PF][GRAD ? NA : 1];
     auto fetch = [&](int slot, int i) {
         const int pos = max(len - 1 - i, 0);
@@ -544,8 +543,8 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
         for (int I = 0; I < NT; ++I)
 #pragma unroll
             for (int K = 0; K < NT; ++K) {
-                const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(
-                    Mb + int64_t(hi_m > 0 ? pm : pos) * NN + (16 * I + ac) * N + 16 * K + trow(l, 0)));
+                const float4 v = *reinterpret_cast<const float4*>(
+                    Mb + int64_t(hi_m > 0 ? pm : pos) * NN + (16 * I + ac) * N + 16 * K + trow(l, 0));
                 float* d = &rm[slot][(I * NT + K) * 4];
                 d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
             }
@@ -553,8 +552,8 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
         for (int I = 0; I < NT; ++I)
 #pragma unroll
             for (int J = 0; J < NT; ++J) {
-                const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(
-                    Rb + int64_t(pos) * NN + (16 * J + c) * N + 16 * I + trow(l, 0)));
+                const float4 v = *reinterpret_cast<const float4*>(
+                    Rb + int64_t(pos) * NN + (16 * J + c) * N + 16 * I + trow(l, 0));
                 float* d = &rr[slot][(I * NT + J) * 4];
                 d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
             }
@@ -625,9 +624,9 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                         for (int b = 0; b < 4; ++b)
                             ag.v[I][K][b] = tr[(16 * I + ac) * TS + 16 * K + trow(l, b)];
                 const vec_t D = chain_step<N>(ag, bv, vzero<N>());
-                store_acc_rows_nt<N>(out, D);
+                store_acc_rows<N, float>(out, D);
             } else {
-                store_acc_rows_nt<N>(out, G);  // t = 0: P_{-1} = I
+                store_acc_rows<N, float>(out, G);  // t = 0: P_{-1} = I
             }
             if (pos < lo_p && cy.dcarry) {
                 // dL/dP_{-1} = Q_0 M_0^T, i.e. its transpose is M_0 G_0
