@@ -27,13 +27,15 @@ __all__ = [
     "build_inputs", "build_inputs_bwd", "scan_fwd", "mru_layer", "MRUBuild", "scan_bwd", "flatten", "mru_scan", "MRUScan",
     "scan_fwd_x", "scan_bwd_x", "scan_fwd_ex", "scan_bwd_ex", "scan_bwd_dx", "build_orthogonal",
     "scan_plan", "scan_chunk", "workspace_bytes", "library_path", "load_library",
-    "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N",
+    "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N", "FUSED_N", "FUSED_FWD_N",
 ]
 
 DIR_FWD = 0
 DIR_BWD = 1
 SUPPORTED_N = (4, 8, 16, 32)
-# Sizes whose scans can start from raw token vectors (input matrices built on chip).
+# Sizes whose forward scan can start from raw token vectors (input matrices
+# built on chip), and sizes whose backward scans can too (FUSED_N).
+FUSED_FWD_N = (4, 8, 16)
 FUSED_N = (4, 8)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmru.so")
@@ -279,18 +281,19 @@ def scan_bwd(M: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
     return out
 
 
-def _xshape(x: torch.Tensor, n: int):
+def _xshape(x: torch.Tensor, n: int, allowed=FUSED_N):
     _require(x, "x", 4)
     B, H, T, nn = x.shape
-    if n not in FUSED_N or nn != n * n:
-        raise ValueError(f"x must be [B,H,T,n*n] with n in {FUSED_N}, got {tuple(x.shape)}, n={n}")
+    if n not in allowed or nn != n * n:
+        raise ValueError(f"x must be [B,H,T,n*n] with n in {allowed}, got {tuple(x.shape)}, n={n}")
     return B, H, T
 
 
 def scan_fwd_x(x: torch.Tensor, n: int, chunk: int = 0, out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """scan_fwd(build_inputs(x, n)) in one pass that never writes the input matrices."""
-    B, H, T = _xshape(x, n)
+    """scan_fwd(build_inputs(x, n)) in one pass that never writes the input
+    matrices (n in FUSED_FWD_N)."""
+    B, H, T = _xshape(x, n, FUSED_FWD_N)
     if out is None:
         out = torch.empty((B, H, T, n, n), dtype=torch.float32, device=x.device)
     else:
@@ -331,11 +334,11 @@ def scan_bwd_x(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 
     return out
 
 
-def _inshape(inp: torch.Tensor, from_x: bool, n: int | None):
+def _inshape(inp: torch.Tensor, from_x: bool, n: int | None, allowed=FUSED_N):
     if from_x:
         if n is None:
             raise ValueError("n is required when the input is raw token vectors")
-        return (*_xshape(inp, n), n)
+        return (*_xshape(inp, n, allowed), n)
     return _mshape(inp)
 
 
@@ -354,10 +357,10 @@ def scan_fwd_ex(inp: torch.Tensor, carry: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None):
     """P_t = P_0 M_1 ... M_t with P_0 = 2^carry_exp * carry (I when carry is None).
 
-    inp is M [B,H,T,n,n], or x [B,H,T,n*n] with from_x (n = 4, 8).  Returns P,
-    or (P, E) with scaled: P_t = 2^E[t] * P[t], max |P[t]| in [0.5, 1].  The
-    last token's (P, E) is the carry into the next segment."""
-    B, H, T, n = _inshape(inp, from_x, n)
+    inp is M [B,H,T,n,n], or x [B,H,T,n*n] with from_x (n in FUSED_FWD_N).
+    Returns P, or (P, E) with scaled: P_t = 2^E[t] * P[t], max |P[t]| in
+    [0.5, 1].  The last token's (P, E) is the carry into the next segment."""
+    B, H, T, n = _inshape(inp, from_x, n, FUSED_FWD_N)
     dev = inp.device
     carry = _carry_arg(carry, B, H, n, dev)
     if carry_exp is not None:

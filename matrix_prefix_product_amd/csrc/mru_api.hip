@@ -237,7 +237,7 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
                          const ScanCarry& cy) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
-    if (from_x && n > 8) return MRU_ERR_SHAPE;  // the matrix-core scans read M
+    if (from_x && n > 16) return MRU_ERR_SHAPE;  // the n = 32 scan reads M
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P) return MRU_ERR_NULL;
@@ -273,7 +273,7 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
         if (st != MRU_OK) return st;
     }
     if (n <= 8) return launched(launch_fwd_valu(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
-    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, cy));
+    return launched(launch_fwd_mfma(M, P, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, cy));
 }
 
 mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float* dM, int64_t B,

@@ -17,8 +17,11 @@
 // product, state times new input).  Backward: the gradient of
 // sum_t <dP_t, P_t>, with G_t = Q_t^T = dP_t^T + M_{t+1} G_{t+1} advanced the
 // same way and dM_t^T = G_t P_{t-1} taken through one LDS transpose of G_t.
+#include <utility>
+
 #include "mru_device.h"
 #include "mru_kernels.h"
+#include "mru_build.h"
 #include "mru_mfma.h"
 
 // Prefetch depth of the retained n = 16 aggregate pass (tokens in flight; the
@@ -149,6 +152,13 @@ constexpr int walk_depth() { return N == 16 ? 4 : (BWD ? 1 : 2); }
 
 // ---------------------------------------------------------------------------- forward
 
+// f(integral_constant<int, I>) for I = Is..., in order: a loop expanded at
+// compile time whatever its body's size.
+template <int... Is, class F>
+__device__ inline void static_for(std::integer_sequence<int, Is...>, F&& f) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+
 // Operand staging of the forward chain.  The A operand of M_t^T needs, in lane
 // l, 4 entries of one column of M_t (M_t[16K + trow(l, b)][16I + tacol(l)],
 // b = 0..3), which row-major memory holds 4*n bytes apart.  Loading them
@@ -235,6 +245,110 @@ __device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4
         a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(o[e]);
 }
 
+// Forward from raw token vectors (n = 16): the operand entries of M_t^T are
+// formed from the staged x_t instead of read.  With X = x_t viewed row-major,
+// M = Lt W where Lt is the unit lower factor (Lt_rk = X_rk for k < r, 1 on the
+// diagonal) and W = diag(e) U (W_kc = e_k X_kc for k < c, e_k on the diagonal),
+// e_k = exp(X_kk - mean_j X_jj) ("Improving Matrix Recurrent Units as an
+// Attention Alternative", Key Points: LDU fill, determinant-correcting
+// scalar).  A lane holds 4 contiguous entries of one row r of X.  Three phases,
+// separated by barriers and spread between a token's products like the LDS
+// transpose of the plain forward:
+//   stage:   every lane writes its piece of X row-major to the slot;
+//   factors: every lane reads the diagonal (mean in index order, as the build
+//            kernel), e_r, and writes its entries of Lt (row-major) and of W
+//            (transposed, so a column of W is a contiguous row);
+//   read:    every lane forms its 4 entries M[trow(l, b)][tacol(l)] as 16-term
+//            dot products of rows of Lt with a row of W^T (fp32, as the build).
+// A slot (Lt, W^T, X) per token parity, as the transpose buffers.  (The lanes
+// read the diagonal from the staged X rather than select it from their own
+// pieces: a select over a piece's entries became an indexed load, which put
+// the retained chunk's registers in scratch memory.)
+template <int N>
+struct StageX {
+    static_assert(N == 16, "the forward from raw token vectors is built for n = 16");
+    static constexpr int LS = Stage<N>::LS;
+    static constexpr int BUF = Stage<N>::BUF;
+    static constexpr int SLOT = 3 * BUF;  // floats: Lt, W^T, X
+};
+
+template <int N>
+__device__ inline void xop_stage(const float (&v)[4 * Stage<N>::NV], float* slot) {
+    using SX = StageX<N>;
+    const int l = threadIdx.x & 63;
+    // n = 16: one piece per lane, row l/4, columns 4(l%4) .. 4(l%4)+3
+    *reinterpret_cast<float4*>(slot + 2 * SX::BUF + (l >> 2) * SX::LS + 4 * (l & 3)) =
+        make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <int N>
+__device__ inline void xop_factors(const float (&v)[4 * Stage<N>::NV], float* slot) {
+    using SX = StageX<N>;
+    const int l = threadIdx.x & 63;
+    const int r = l >> 2;
+    const int c0 = 4 * (l & 3);
+    const float* xs = slot + 2 * SX::BUF;
+    float d[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) d[k] = xs[k * (SX::LS + 1)];
+    const float mean = ldu_mean_diag<N>(d);
+    const float er = expf(xs[r * (SX::LS + 1)] - mean);
+    float lt[4], wt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j;
+        lt[j] = c < r ? v[j] : (c == r ? 1.f : 0.f);
+        wt[j] = c > r ? er * v[j] : (c == r ? er : 0.f);
+    }
+    *reinterpret_cast<float4*>(slot + r * SX::LS + c0) = make_float4(lt[0], lt[1], lt[2], lt[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) slot[SX::BUF + (c0 + j) * SX::LS + r] = wt[j];
+}
+
+template <int N>
+__device__ inline void xop_read(float (&o)[4 * Stage<N>::NV], const float* slot) {
+    using SX = StageX<N>;
+    const int l = threadIdx.x & 63;
+    float w[N];  // column tacol(l) of W
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(slot + SX::BUF + tacol(l) * SX::LS + 4 * q);
+        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float* lrow = slot + trow(l, b) * SX::LS;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            const float4 t = *reinterpret_cast<const float4*>(lrow + 4 * q);
+            acc = fmaf(t.x, w[4 * q], acc);
+            acc = fmaf(t.y, w[4 * q + 1], acc);
+            acc = fmaf(t.z, w[4 * q + 2], acc);
+            acc = fmaf(t.w, w[4 * q + 3], acc);
+        }
+        o[b] = acc;
+    }
+}
+
+// Floats per token-parity slot of the forward from raw token vectors (0 otherwise).
+template <int N, bool FX>
+constexpr int xslot() {
+    if constexpr (FX) return StageX<N>::SLOT;
+    else return 0;
+}
+
+// The three phases back to back (a chunk's first token).
+template <int N>
+__device__ inline void to_operand_x(float (&o)[4 * Stage<N>::NV], const float (&v)[4 * Stage<N>::NV],
+                                    float* slot) {
+    xop_stage<N>(v, slot);
+    __syncthreads();
+    xop_factors<N>(v, slot);
+    __syncthreads();
+    xop_read<N>(o, slot);
+}
+
 // Software pipelining of the forward chain.  Instructions issue in order, and
 // each of a token's products waits at issue for the previous one's
 // accumulator, so anything placed after them would only start once the last
@@ -261,10 +375,10 @@ __device__ inline void store_prefix(float* __restrict__ P, int32_t* __restrict__
 // the token PF further on, address clamped into the chunk) as soon as its
 // pieces have been turned into operands.  The main loop runs whole blocks of PF
 // tokens so every ring slot stays in fixed registers.
-template <int N, int PF, bool WRITE, bool SC>
-__device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
+template <int N, int PF, bool WRITE, bool FX, bool SC>
+__device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
                           float* __restrict__ P, int32_t* __restrict__ pexp, int64_t base, int len,
-                          float* tlds) {
+                          float* tlds, float* xlds) {
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NN = F::NN;
@@ -275,21 +389,36 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __rest
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_token<N>(ring[p], Mb + int64_t(min(p, len - 1)) * NN);
     float o[NA];  // operands of the next token to multiply
-    to_operand<N>(o, ring[0], tlds);
+    if constexpr (FX) to_operand_x<N>(o, ring[0], xlds);
+    else to_operand<N>(o, ring[0], tlds);
     load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
     auto step = [&](int p, int t, bool refill) {
         typename F::aop_t a;
         operand_from<N>(a, o);
         const int pn = (p + 1) % PF;  // ring slot of token t + 1
         float* tb = tlds + ((t + 1) & 1) * Stage<N>::BUF;
+        float* xb = xlds + ((t + 1) & 1) * xslot<N, FX>();
         // token t+1's operand goes through LDS while token t's products run
         vec_t Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
-            if (k == 0 && t + 1 < len) operand_write<N>(ring[pn], tb);
-            if (k == 1 && t + 1 < len) {
-                __syncthreads();
-                operand_read<N>(o, tb);
+            if constexpr (FX) {
+                if (k == 0 && t + 1 < len) xop_stage<N>(ring[pn], xb);
+                if (k == 1 && t + 1 < len) {
+                    __syncthreads();
+                    xop_factors<N>(ring[pn], xb);
+                }
+                if (k == 2 && WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
+                if (k == 2 && t + 1 < len) {
+                    __syncthreads();
+                    xop_read<N>(o, xb);
+                }
+            } else {
+                if (k == 0 && t + 1 < len) operand_write<N>(ring[pn], tb);
+                if (k == 1 && t + 1 < len) {
+                    __syncthreads();
+                    operand_read<N>(o, tb);
+                }
+                if (k == 2 && WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
             }
-            if (k == 2 && WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
             if (k == 3 && t + 1 < len && refill)
                 load_token<N>(ring[pn], Mb + int64_t(min(t + 1 + PF, len - 1)) * NN);
         });
@@ -313,10 +442,10 @@ __device__ void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __rest
 // chunk), converts each to its operand entries in place, and the apply pass
 // reuses them, so each input matrix is read from HBM once even when the chunk
 // needs a carry.
-template <int N, int KR, int PF, bool SC>
-__device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
+template <int N, int KR, int PF, bool FX, bool SC>
+__device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
                                 int64_t base, int len, float (&buf)[KR][4 * Stage<N>::NV],
-                                float* tlds) {
+                                float* tlds, float* xlds) {
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NN = F::NN;
@@ -327,28 +456,48 @@ __device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* 
     for (int p = 0; p < PF && p < KR; ++p) load_token<N>(buf[p], Mb + int64_t(min(p, len - 1)) * NN);
     {
         float o[NA];
-        to_operand<N>(o, buf[0], tlds);
+        if constexpr (FX) to_operand_x<N>(o, buf[0], xlds);
+        else to_operand<N>(o, buf[0], tlds);
 #pragma unroll
         for (int e = 0; e < NA; ++e) buf[0][e] = o[e];
     }
-#pragma unroll
-    for (int t = 0; t < KR; ++t) {
-        if (t + PF < KR) load_token<N>(buf[t + PF], Mb + int64_t(min(t + PF, len - 1)) * NN);
+    // expanded at compile time (an index sequence, not the loop unroller: with
+    // the forward from raw token vectors the body outgrows the unroller's size
+    // limit, and a rolled loop would index buf, moving it to scratch memory)
+    static_for(std::make_integer_sequence<int, KR>{}, [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (t + PF < KR) load_token<N>(buf[t + PF], Mb + int64_t(min(t + PF, len - 1)) * NN);
         __builtin_amdgcn_sched_barrier(0);
         if (t < len) {
             typename F::aop_t a;
             operand_from<N>(a, buf[t]);
             float* tb = tlds + ((t + 1) & 1) * Stage<N>::BUF;
+            float* xb = xlds + ((t + 1) & 1) * xslot<N, FX>();
             const bool next = t + 1 < KR && t + 1 < len;
             vec_t Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
-                if (t + 1 < KR) {  // compile-time: buf[t + 1] exists
-                    if (k == 0 && next) operand_write<N>(buf[t + 1], tb);
-                    if (k == 1 && next) {
-                        float o[NA];
-                        __syncthreads();
-                        operand_read<N>(o, tb);
+                if constexpr (t + 1 < KR) {  // buf[t + 1] exists
+                    if constexpr (FX) {
+                        if (k == 0 && next) xop_stage<N>(buf[t + 1], xb);
+                        if (k == 1 && next) {
+                            __syncthreads();
+                            xop_factors<N>(buf[t + 1], xb);
+                        }
+                        if (k == 2 && next) {
+                            float o[NA];
+                            __syncthreads();
+                            xop_read<N>(o, xb);
 #pragma unroll
-                        for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+                            for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+                        }
+                    } else {
+                        if (k == 0 && next) operand_write<N>(buf[t + 1], tb);
+                        if (k == 1 && next) {
+                            float o[NA];
+                            __syncthreads();
+                            operand_read<N>(o, tb);
+#pragma unroll
+                            for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+                        }
                     }
                 }
             });
@@ -356,11 +505,11 @@ __device__ void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* 
             X = Xn;
             if constexpr (SC) renorm_acc<N>(X, ex);
         }
-    }
+    });
 }
 
 template <int N, int KR, bool SC>
-__device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __restrict__ P,
+__device__ __attribute__((always_inline)) void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __restrict__ P,
                                  int32_t* __restrict__ pexp, int64_t base, int len,
                                  const float (&buf)[KR][4 * Stage<N>::NV]) {
     using F = Mf<N>;
@@ -386,7 +535,7 @@ __device__ void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __res
 #define MRU_MFMA_FWD_WAVES 1
 #endif
 
-template <int N, int PF, int KR, bool SC>
+template <int N, int PF, int KR, bool FX, bool SC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MRU_MFMA_FWD_WAVES)))
 void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
@@ -398,6 +547,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     constexpr int NN = N * N;
     __shared__ double xl[NN];
     __shared__ __align__(16) float tlds[2 * Stage<N>::BUF];
+    __shared__ __align__(16) float xlds[FX ? 2 * xslot<N, FX>() : 4];  // FX: the token factors
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -411,7 +561,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     int ex = 0;
     if (!multi) {
         vec_t X = init_acc<N, SC>(ex, cy, seq);
-        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
+        fwd_sweep<N, PF, true, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
         return;
     }
     const WsLayout L = ws_layout(nchunks, N, sizeof(acc_t), 2);
@@ -428,9 +578,9 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0)
-        fwd_pass_retain<N, KR, (N == 16 ? MRU_PFR16 : PF), SC>(X, ex, M, ch.base, ch.len, buf, tlds);
+        fwd_pass_retain<N, KR, (N == 16 ? MRU_PFR16 : PF), FX, SC>(X, ex, M, ch.base, ch.len, buf, tlds, xlds);
     else
-        fwd_sweep<N, PF, false, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
+        fwd_sweep<N, PF, false, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
     const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
     if (SC && l == 0) ws_store(&agg_exp[c], int32_t(a_ex));
@@ -499,7 +649,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     if constexpr (KR > 0)
         fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf);
     else
-        fwd_sweep<N, PF, true, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds);
+        fwd_sweep<N, PF, true, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
 }
 
 // ---------------------------------------------------------------------------- backward
@@ -741,15 +891,15 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
 }
 
-template <int N, int PF, int KR>
+template <int N, int PF, int KR, bool FX>
 hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, int64_t nch,
                    int64_t Z, void* ws, hipStream_t stream, const ScanCarry& cy) {
     if (cy.out_exp)
-        hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR, true>), dim3(unsigned(S * nch)), dim3(64), 0,
-                           stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
+        hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR, FX, true>), dim3(unsigned(S * nch)), dim3(64),
+                           0, stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     else
-        hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR, false>), dim3(unsigned(S * nch)), dim3(64), 0,
-                           stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
+        hipLaunchKernelGGL((fwd_mfma_kernel<N, PF, KR, FX, false>), dim3(unsigned(S * nch)), dim3(64),
+                           0, stream, M, P, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
@@ -776,14 +926,18 @@ constexpr int kRetain16 = MRU_RETAIN16;
 int mfma_retain_tokens(int n) { return n == 16 ? kRetain16 : 0; }
 
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
-                           int64_t nch, int64_t Z, void* ws, hipStream_t stream,
+                           int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
                            const ScanCarry& cy) {
     if (n == 16) {
-        if (kRetain16 > 0 && nch > 1 && K <= kRetain16)
-            return run_fwd<16, MRU_PF16, kRetain16>(M, P, S, T, K, nch, Z, ws, stream, cy);
-        return run_fwd<16, MRU_PF16, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        const bool retain = kRetain16 > 0 && nch > 1 && K <= kRetain16;
+        if (from_x) {
+            if (retain) return run_fwd<16, MRU_PF16, kRetain16, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+            return run_fwd<16, MRU_PF16, 0, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        }
+        if (retain) return run_fwd<16, MRU_PF16, kRetain16, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd<16, MRU_PF16, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
-    if (n == 32) return run_fwd<32, 4, 0>(M, P, S, T, K, nch, Z, ws, stream, cy);
+    if (n == 32 && !from_x) return run_fwd<32, 4, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
     return hipErrorInvalidValue;
 }
 

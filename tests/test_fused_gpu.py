@@ -1,8 +1,10 @@
-"""GPU parity of the scans that start from raw token vectors (n = 4, 8).
+"""GPU parity of the scans that start from raw token vectors (forward n = 4, 8,
+16; backward n = 4, 8).
 
 mru_scan_fwd_x / mru_scan_bwd_x multiply by the LDU factors of each input
-state matrix instead of forming it, so they agree with build-then-scan up to
-rounding order; both are graded against the fp64 oracle
+state matrix instead of forming it (n = 16: form it on chip for the fp64
+chain), so they agree with build-then-scan up to rounding order; both are
+graded against the fp64 oracle
 (scan_ref(build_ref(x)), bwd_ref(build_ref(x), R)) with the forward / backward
 tolerances, and must be deterministic run to run.  mru_scan_bwd_dx goes on to
 dL/dx in the same pass, graded against build_vjp_ref of the oracle's backward.
@@ -12,12 +14,12 @@ import pytest
 import torch
 
 from gpu_helpers import BUILD_TOL, BWD_TOL, FWD_TOL, dev, fwd_errors, host, say, summary
-from oracle import build_ref, build_vjp_ref, bwd_ref, rel_fro_err
+from oracle import build_ref, build_vjp_ref, bwd_ref, rel_fro_err, scaled_ref, scan_ref
 from workloads import gen_R, gen_x
 
 pytestmark = pytest.mark.gpu
 
-SIGMA = {4: (0.1, 0.05), 8: (0.1, 0.05)}
+SIGMA = {4: (0.1, 0.05), 8: (0.1, 0.05), 16: (0.05, 0.02)}
 
 CASES = [
     (4, 1, 1, 1024, 0), (4, 3, 2, 203, 3), (4, 2, 2, 97, 1), (4, 5, 1, 120, 120),
@@ -226,12 +228,76 @@ def test_fused_layer_autograd(mpp, n):
 
 
 def test_fused_rejects_matrix_core_sizes(mpp):
-    x = torch.zeros(1, 1, 4, 256, device="cuda")
+    # the forward from x covers n = 4, 8, 16, the backward n = 4, 8
+    x = torch.zeros(1, 1, 4, 1024, device="cuda")
     with pytest.raises(ValueError):
-        mpp.scan_fwd_x(x, 16)
+        mpp.scan_fwd_x(x, 32)
     lib = mpp.load_library()
-    P = torch.empty(1, 1, 4, 16, 16, device="cuda")
+    P = torch.empty(1, 1, 4, 32, 32, device="cuda")
     import ctypes
     st = lib.mru_scan_fwd_x(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(P.data_ptr()),
-                            1, 1, 4, 16, 0, None, 0, None)
+                            1, 1, 4, 32, 0, None, 0, None)
     assert st == 2
+    x16 = torch.zeros(1, 1, 4, 256, device="cuda")
+    P16 = torch.zeros(1, 1, 4, 16, 16, device="cuda")
+    with pytest.raises(ValueError):
+        mpp.scan_bwd_x(x16, P16, P16)
+
+
+# n = 16 from raw token vectors: every plan shape of the matrix-core forward --
+# one chunk per sequence (streamed), register-retained chunks (auto plan, a
+# ragged forced chunk, exactly 64 tokens), streamed chunks longer than the
+# register buffer, a single token
+N16_CASES = [(128, 16, 40, 0), (4, 4, 1000, 0), (2, 3, 203, 5), (2, 2, 130, 64),
+             (1, 2, 300, 100), (3, 1, 1, 0)]
+
+
+@pytest.mark.parametrize("B,H,T,chunk", N16_CASES)
+def test_fused_fwd_n16(mpp, B, H, T, chunk):
+    n = 16
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD, chunk)
+    say(f"[fused fwd n=16] B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    x = _x(B, H, T, n, seed=T + 7)
+    xd = dev(x)
+    P = mpp.scan_fwd_x(xd, n, chunk)
+    again = mpp.scan_fwd_x(xd, n, chunk)
+    assert torch.equal(P.view(torch.int32), again.view(torch.int32)), "not deterministic"
+    err, dom, P_ref = fwd_errors(host(P), build_ref(x, n))
+    say("  " + summary(err, dom))
+    assert dom.all() and err.max() <= FWD_TOL
+    # against build + scan on the same tokens: the token matrices are rounded to
+    # fp32 by both, from sums in different orders
+    P_two = host(mpp.scan_fwd(mpp.build_inputs(xd, n), chunk))
+    d = rel_fro_err(host(P), P_two.astype(np.float64))
+    say(f"  against build + scan: max {d.max():.3e}")
+    assert d.max() <= FWD_TOL
+
+
+@pytest.mark.parametrize("chunk", [0, 9, 100])
+def test_fused_fwd_n16_carry_and_scaled(mpp, chunk):
+    # a carried-in state, and the scaled form: 2^E * P~ carries the plain scan's
+    # bits (exact powers of two), both graded against the oracle
+    n, B, H, T = 16, 2, 2, 400
+    x = _x(B, H, T, n, seed=11)
+    rng = np.random.default_rng(4)
+    C = (np.eye(n) + 0.1 * rng.standard_normal((B, H, n, n))).astype(np.float32)
+    xd, Cd = dev(x), dev(C)
+    P = host(mpp.scan_fwd_ex(xd, carry=Cd, from_x=True, n=n, chunk=chunk))
+    Pm, E = mpp.scan_fwd_ex(xd, carry=Cd, scaled=True, from_x=True, n=n, chunk=chunk)
+    Pm, E = host(Pm), host(E)
+    assert np.array_equal(np.ldexp(Pm, E[..., None, None]).astype(np.float32), P)
+    ref = scan_ref(build_ref(x, n), C.astype(np.float64))
+    err = rel_fro_err(np.ldexp(Pm.astype(np.float64), E[..., None, None]), ref)
+    say(f"[fused fwd n=16 carry, scaled] chunk={chunk}: max {err.max():.3e}")
+    assert err.max() <= FWD_TOL
+    _, E_ref = scaled_ref(ref)
+    assert np.abs(E - E_ref).max() <= 1
+
+
+def test_fused_fwd_n16_zero_input_is_identity(mpp):
+    # x = 0: mean 0, e = 1, both factors I, so every token matrix and prefix is I exactly
+    n, T = 16, 150
+    xd = torch.zeros(2, 2, T, n * n, device="cuda")
+    for chunk in (0, 7, 100):
+        P = host(mpp.scan_fwd_x(xd, n, chunk))
+        assert np.array_equal(P, np.broadcast_to(np.eye(n, dtype=np.float32), P.shape))
