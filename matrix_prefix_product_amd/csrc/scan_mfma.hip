@@ -247,29 +247,29 @@ __device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4
 
 // Forward from raw token vectors (n = 16): the operand entries of M_t^T are
 // formed from the staged x_t instead of read.  With X = x_t viewed row-major,
-// M = Lt W where Lt is the unit lower factor (Lt_rk = X_rk for k < r, 1 on the
+// M = Lt W where Lt is the unit lower factor (Lt_ik = X_ik for k < i, 1 on the
 // diagonal) and W = diag(e) U (W_kc = e_k X_kc for k < c, e_k on the diagonal),
 // e_k = exp(X_kk - mean_j X_jj) ("Improving Matrix Recurrent Units as an
 // Attention Alternative", Key Points: LDU fill, determinant-correcting
-// scalar).  A lane holds 4 contiguous entries of one row r of X.  Three phases,
-// separated by barriers and spread between a token's products like the LDS
-// transpose of the plain forward:
-//   stage:   every lane writes its piece of X row-major to the slot;
-//   factors: every lane reads the diagonal (mean in index order, as the build
-//            kernel), e_r, and writes its entries of Lt (row-major) and of W
-//            (transposed, so a column of W is a contiguous row);
-//   read:    every lane forms its 4 entries M[trow(l, b)][tacol(l)] as 16-term
-//            dot products of rows of Lt with a row of W^T (fp32, as the build).
-// A slot (Lt, W^T, X) per token parity, as the transpose buffers.  (The lanes
-// read the diagonal from the staged X rather than select it from their own
-// pieces: a select over a piece's entries became an indexed load, which put
-// the retained chunk's registers in scratch memory.)
+// scalar).  The product runs on the matrix core in fp32 (four
+// v_mfma_f32_16x16x4f32, D[i][j] in lane j + 16(i/4), register i%4): taking
+// W's columns in the order tacol, lane l's four results are exactly its
+// A-operand entries M[trow(l, b)][tacol(l)] of the fp64 chain.  Three phases,
+// separated by barriers and spread between the chain's products:
+//   stage:   every lane writes its 16-byte piece of X row-major to the slot;
+//   factors: every lane reads X_kk for k = l%16, sums the 16 over its row of
+//            lanes (DPP butterfly: each step adds two values in either order,
+//            so every lane gets the same bits), forms e_{l%16}; lanes 0..15
+//            write e to the slot;
+//   read:    every lane reads its 4 entries of Lt and of W from X and e and
+//            issues the four fp32 products.
+// A slot (X, e) per token parity, as the transpose buffers.
 template <int N>
 struct StageX {
     static_assert(N == 16, "the forward from raw token vectors is built for n = 16");
     static constexpr int LS = Stage<N>::LS;
     static constexpr int BUF = Stage<N>::BUF;
-    static constexpr int SLOT = 3 * BUF;  // floats: Lt, W^T, X
+    static constexpr int SLOT = BUF + N;  // floats: X (row stride LS), e
 };
 
 template <int N>
@@ -277,58 +277,49 @@ __device__ inline void xop_stage(const float (&v)[4 * Stage<N>::NV], float* slot
     using SX = StageX<N>;
     const int l = threadIdx.x & 63;
     // n = 16: one piece per lane, row l/4, columns 4(l%4) .. 4(l%4)+3
-    *reinterpret_cast<float4*>(slot + 2 * SX::BUF + (l >> 2) * SX::LS + 4 * (l & 3)) =
-        make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(slot + (l >> 2) * SX::LS + 4 * (l & 3)) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Sum over each row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror).
+__device__ inline float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
 }
 
 template <int N>
-__device__ inline void xop_factors(const float (&v)[4 * Stage<N>::NV], float* slot) {
+__device__ inline void xop_factors(float* slot) {
     using SX = StageX<N>;
     const int l = threadIdx.x & 63;
-    const int r = l >> 2;
-    const int c0 = 4 * (l & 3);
-    const float* xs = slot + 2 * SX::BUF;
-    float d[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k) d[k] = xs[k * (SX::LS + 1)];
-    const float mean = ldu_mean_diag<N>(d);
-    const float er = expf(xs[r * (SX::LS + 1)] - mean);
-    float lt[4], wt[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = c0 + j;
-        lt[j] = c < r ? v[j] : (c == r ? 1.f : 0.f);
-        wt[j] = c > r ? er * v[j] : (c == r ? er : 0.f);
-    }
-    *reinterpret_cast<float4*>(slot + r * SX::LS + c0) = make_float4(lt[0], lt[1], lt[2], lt[3]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) slot[SX::BUF + (c0 + j) * SX::LS + r] = wt[j];
+    const float dk = slot[(l & 15) * (SX::LS + 1)];  // X_kk, k = l % 16
+    const float mean = row16_sum(dk) * (1.0f / N);  // exact scaling by 1/16
+    const float ek = expf(dk - mean);
+    if (l < N) slot[SX::BUF + l] = ek;
 }
 
 template <int N>
 __device__ inline void xop_read(float (&o)[4 * Stage<N>::NV], const float* slot) {
     using SX = StageX<N>;
+    typedef float f4 __attribute__((ext_vector_type(4)));
     const int l = threadIdx.x & 63;
-    float w[N];  // column tacol(l) of W
+    const int i = l & 15;    // row of Lt this lane supplies (A operand)
+    const int c = tacol(l);  // column of W this lane supplies (B operand, reordered)
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-        const float4 t = *reinterpret_cast<const float4*>(slot + SX::BUF + tacol(l) * SX::LS + 4 * q);
-        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
+    for (int s = 0; s < N / 4; ++s) {
+        const int k = 4 * s + (l >> 4);
+        const float xik = slot[i * SX::LS + k];
+        const float xkc = slot[k * SX::LS + c];
+        const float ek = slot[SX::BUF + k];
+        const float a = k < i ? xik : (k == i ? 1.f : 0.f);
+        const float b = c > k ? ek * xkc : (c == k ? ek : 0.f);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const float* lrow = slot + trow(l, b) * SX::LS;
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < N / 4; ++q) {
-            const float4 t = *reinterpret_cast<const float4*>(lrow + 4 * q);
-            acc = fmaf(t.x, w[4 * q], acc);
-            acc = fmaf(t.y, w[4 * q + 1], acc);
-            acc = fmaf(t.z, w[4 * q + 2], acc);
-            acc = fmaf(t.w, w[4 * q + 3], acc);
-        }
-        o[b] = acc;
-    }
+    for (int r = 0; r < 4; ++r) o[r] = acc[r];
 }
 
 // Floats per token-parity slot of the forward from raw token vectors (0 otherwise).
@@ -344,7 +335,7 @@ __device__ inline void to_operand_x(float (&o)[4 * Stage<N>::NV], const float (&
                                     float* slot) {
     xop_stage<N>(v, slot);
     __syncthreads();
-    xop_factors<N>(v, slot);
+    xop_factors<N>(slot);
     __syncthreads();
     xop_read<N>(o, slot);
 }
@@ -389,39 +380,64 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_token<N>(ring[p], Mb + int64_t(min(p, len - 1)) * NN);
     float o[NA];  // operands of the next token to multiply
-    if constexpr (FX) to_operand_x<N>(o, ring[0], xlds);
-    else to_operand<N>(o, ring[0], tlds);
-    load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
+    if constexpr (FX) {
+        // Two deep: token t+1's operand is read at the start of step t from
+        // factors written (and fenced) during step t-1, and token t+2 is staged
+        // and factored during step t, so no LDS round trip waits in the step.
+        // The ring then holds tokens t+2 .. t+1+PF at the start of step t.
+        static_assert(PF >= 3, "two tokens ahead of the chain");
+        to_operand_x<N>(o, ring[0], xlds);
+        if (len > 1) {
+            float* x1 = xlds + xslot<N, FX>();
+            xop_stage<N>(ring[1], x1);
+            __syncthreads();
+            xop_factors<N>(x1);
+            __syncthreads();
+        }
+        load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
+        load_token<N>(ring[1], Mb + int64_t(min(PF + 1, len - 1)) * NN);
+    } else {
+        to_operand<N>(o, ring[0], tlds);
+        load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
+    }
     auto step = [&](int p, int t, bool refill) {
         typename F::aop_t a;
         operand_from<N>(a, o);
-        const int pn = (p + 1) % PF;  // ring slot of token t + 1
-        float* tb = tlds + ((t + 1) & 1) * Stage<N>::BUF;
-        float* xb = xlds + ((t + 1) & 1) * xslot<N, FX>();
-        // token t+1's operand goes through LDS while token t's products run
-        vec_t Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
-            if constexpr (FX) {
-                if (k == 0 && t + 1 < len) xop_stage<N>(ring[pn], xb);
-                if (k == 1 && t + 1 < len) {
-                    __syncthreads();
-                    xop_factors<N>(ring[pn], xb);
+        vec_t Xn;
+        if constexpr (FX) {
+            const int p2 = (p + 2) % PF;  // ring slot of token t + 2
+            float* x1 = xlds + ((t + 1) & 1) * xslot<N, FX>();
+            float* x2 = xlds + (t & 1) * xslot<N, FX>();  // token t + 2's slot
+            Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
+                if (k == 0 && t + 1 < len) xop_read<N>(o, x1);
+                if (k == 1 && t + 2 < len) xop_stage<N>(ring[p2], x2);
+                if (k == 2) {
+                    if (WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
+                    if (t + 2 < len) {
+                        __syncthreads();
+                        xop_factors<N>(x2);
+                    }
                 }
-                if (k == 2 && WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
-                if (k == 2 && t + 1 < len) {
+                if (k == 3 && t + 2 < len) {
                     __syncthreads();
-                    xop_read<N>(o, xb);
+                    if (refill) load_token<N>(ring[p2], Mb + int64_t(min(t + 2 + PF, len - 1)) * NN);
                 }
-            } else {
+            });
+        } else {
+            const int pn = (p + 1) % PF;  // ring slot of token t + 1
+            float* tb = tlds + ((t + 1) & 1) * Stage<N>::BUF;
+            // token t+1's operand goes through LDS while token t's products run
+            Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
                 if (k == 0 && t + 1 < len) operand_write<N>(ring[pn], tb);
                 if (k == 1 && t + 1 < len) {
                     __syncthreads();
                     operand_read<N>(o, tb);
                 }
                 if (k == 2 && WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
-            }
-            if (k == 3 && t + 1 < len && refill)
-                load_token<N>(ring[pn], Mb + int64_t(min(t + 1 + PF, len - 1)) * NN);
-        });
+                if (k == 3 && t + 1 < len && refill)
+                    load_token<N>(ring[pn], Mb + int64_t(min(t + 1 + PF, len - 1)) * NN);
+            });
+        }
         __builtin_amdgcn_sched_barrier(0);
         X = Xn;
         if constexpr (SC) renorm_acc<N>(X, ex);
@@ -461,6 +477,18 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
 #pragma unroll
         for (int e = 0; e < NA; ++e) buf[0][e] = o[e];
     }
+    if constexpr (FX && KR > 1) {
+        // two deep, as in fwd_sweep: token 1 is staged and factored before the
+        // first step, token t+2 during step t, token t+1's operand read in step t
+        static_assert(PF >= 3, "two tokens ahead of the chain");
+        if (len > 1) {
+            float* x1 = xlds + xslot<N, FX>();
+            xop_stage<N>(buf[1], x1);
+            __syncthreads();
+            xop_factors<N>(x1);
+            __syncthreads();
+        }
+    }
     // expanded at compile time (an index sequence, not the loop unroller: with
     // the forward from raw token vectors the body outgrows the unroller's size
     // limit, and a rolled loop would index buf, moving it to scratch memory)
@@ -477,17 +505,21 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
             vec_t Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
                 if constexpr (t + 1 < KR) {  // buf[t + 1] exists
                     if constexpr (FX) {
-                        if (k == 0 && next) xop_stage<N>(buf[t + 1], xb);
-                        if (k == 1 && next) {
-                            __syncthreads();
-                            xop_factors<N>(buf[t + 1], xb);
-                        }
-                        if (k == 2 && next) {
+                        if (k == 0 && next) {
                             float o[NA];
-                            __syncthreads();
                             xop_read<N>(o, xb);
 #pragma unroll
                             for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+                        }
+                        if constexpr (t + 2 < KR) {  // buf[t + 2] exists
+                            float* x2 = xlds + (t & 1) * xslot<N, FX>();
+                            const bool next2 = t + 2 < len;
+                            if (k == 1 && next2) xop_stage<N>(buf[t + 2], x2);
+                            if (k == 2 && next2) {
+                                __syncthreads();
+                                xop_factors<N>(x2);
+                            }
+                            if (k == 3 && next2) __syncthreads();
                         }
                     } else {
                         if (k == 0 && next) operand_write<N>(buf[t + 1], tb);
