@@ -19,7 +19,8 @@ never stored.  Prints ONE JSON line:
   unfused       the separate kernels (build x -> M, scan M -> P, backward from M,
                 and the build's own backward x, dM -> dx) timed alone, and the
                 layer backward x, P, dL/dP -> dL/dx in one pass (bwd_dx)
-  n16, n32      forward-scan throughput on the n=16 and n=32 workloads
+  n16, n32      forward-scan throughput on the n=16 and n=32 workloads (n16.from_x:
+                the same scan from the raw token vectors, and build then scan)
   n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload
   small         the two small workloads (one 1024-token n=4 sequence; the 8x8x256
                 n=8 step): launch-bound latencies
@@ -225,21 +226,34 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
     scale = torch.full((n, n), so, device="cuda")
     scale.fill_diagonal_(sd)
     x = (torch.randn((B, H, T, n, n), generator=g, device="cuda") * scale).reshape(B, H, T, n * n)
-    M = mpp.build_inputs(x.contiguous(), n)
-    del x
+    x = x.contiguous()
+    M = mpp.build_inputs(x, n)
     P = torch.empty_like(M)
     ws = torch.empty(max(mpp.workspace_bytes(B, H, T, n), 256), dtype=torch.uint8, device="cuda")
-    for _ in range(2):
-        mpp.scan_fwd(M, out=P, workspace=ws)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    ev[0].record()
-    for i in range(reps):
-        mpp.scan_fwd(M, out=P, workspace=ws)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
-    med = times[len(times) // 2]
+
+    def median_ms(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+        return times[len(times) // 2]
+
+    med = median_ms(lambda: mpp.scan_fwd(M, out=P, workspace=ws))
+    # the same scan from the raw token vectors (input matrices formed on chip), and
+    # the two-call path it replaces, where that exists for this n
+    from_x = None
+    if n in mpp.FUSED_FWD_N:
+        t_x = median_ms(lambda: mpp.scan_fwd_x(x, n, out=P, workspace=ws))
+        t_b = median_ms(lambda: mpp.build_inputs(x, n, out=M))
+        from_x = {"median_us": round(t_x * 1e3, 1), "build_then_scan_us": round((t_b + med) * 1e3, 1),
+                  "tokens_per_s": B * T / (t_x * 1e-3)}
+    del x
     S = B * H
     b = algorithmic_bytes("fwd", S, T, n)
     K, nch, Z, _ = mpp.scan_plan(B, H, T, n)
@@ -260,6 +274,7 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
         "matrix_tflops": round(impl_flops / (med * 1e-3) / 1e12, 2),
         "matrix_peak_tflops": peak,
         "matrix_util": round(impl_flops / (med * 1e-3) / 1e12 / peak, 4),
+        "from_x": from_x,
         "data": "synthetic, seeded on the GPU (torch.Generator), same scales as the workload",
     }
 
