@@ -494,10 +494,34 @@ class MRULayerFused(torch.autograd.Function):
         return scan_bwd_dx(x, P, dP.contiguous(), chunk=ctx.chunk), None, None
 
 
+class MRULayerFwdX(torch.autograd.Function):
+    """P = scan_fwd_x(x, n) (n in FUSED_FWD_N but not FUSED_N); the backward
+    rebuilds the input matrices from x, then scan_bwd and build_inputs_bwd.
+    Only x and P are kept between the passes."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, n: int, chunk: int = 0):
+        x = x.contiguous()
+        P = scan_fwd_x(x, n, chunk)
+        ctx.save_for_backward(x, P)
+        ctx.n, ctx.chunk = n, chunk
+        return P
+
+    @staticmethod
+    def backward(ctx, dP: torch.Tensor):
+        x, P = ctx.saved_tensors
+        M = build_inputs(x, ctx.n)
+        dM = scan_bwd(M, P, dP.contiguous(), ctx.chunk)
+        return build_inputs_bwd(x, dM), None, None
+
+
 def mru_layer(x: torch.Tensor, n: int, chunk: int = 0) -> torch.Tensor:
     """The MRU token mixer up to the output state matrices: x [B,H,T,n*n] ->
     P [B,H,T,n,n] (flatten() gives the output vectors), differentiable in x.
-    For n in FUSED_N the scans build the input matrices on chip."""
+    For n in FUSED_N both scans build the input matrices on chip; for the
+    other n in FUSED_FWD_N the forward does, and the backward rebuilds them."""
     if n in FUSED_N:
         return MRULayerFused.apply(x, n, chunk)
+    if n in FUSED_FWD_N:
+        return MRULayerFwdX.apply(x, n, chunk)
     return MRUScan.apply(MRUBuild.apply(x, n), chunk)
