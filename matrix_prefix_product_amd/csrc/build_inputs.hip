@@ -242,10 +242,10 @@ hipError_t run_build(const float* x, float* M, int64_t ntok, hipStream_t stream)
 #define MRU_BUILD_R8 1
 #endif
 #ifndef MRU_BUILD_R16
-#define MRU_BUILD_R16 2
+#define MRU_BUILD_R16 1
 #endif
 #ifndef MRU_BUILD_R32
-#define MRU_BUILD_R32 2
+#define MRU_BUILD_R32 1
 #endif
 
 hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream) {
