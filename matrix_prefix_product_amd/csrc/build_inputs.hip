@@ -222,6 +222,75 @@ hipError_t run_build_bwd(const float* x, const float* dM, float* dx, int64_t nto
     return hipGetLastError();
 }
 
+// n = 16, 32 on the matrix cores.  M = Lt W, Lt the unit lower factor and
+// W = diag(e) U, as fp32 16x16x4 products (v_mfma_f32_16x16x4f32: A[i][k] in
+// lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane j + 16(i/4), register
+// i%4); tile (I, J) sums the k-tiles K <= min(I, J) (the others are zero).  One
+// wave per token: the token is staged in LDS, its diagonal summed over a
+// 16-lane row with DPP (each lane adds N/16 entries first), e formed by lanes
+// 0..N-1, then every lane reads its operand entries of Lt and W.  The lanes of
+// a row read the same k; everything else is registers.
+__device__ inline float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+template <int N>
+__global__ __launch_bounds__(64) void build_mfma_kernel(const float* __restrict__ x,
+                                                       float* __restrict__ M, int64_t ntok) {
+    static_assert(N == 16 || N == 32, "matrix-core build for n = 16, 32");
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int NT = N / 16;
+    constexpr int NN = N * N;
+    constexpr int LS = N + 4;       // LDS row stride (floats)
+    constexpr int NV = NN / 256;    // float4 pieces per lane and token
+    __shared__ __align__(16) float xs[N * LS];
+    __shared__ float es[N];
+    const int l = threadIdx.x;
+    for (int64_t tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
+        float4 v[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) v[q] = reinterpret_cast<const float4*>(x + tok * NN)[q * 64 + l];
+        __syncthreads();  // the previous token's reads are done
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int f = q * 64 + l;
+            *reinterpret_cast<float4*>(xs + (f / (N / 4)) * LS + 4 * (f % (N / 4))) = v[q];
+        }
+        __syncthreads();
+        float dsum = 0.f;
+#pragma unroll
+        for (int m = 0; m < NT; ++m) dsum += xs[((l & 15) + 16 * m) * (LS + 1)];
+        const float mean = row16_sum(dsum) * (1.0f / N);  // exact scaling by 1/n
+        if (l < N) es[l] = expf(xs[l * (LS + 1)] - mean);
+        __syncthreads();
+        float* out = M + tok * NN;
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int i = 16 * I + (l & 15);
+                const int j = 16 * J + (l & 15);
+#pragma unroll
+                for (int K = 0; K <= (I < J ? I : J); ++K)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int k = 16 * K + 4 * s4 + (l >> 4);
+                        const float a = k < i ? xs[i * LS + k] : (k == i ? 1.f : 0.f);
+                        const float ek = es[k];
+                        const float b = j > k ? ek * xs[k * LS + j] : (j == k ? ek : 0.f);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+                    }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(16 * I + 4 * (l >> 4) + r) * N + j] = acc[r];
+            }
+    }
+}
+
 template <int N, int R>
 hipError_t run_build(const float* x, float* M, int64_t ntok, hipStream_t stream) {
     constexpr int TPI = kBuildThreads / (N / R);
@@ -233,6 +302,14 @@ hipError_t run_build(const float* x, float* M, int64_t ntok, hipStream_t stream)
 }
 
 }  // namespace
+
+template <int N>
+hipError_t run_build_mfma(const float* x, float* M, int64_t ntok, hipStream_t stream) {
+    int64_t blocks = ntok;
+    if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride beyond 64 waves per CU
+    hipLaunchKernelGGL((build_mfma_kernel<N>), dim3(unsigned(blocks)), dim3(64), 0, stream, x, M, ntok);
+    return hipGetLastError();
+}
 
 // Rows per lane for each n (overridable at build time for tuning sweeps).
 #ifndef MRU_BUILD_R4
@@ -252,8 +329,8 @@ hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream
     switch (n) {
         case 4: return run_build<4, MRU_BUILD_R4>(x, M, ntok, stream);
         case 8: return run_build<8, MRU_BUILD_R8>(x, M, ntok, stream);
-        case 16: return run_build<16, MRU_BUILD_R16>(x, M, ntok, stream);
-        case 32: return run_build<32, MRU_BUILD_R32>(x, M, ntok, stream);
+        case 16: return run_build_mfma<16>(x, M, ntok, stream);
+        case 32: return run_build_mfma<32>(x, M, ntok, stream);
         default: return hipErrorInvalidValue;
     }
 }
