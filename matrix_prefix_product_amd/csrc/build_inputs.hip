@@ -7,8 +7,10 @@
 //   c = |det(L D U)|^(-1/n) = exp(-mean_i X_ii)     (det L = det U = 1),
 //   M = c L D U = L diag(e) U  with  e_k = exp(X_kk - mean_i X_ii),
 // so  M_ij = sum_{k <= min(i, j)} L_ik e_k U_kj.
-// Elementwise over tokens: a group of n/R lanes builds one token, each lane R
-// rows of M, from the token staged in LDS.  HBM-bound (8 n^2 bytes per token).
+// Elementwise over tokens.  n = 4, 8: a group of n/R lanes builds one token,
+// each lane R rows of M, from the token staged in LDS; n = 16, 32: one wave per
+// token on the matrix cores (build_mfma_kernel).  HBM-bound (8 n^2 bytes per
+// token).
 #include <type_traits>
 
 #include "mru_build.h"
@@ -311,18 +313,13 @@ hipError_t run_build_mfma(const float* x, float* M, int64_t ntok, hipStream_t st
     return hipGetLastError();
 }
 
-// Rows per lane for each n (overridable at build time for tuning sweeps).
+// Rows per lane of the vector-ALU build (n = 4, 8; overridable at build time for
+// tuning sweeps).
 #ifndef MRU_BUILD_R4
 #define MRU_BUILD_R4 1
 #endif
 #ifndef MRU_BUILD_R8
 #define MRU_BUILD_R8 1
-#endif
-#ifndef MRU_BUILD_R16
-#define MRU_BUILD_R16 1
-#endif
-#ifndef MRU_BUILD_R32
-#define MRU_BUILD_R32 1
 #endif
 
 hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream) {
