@@ -305,6 +305,130 @@ hipError_t run_build(const float* x, float* M, int64_t ntok, hipStream_t stream)
 
 }  // namespace
 
+// Its gradient at n = 16, 32 on the matrix cores, one wave per token.  With
+// G = dL/dM, H = G U^T and (L^T G) as fp32 16x16x4 products (only the k-tiles
+// where the triangular factor is nonzero), every lane holds entries (i, j) of
+// both in the accumulator layout and writes
+//   dX_ij = e_j H_ij (i > j),  e_i (L^T G)_ij (i < j),  e_i g_i - mean_k e_k g_k (i = j),
+// g_i = sum_j (L^T G)_ij U_ij: a 16-lane DPP sum per accumulator row (lanes of
+// a DPP row hold one row of a tile), and the mean over the four lane rows
+// through LDS, added in a fixed order.
+template <int N>
+__global__ __launch_bounds__(64) void build_bwd_mfma_kernel(const float* __restrict__ x,
+                                                           const float* __restrict__ dM,
+                                                           float* __restrict__ dx, int64_t ntok) {
+    static_assert(N == 16 || N == 32, "matrix-core build backward for n = 16, 32");
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int NT = N / 16;
+    constexpr int NN = N * N;
+    constexpr int LS = N + 4;
+    constexpr int NV = NN / 256;
+    __shared__ __align__(16) float xs[N * LS];
+    __shared__ __align__(16) float gs[N * LS];
+    __shared__ float es[N];
+    __shared__ float part[4];
+    const int l = threadIdx.x;
+    const int m = l >> 4;  // lane row: accumulator rows 4m .. 4m+3 of each tile
+    for (int64_t tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
+        float4 vx[NV], vg[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            vx[q] = reinterpret_cast<const float4*>(x + tok * NN)[q * 64 + l];
+            vg[q] = reinterpret_cast<const float4*>(dM + tok * NN)[q * 64 + l];
+        }
+        __syncthreads();  // the previous token's reads are done
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int f = q * 64 + l;
+            const int off = (f / (N / 4)) * LS + 4 * (f % (N / 4));
+            *reinterpret_cast<float4*>(xs + off) = vx[q];
+            *reinterpret_cast<float4*>(gs + off) = vg[q];
+        }
+        __syncthreads();
+        float dsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dsum += xs[((l & 15) + 16 * t) * (LS + 1)];
+        const float mean = row16_sum(dsum) * (1.0f / N);
+        if (l < N) es[l] = expf(xs[l * (LS + 1)] - mean);
+        __syncthreads();
+        f4 h[NT][NT], u[NT][NT];  // H and L^T G, accumulator layout
+        float eg = 0.f;           // sum over this lane row's diagonal entries of e_i g_i
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+                const int i = 16 * I + (l & 15);  // A-operand row
+                const int j = 16 * J + (l & 15);  // B-operand column
+                f4 ah = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int K = J; K < NT; ++K)  // H = G U^T: U[j][k] = 0 for k < j
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int k = 16 * K + 4 * s4 + m;
+                        const float a = gs[i * LS + k];
+                        const float b = k > j ? xs[j * LS + k] : (k == j ? 1.f : 0.f);
+                        ah = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, ah, 0, 0, 0);
+                    }
+#pragma unroll
+                for (int K = I; K < NT; ++K)  // L^T G: L[k][i] = 0 for k < i
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int k = 16 * K + 4 * s4 + m;
+                        const float a = k > i ? xs[k * LS + i] : (k == i ? 1.f : 0.f);
+                        const float b = gs[k * LS + j];
+                        au = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, au, 0, 0, 0);
+                    }
+                h[I][J] = ah;
+                u[I][J] = au;
+            }
+        // g_i for this lane row's rows i = 16I + 4m + r
+        float g[NT][4];
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * m + r;
+                float p = 0.f;
+#pragma unroll
+                for (int J = 0; J < NT; ++J) {
+                    const int j = 16 * J + (l & 15);
+                    const float uij = j > i ? xs[i * LS + j] : (j == i ? 1.f : 0.f);
+                    p = fmaf(u[I][J][r], uij, p);
+                }
+                g[I][r] = row16_sum(p);
+                eg += es[i] * g[I][r];
+            }
+        if ((l & 15) == 0) part[m] = eg;
+        __syncthreads();
+        const float meaneg = (((part[0] + part[1]) + part[2]) + part[3]) * (1.0f / N);
+        float* out = dx + tok * NN;
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int J = 0; J < NT; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * m + r;
+                    const int j = 16 * J + (l & 15);
+                    float v;
+                    if (i > j) v = es[j] * h[I][J][r];
+                    else if (i < j) v = es[i] * u[I][J][r];
+                    else v = es[i] * g[I][r] - meaneg;
+                    out[i * N + j] = v;
+                }
+    }
+}
+
+template <int N>
+hipError_t run_build_bwd_mfma(const float* x, const float* dM, float* dx, int64_t ntok,
+                              hipStream_t stream) {
+    int64_t blocks = ntok;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    hipLaunchKernelGGL((build_bwd_mfma_kernel<N>), dim3(unsigned(blocks)), dim3(64), 0, stream, x, dM,
+                       dx, ntok);
+    return hipGetLastError();
+}
+
 template <int N>
 hipError_t run_build_mfma(const float* x, float* M, int64_t ntok, hipStream_t stream) {
     int64_t blocks = ntok;
@@ -337,8 +461,8 @@ hipError_t launch_build_bwd(const float* x, const float* dM, float* dx, int64_t 
     switch (n) {
         case 4: return run_build_bwd<4>(x, dM, dx, ntok, stream);
         case 8: return run_build_bwd<8>(x, dM, dx, ntok, stream);
-        case 16: return run_build_bwd<16>(x, dM, dx, ntok, stream);
-        case 32: return run_build_bwd<32>(x, dM, dx, ntok, stream);
+        case 16: return run_build_bwd_mfma<16>(x, dM, dx, ntok, stream);
+        case 32: return run_build_bwd_mfma<32>(x, dM, dx, ntok, stream);
         default: return hipErrorInvalidValue;
     }
 }
