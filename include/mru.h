@@ -180,12 +180,12 @@ mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t 
  * mru_scan_fwd in one pass that reads x once and writes P once.  No input
  * state matrix is stored.  For n in {4, 8} each step multiplies the running
  * state by the LDU factors in turn (L, then diag(e), then U, same cost as a
- * dense product); for n = 16 each token's matrix is formed on chip, in fp32
- * as by mru_build_inputs (as the unit lower factor times diag(e) U), and fed
- * to the same fp64 chain as mru_scan_fwd.  Results agree with the two-call
+ * dense product); for n = 16, 32 each token's matrix is formed on chip, in
+ * fp32 as by mru_build_inputs (as the unit lower factor times diag(e) U), and
+ * fed to the same fp64 chain as mru_scan_fwd.  Results agree with the two-call
  * path up to rounding order.  Arguments as for mru_scan_fwd with x
- * ([B][H][T][n*n]) in place of M; x and P must not overlap.  n in {4, 8, 16};
- * n = 32 returns MRU_ERR_SHAPE.
+ * ([B][H][T][n*n]) in place of M; x and P must not overlap.  n in {4, 8, 16,
+ * 32}.
  */
 mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
                           int32_t chunk, void* ws, size_t ws_bytes, void* stream);
@@ -233,7 +233,7 @@ mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float
  *   P_t = P_0 M_1 ... M_t,   P_0 = 2^carry_exp[b][h] * carry[b][h]  (t = 1..T).
  *
  * in         M [B][H][T][n][n], or x [B][H][T][n*n] when from_x != 0 (then
- *            n in {4, 8, 16}, as mru_scan_fwd_x).
+ *            any n, as mru_scan_fwd_x).
  * carry      [B][H][n][n] fp32, 16-byte aligned, or NULL for P_0 = I.
  * carry_exp  [B][H] int32, or NULL for exponents 0.
  * P          [B][H][T][n][n] fp32, written.

@@ -35,7 +35,7 @@ DIR_BWD = 1
 SUPPORTED_N = (4, 8, 16, 32)
 # Sizes whose forward scan can start from raw token vectors (input matrices
 # built on chip), and sizes whose backward scans can too (FUSED_N).
-FUSED_FWD_N = (4, 8, 16)
+FUSED_FWD_N = (4, 8, 16, 32)
 FUSED_N = (4, 8)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmru.so")

@@ -237,7 +237,6 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
                          const ScanCarry& cy) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
-    if (from_x && n > 16) return MRU_ERR_SHAPE;  // the n = 32 scan reads M
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P) return MRU_ERR_NULL;

@@ -35,7 +35,7 @@ struct ScanCarry {
 // sequence (possibly padded with empty chunks), supers of Z chunks.  nch == 1
 // runs without workspace; nch > 1 needs a cleared workspace header and flags.
 // from_x: the first array holds raw token vectors and the kernel builds the
-// input matrices on the fly (never writing them); forward n = 4, 8, 16,
+// input matrices on the fly (never writing them); forward n = 4, 8, 16, 32,
 // backward n = 4, 8.  to_dx (backward, with
 // from_x): the output is dL/dx, the gradient through the build, instead of dL/dM.
 hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,

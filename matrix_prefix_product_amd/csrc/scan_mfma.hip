@@ -245,7 +245,7 @@ __device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4
         a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(o[e]);
 }
 
-// Forward from raw token vectors (n = 16): the operand entries of M_t^T are
+// Forward from raw token vectors (n = 16, 32): the operand entries of M_t^T are
 // formed from the staged x_t instead of read.  With X = x_t viewed row-major,
 // M = Lt W where Lt is the unit lower factor (Lt_ik = X_ik for k < i, 1 on the
 // diagonal) and W = diag(e) U (W_kc = e_k X_kc for k < c, e_k on the diagonal),
@@ -253,8 +253,8 @@ __device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4
 // Attention Alternative", Key Points: LDU fill, determinant-correcting
 // scalar).  The product runs on the matrix core in fp32 (four
 // v_mfma_f32_16x16x4f32, D[i][j] in lane j + 16(i/4), register i%4): taking
-// W's columns in the order tacol, lane l's four results are exactly its
-// A-operand entries M[trow(l, b)][tacol(l)] of the fp64 chain.  Three phases,
+// W's columns in the order tacol, lane l's results are exactly its A-operand
+// entries M[16K + trow(l, b)][16I + tacol(l)] of the fp64 chain.  Three phases,
 // separated by barriers and spread between the chain's products:
 //   stage:   every lane writes its 16-byte piece of X row-major to the slot;
 //   factors: every lane reads X_kk for k = l%16, sums the 16 over its row of
@@ -266,7 +266,7 @@ __device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4
 // A slot (X, e) per token parity, as the transpose buffers.
 template <int N>
 struct StageX {
-    static_assert(N == 16, "the forward from raw token vectors is built for n = 16");
+    static_assert(N == 16 || N == 32, "the forward from raw token vectors: n = 16, 32");
     static constexpr int LS = Stage<N>::LS;
     static constexpr int BUF = Stage<N>::BUF;
     static constexpr int SLOT = BUF + N;  // floats: X (row stride LS), e
@@ -276,8 +276,12 @@ template <int N>
 __device__ inline void xop_stage(const float (&v)[4 * Stage<N>::NV], float* slot) {
     using SX = StageX<N>;
     const int l = threadIdx.x & 63;
-    // n = 16: one piece per lane, row l/4, columns 4(l%4) .. 4(l%4)+3
-    *reinterpret_cast<float4*>(slot + (l >> 2) * SX::LS + 4 * (l & 3)) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+    for (int q = 0; q < Stage<N>::NV; ++q) {
+        const int f = q * 64 + l;  // float4 index within the token, as load_token
+        *reinterpret_cast<float4*>(slot + (f / (N / 4)) * SX::LS + 4 * (f % (N / 4))) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
 }
 
 // Sum over each row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -293,33 +297,48 @@ __device__ inline float row16_sum(float v) {
 template <int N>
 __device__ inline void xop_factors(float* slot) {
     using SX = StageX<N>;
+    constexpr int NT = N / 16;
     const int l = threadIdx.x & 63;
-    const float dk = slot[(l & 15) * (SX::LS + 1)];  // X_kk, k = l % 16
-    const float mean = row16_sum(dk) * (1.0f / N);  // exact scaling by 1/16
-    const float ek = expf(dk - mean);
+    float dsum = 0.f;  // X_kk for k = l%16 (+ 16, n = 32)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dsum += slot[((l & 15) + 16 * t) * (SX::LS + 1)];
+    const float mean = row16_sum(dsum) * (1.0f / N);  // exact scaling by 1/n
+    const int k = l & (N - 1);
+    const float ek = expf(slot[k * (SX::LS + 1)] - mean);
     if (l < N) slot[SX::BUF + l] = ek;
 }
 
+// Operand entries o[(I * NT + K) * 4 + b] = M[16K + trow(l, b)][16I + tacol(l)]:
+// output tile (K, I) of Lt W with W's columns in the order tacol, summing the
+// k-tiles T <= min(K, I) (the others are zero).
 template <int N>
 __device__ inline void xop_read(float (&o)[4 * Stage<N>::NV], const float* slot) {
     using SX = StageX<N>;
+    constexpr int NT = N / 16;
     typedef float f4 __attribute__((ext_vector_type(4)));
     const int l = threadIdx.x & 63;
-    const int i = l & 15;    // row of Lt this lane supplies (A operand)
-    const int c = tacol(l);  // column of W this lane supplies (B operand, reordered)
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < N / 4; ++s) {
-        const int k = 4 * s + (l >> 4);
-        const float xik = slot[i * SX::LS + k];
-        const float xkc = slot[k * SX::LS + c];
-        const float ek = slot[SX::BUF + k];
-        const float a = k < i ? xik : (k == i ? 1.f : 0.f);
-        const float b = c > k ? ek * xkc : (c == k ? ek : 0.f);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-    }
+    for (int I = 0; I < NT; ++I)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = acc[r];
+        for (int K = 0; K < NT; ++K) {
+            const int i = 16 * K + (l & 15);  // row of Lt this lane supplies (A operand)
+            const int c = 16 * I + tacol(l);  // column of W this lane supplies (B operand)
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int T = 0; T <= (K < I ? K : I); ++T)
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int k = 16 * T + 4 * s4 + (l >> 4);
+                    const float xik = slot[i * SX::LS + k];
+                    const float xkc = slot[k * SX::LS + c];
+                    const float ek = slot[SX::BUF + k];
+                    const float a = k < i ? xik : (k == i ? 1.f : 0.f);
+                    const float b = c > k ? ek * xkc : (c == k ? ek : 0.f);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[(I * NT + K) * 4 + r] = acc[r];
+        }
 }
 
 // Floats per token-parity slot of the forward from raw token vectors (0 otherwise).
@@ -969,7 +988,10 @@ hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n
         if (retain) return run_fwd<16, MRU_PF16, kRetain16, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
         return run_fwd<16, MRU_PF16, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
-    if (n == 32 && !from_x) return run_fwd<32, 4, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
+    if (n == 32) {
+        if (from_x) return run_fwd<32, 4, 0, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd<32, 4, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -128,8 +128,7 @@ def test_fused_entries_validate_before_any_launch(mpp):
     lib = mpp.load_library()
     nul = ctypes.c_void_p(0)
     a, b, c, d = (ctypes.c_void_p(v) for v in (0x100000, 0x200000, 0x300000, 0x400000))
-    # the forward starts from token vectors for n = 4, 8, 16, the backward for n = 4, 8
-    assert lib.mru_scan_fwd_x(a, b, 1, 1, 16, 32, 0, nul, 0, nul) == 2
+    # the forward starts from token vectors for every n, the backward for n = 4, 8
     assert lib.mru_scan_bwd_x(a, b, c, d, 1, 1, 16, 16, 0, nul, 0, nul) == 2
     assert lib.mru_scan_bwd_x(a, b, c, d, 1, 1, 16, 32, 0, nul, 0, nul) == 2
     assert lib.mru_scan_fwd_x(a, b, 1, 1, 16, 6, 0, nul, 0, nul) == 2
@@ -156,8 +155,8 @@ def test_extended_entries_validate_before_any_launch(mpp):
                                nul, 0, nul) == 4
     assert lib.mru_scan_fwd_ex(a, 0, ctypes.c_void_p(0x200000 + 256), nul, b, nul, 1, 1, 8, 8,
                                1 << 20, nul, 0, nul) == 4
-    # from_x: forward n = 4, 8, 16, backward n = 4, 8; empty is a no-op
-    assert lib.mru_scan_fwd_ex(a, 1, nul, nul, b, nul, 1, 1, 8, 32, 0, nul, 0, nul) == 2
+    # from_x: forward every n, backward n = 4, 8; empty is a no-op
+    assert lib.mru_scan_fwd_ex(a, 1, nul, nul, b, nul, 1, 1, 8, 6, 0, nul, 0, nul) == 2
     assert lib.mru_scan_bwd_ex(a, 1, nul, b, c, d, nul, 1, 1, 8, 16, 0, nul, 0, nul) == 2
     assert lib.mru_scan_fwd_ex(nul, 0, c, nul, nul, nul, 1, 1, 0, 8, 0, nul, 0, nul) == 0
     # backward: dcarry overlapping dM or the carry, misaligned dcarry

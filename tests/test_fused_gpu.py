@@ -19,7 +19,7 @@ from workloads import gen_R, gen_x
 
 pytestmark = pytest.mark.gpu
 
-SIGMA = {4: (0.1, 0.05), 8: (0.1, 0.05), 16: (0.05, 0.02)}
+SIGMA = {4: (0.1, 0.05), 8: (0.1, 0.05), 16: (0.05, 0.02), 32: (0.02, 0.01)}
 
 CASES = [
     (4, 1, 1, 1024, 0), (4, 3, 2, 203, 3), (4, 2, 2, 97, 1), (4, 5, 1, 120, 120),
@@ -228,35 +228,35 @@ def test_fused_layer_autograd(mpp, n):
 
 
 def test_fused_rejects_matrix_core_sizes(mpp):
-    # the forward from x covers n = 4, 8, 16, the backward n = 4, 8
-    x = torch.zeros(1, 1, 4, 1024, device="cuda")
-    with pytest.raises(ValueError):
-        mpp.scan_fwd_x(x, 32)
-    lib = mpp.load_library()
-    P = torch.empty(1, 1, 4, 32, 32, device="cuda")
+    # the forward from x covers every n, the backward n = 4, 8
     import ctypes
-    st = lib.mru_scan_fwd_x(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(P.data_ptr()),
-                            1, 1, 4, 32, 0, None, 0, None)
-    assert st == 2
-    x16 = torch.zeros(1, 1, 4, 256, device="cuda")
-    P16 = torch.zeros(1, 1, 4, 16, 16, device="cuda")
-    with pytest.raises(ValueError):
-        mpp.scan_bwd_x(x16, P16, P16)
+    lib = mpp.load_library()
+    for n in (16, 32):
+        x = torch.zeros(1, 1, 4, n * n, device="cuda")
+        P = torch.zeros(1, 1, 4, n, n, device="cuda")
+        with pytest.raises(ValueError):
+            mpp.scan_bwd_x(x, P, P)
+        with pytest.raises(ValueError):
+            mpp.scan_bwd_dx(x, P, P)
+        st = lib.mru_scan_bwd_x(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(P.data_ptr()),
+                                ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(x.data_ptr() + 4096),
+                                1, 1, 4, n, 0, None, 0, None)
+        assert st == 2
 
 
-# n = 16 from raw token vectors: every plan shape of the matrix-core forward --
-# one chunk per sequence (streamed), register-retained chunks (auto plan, a
-# ragged forced chunk, exactly 64 tokens), streamed chunks longer than the
-# register buffer, a single token
-N16_CASES = [(128, 16, 40, 0), (4, 4, 1000, 0), (2, 3, 203, 5), (2, 2, 130, 64),
-             (1, 2, 300, 100), (3, 1, 1, 0)]
+# n = 16, 32 from raw token vectors: every plan shape of the matrix-core
+# forward -- one chunk per sequence (streamed), register-retained chunks (n = 16:
+# auto plan, a ragged forced chunk, exactly 64 tokens), streamed chunks (longer
+# than the register buffer; every n = 32 chunk), a single token
+N16_CASES = [(16, 128, 16, 40, 0), (16, 4, 4, 1000, 0), (16, 2, 3, 203, 5), (16, 2, 2, 130, 64),
+             (16, 1, 2, 300, 100), (16, 3, 1, 1, 0),
+             (32, 64, 16, 12, 0), (32, 1, 4, 700, 0), (32, 2, 1, 301, 37), (32, 2, 1, 1, 0)]
 
 
-@pytest.mark.parametrize("B,H,T,chunk", N16_CASES)
-def test_fused_fwd_n16(mpp, B, H, T, chunk):
-    n = 16
+@pytest.mark.parametrize("n,B,H,T,chunk", N16_CASES)
+def test_fused_fwd_n16(mpp, n, B, H, T, chunk):
     plan = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD, chunk)
-    say(f"[fused fwd n=16] B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    say(f"[fused fwd n={n}] B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
     x = _x(B, H, T, n, seed=T + 7)
     xd = dev(x)
     P = mpp.scan_fwd_x(xd, n, chunk)
@@ -273,11 +273,11 @@ def test_fused_fwd_n16(mpp, B, H, T, chunk):
     assert d.max() <= FWD_TOL
 
 
-@pytest.mark.parametrize("chunk", [0, 9, 100])
-def test_fused_fwd_n16_carry_and_scaled(mpp, chunk):
+@pytest.mark.parametrize("n,chunk", [(16, 0), (16, 9), (16, 100), (32, 0), (32, 21)])
+def test_fused_fwd_n16_carry_and_scaled(mpp, n, chunk):
     # a carried-in state, and the scaled form: 2^E * P~ carries the plain scan's
     # bits (exact powers of two), both graded against the oracle
-    n, B, H, T = 16, 2, 2, 400
+    B, H, T = 2, 2, 400
     x = _x(B, H, T, n, seed=11)
     rng = np.random.default_rng(4)
     C = (np.eye(n) + 0.1 * rng.standard_normal((B, H, n, n))).astype(np.float32)
@@ -288,15 +288,16 @@ def test_fused_fwd_n16_carry_and_scaled(mpp, chunk):
     assert np.array_equal(np.ldexp(Pm, E[..., None, None]).astype(np.float32), P)
     ref = scan_ref(build_ref(x, n), C.astype(np.float64))
     err = rel_fro_err(np.ldexp(Pm.astype(np.float64), E[..., None, None]), ref)
-    say(f"[fused fwd n=16 carry, scaled] chunk={chunk}: max {err.max():.3e}")
+    say(f"[fused fwd n={n} carry, scaled] chunk={chunk}: max {err.max():.3e}")
     assert err.max() <= FWD_TOL
     _, E_ref = scaled_ref(ref)
     assert np.abs(E - E_ref).max() <= 1
 
 
-def test_fused_fwd_n16_zero_input_is_identity(mpp):
+@pytest.mark.parametrize("n", [16, 32])
+def test_fused_fwd_n16_zero_input_is_identity(mpp, n):
     # x = 0: mean 0, e = 1, both factors I, so every token matrix and prefix is I exactly
-    n, T = 16, 150
+    T = 150
     xd = torch.zeros(2, 2, T, n * n, device="cuda")
     for chunk in (0, 7, 100):
         P = host(mpp.scan_fwd_x(xd, n, chunk))
