@@ -19,8 +19,8 @@ never stored.  Prints ONE JSON line:
   unfused       the separate kernels (build x -> M, scan M -> P, backward from M,
                 and the build's own backward x, dM -> dx) timed alone, and the
                 layer backward x, P, dL/dP -> dL/dx in one pass (bwd_dx)
-  n16, n32      forward-scan throughput on the n=16 and n=32 workloads (n16.from_x:
-                the same scan from the raw token vectors, and build then scan)
+  n16, n32      forward-scan throughput on the n=16 and n=32 workloads (from_x: the
+                same scan from the raw token vectors, and build then scan)
   n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload
   small         the two small workloads (one 1024-token n=4 sequence; the 8x8x256
                 n=8 step): launch-bound latencies
