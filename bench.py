@@ -21,7 +21,9 @@ never stored.  Prints ONE JSON line:
                 layer backward x, P, dL/dP -> dL/dx in one pass (bwd_dx)
   n16, n32      forward-scan throughput on the n=16 and n=32 workloads (from_x: the
                 same scan from the raw token vectors, and build then scan)
-  n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload
+  n16_fwd_bwd   forward and backward scans on the n=16 forward+backward workload,
+                and its layer step from the raw token vectors (forward x -> P,
+                one-pass backward to dL/dx) against the three-kernel backward
   small         the two small workloads (one 1024-token n=4 sequence; the 8x8x256
                 n=8 step): launch-bound latencies
   next          the scaled forward, the orthogonal input builds and a
@@ -60,10 +62,17 @@ COUNTED_SOURCES = ("mru_api.hip", "mru_build.h", "mru_device.h", "mru_kernels.h"
                    "build_inputs.hip", "scan_valu.hip")
 
 
-def source_hash() -> str:
+# The sources of the matrix-core kernels (n = 16, 32) whose counted utilisation
+# profiles/mfma_util.json records.
+MFMA_SOURCES = ("mru_api.hip", "mru_build.h", "mru_device.h", "mru_kernels.h", "mru_mfma.h",
+                "build_inputs.hip", "scan_mfma.hip")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
+
+
+def source_hash(files=COUNTED_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
-    for p in sorted(os.path.join(csrc, f) for f in COUNTED_SOURCES):
+    for p in sorted(os.path.join(csrc, f) for f in files):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -71,17 +80,23 @@ def source_hash() -> str:
 
 
 def algorithmic_bytes(kind: str, S: int, T: int, n: int) -> int:
-    # bytes per matrix entry per token-head (4-byte entries): build reads x and
-    # writes M, forward reads M (or x) and writes P, build backward reads x and
-    # dM and writes dx.  The backward reads M (or x) and dP and writes dM; for
-    # n <= 8 it reads one stored prefix per 4 tokens (recomputing the others),
-    # 13 bytes in all, for n = 16, 32 every prefix, 16.  The layer backward
-    # (bwd_dx, n <= 8) reads x, dP and one prefix in four and writes dx: 13.
+    # Algorithmic bytes per matrix entry per token-head (4-byte entries), the
+    # definition's own traffic: build reads x and writes M, forward reads M (or
+    # x) and writes P, backward reads M (or x), P and dP and writes dM (or dx),
+    # build backward reads x and dM and writes dx.
     per = {"build": 8, "fwd": 8, "bwd": 16, "fwd_x": 8, "bwd_x": 16, "build_bwd": 12,
-           "bwd_dx": 13}[kind]
-    if kind in ("bwd", "bwd_x") and n <= 8:
-        per = 13
+           "bwd_dx": 16}[kind]
     return per * n * n * S * T
+
+
+def design_bytes(kind: str, S: int, T: int, n: int) -> int:
+    # The bytes a kernel moves by design, where that is less than the
+    # algorithmic count: for n <= 8 the backwards from raw token vectors (bwd_x,
+    # bwd_dx) read one stored prefix per 4 tokens and recompute the others, 13
+    # bytes per entry instead of 16.
+    if kind in ("bwd_x", "bwd_dx") and n <= 8:
+        return 13 * n * n * S * T
+    return algorithmic_bytes(kind, S, T, n)
 
 
 def algorithmic_flops(kind: str, S: int, T: int, n: int) -> int:
@@ -101,6 +116,32 @@ def load_traffic(workload: str, kernel: str):
     if not k:
         return None
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def load_mfma_util(workload: str, kernel: str):
+    """Matrix-core utilisation counted by rocprofv3 (SQ_VALU_MFMA_BUSY_CYCLES
+    over GRBM_GUI_ACTIVE x 1024 SIMDs) for this workload's kernel, when the
+    record was taken on the current matrix-core sources; else None."""
+    try:
+        rec = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(MFMA_SOURCES):
+        return None
+    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if not k else k
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), read before the GPU is touched."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 # Batch rows of the timed workload whose GPU outputs the host leg checks
@@ -177,6 +218,7 @@ def cpu_leg(w, budget_s: float, max_workers: int = 16):
         "value": head_tokens / w.H / dt,
         "unit": "tokens/s",
         "cores": 1,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{nb} batch rows x {w.H} heads x {T} tokens of {w.name} (fp64 numpy build_ref + "
                   f"scan_ref + bwd_ref, {dt:.1f} s, BLAS limited to 1 thread)",
@@ -185,6 +227,7 @@ def cpu_leg(w, budget_s: float, max_workers: int = 16):
             "value": head_tokens / w.H / dt_par,
             "unit": "tokens/s",
             "cores": workers,
+            "cpu_model": cpu_model(),
             "sample": f"the same sample split over {workers} forked processes by batch rows, "
                       f"one BLAS thread each, {dt_par:.2f} s wall",
         },
@@ -209,14 +252,31 @@ def cpu_parity(ref, gpu):
 
 def kernel_record(kind, avg_ms, S, T, n, workload):
     b = algorithmic_bytes(kind, S, T, n)
+    d = design_bytes(kind, S, T, n)
     gbs = b / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(workload, kind)
     return {
         "avg_us": round(avg_ms * 1e3, 2),
         "algorithmic_bytes": b,
         "achieved_GBs": round(gbs, 1),
         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-        "traffic": load_traffic(workload, kind),
+        "design_bytes": d,
+        "frac_hbm_design": round(d / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "frac_hbm_traffic": (None if traffic is None else
+                             round(traffic / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
     }
+
+
+def ws_ok(mpp, ws, B, H, T, n, direction):
+    """The status word of the last scan on ws is 0 (plans with a workspace only);
+    exits if a look-back wait timed out, since the timed outputs are invalid."""
+    if mpp.workspace_bytes(B, H, T, n, direction) == 0:
+        return True
+    st = mpp.ws_status(ws)
+    if st != 0:
+        sys.exit(f"a look-back wait timed out (status {st}) on B={B} H={H} T={T} n={n}")
+    return True
 
 
 def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
@@ -245,14 +305,19 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
         return times[len(times) // 2]
 
     med = median_ms(lambda: mpp.scan_fwd(M, out=P, workspace=ws))
+    ws_ok(mpp, ws, B, H, T, n, mpp.DIR_FWD)
     # the same scan from the raw token vectors (input matrices formed on chip), and
     # the two-call path it replaces, where that exists for this n
     from_x = None
     if n in mpp.FUSED_FWD_N:
         t_x = median_ms(lambda: mpp.scan_fwd_x(x, n, out=P, workspace=ws))
+        ws_ok(mpp, ws, B, H, T, n, mpp.DIR_FWD)
         t_b = median_ms(lambda: mpp.build_inputs(x, n, out=M))
         from_x = {"median_us": round(t_x * 1e3, 1), "build_then_scan_us": round((t_b + med) * 1e3, 1),
-                  "tokens_per_s": B * T / (t_x * 1e-3)}
+                  "build_us": round(t_b * 1e3, 1),
+                  "tokens_per_s": B * T / (t_x * 1e-3),
+                  "matrix_util_counted": load_mfma_util(name, "fwd_x"),
+                  "build_matrix_util_counted": load_mfma_util(name, "build")}
     del x
     S = B * H
     b = algorithmic_bytes("fwd", S, T, n)
@@ -274,6 +339,7 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
         "matrix_tflops": round(impl_flops / (med * 1e-3) / 1e12, 2),
         "matrix_peak_tflops": peak,
         "matrix_util": round(impl_flops / (med * 1e-3) / 1e12 / peak, 4),
+        "matrix_util_counted": load_mfma_util(name, "fwd"),
         "from_x": from_x,
         "data": "synthetic, seeded on the GPU (torch.Generator), same scales as the workload",
     }
@@ -281,14 +347,17 @@ def fwd_only(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
 
 def fwd_bwd(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
     """Forward and backward scans (M -> P, then M, P, dL/dP -> dL/dM) on the
-    n = 16 forward+backward workload; inputs generated on the GPU from a seed,
+    n = 16 forward+backward workload, and the layer step from the raw token
+    vectors (x -> P, then x, P, dL/dP -> dL/dx in one pass) beside the
+    three-kernel backward it replaces; inputs generated on the GPU from a seed,
     dL/dP drawn N(0, 1)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     scale = torch.full((n, n), so, device="cuda")
     scale.fill_diagonal_(sd)
     x = (torch.randn((B, H, T, n, n), generator=g, device="cuda") * scale).reshape(B, H, T, n * n)
-    M = mpp.build_inputs(x.contiguous(), n)
+    x_layer = x.contiguous()
+    M = mpp.build_inputs(x_layer, n)
     del x
     R = torch.randn((B, H, T, n, n), generator=g, device="cuda")
     P = torch.empty_like(M)
@@ -297,6 +366,8 @@ def fwd_bwd(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
     ws_b = torch.empty(max(mpp.workspace_bytes(B, H, T, n, mpp.DIR_BWD), 256), dtype=torch.uint8, device="cuda")
     t_f = _time(torch, lambda: mpp.scan_fwd(M, out=P, workspace=ws_f), reps)
     t_b = _time(torch, lambda: mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b), reps)
+    ws_ok(mpp, ws_f, B, H, T, n, mpp.DIR_FWD)
+    ws_ok(mpp, ws_b, B, H, T, n, mpp.DIR_BWD)
     S = B * H
     out = {"workload": f"{name}: B={B},H={H},T={T},n={n}, forward scan then backward scan"}
     for kind, us in (("fwd", t_f), ("bwd", t_b)):
@@ -316,10 +387,36 @@ def fwd_bwd(mpp, torch, name, B, H, T, n, so, sd, reps, seed):
             "matrix_tflops": round(flops / (us * 1e-6) / 1e12, 2),
             "matrix_peak_tflops": FP64_PEAK_TFLOPS,
             "matrix_util": round(flops / (us * 1e-6) / 1e12 / FP64_PEAK_TFLOPS, 4),
+            "matrix_util_counted": load_mfma_util(name, kind),
         }
     out["tokens_per_s"] = B * T / ((t_f + t_b) * 1e-6)
+    # the layer step from the raw token vectors: forward x -> P and the one-pass
+    # backward x, P, dL/dP -> dL/dx, against the three-kernel backward it replaces
+    # (build x -> M, backward to dL/dM, the build's gradient dL/dM -> dL/dx)
+    x = x_layer
+    dx = torch.empty_like(x)
+    t_fx = _time(torch, lambda: mpp.scan_fwd_x(x, n, out=P, workspace=ws_f), reps)
+    ws_ok(mpp, ws_f, B, H, T, n, mpp.DIR_FWD)
+    t_dx = _time(torch, lambda: mpp.scan_bwd_dx(x, P, R, out=dx, workspace=ws_b), reps)
+    ws_ok(mpp, ws_b, B, H, T, n, mpp.DIR_BWD)
+    t_bx = _time(torch, lambda: mpp.scan_bwd_x(x, P, R, out=dM, workspace=ws_b), reps)
+    t_build = _time(torch, lambda: mpp.build_inputs(x, n, out=M), reps)
+    t_bm = _time(torch, lambda: mpp.scan_bwd(M, P, R, out=dM, workspace=ws_b), reps)
+    t_bb = _time(torch, lambda: mpp.build_inputs_bwd(x, dM, out=dx), reps)
+    out["layer_from_x"] = {
+        "fwd_x_us": round(t_fx, 1),
+        "bwd_dx_us": round(t_dx, 1),
+        "step_us": round(t_fx + t_dx, 1),
+        "step_tokens_per_s": B * T / ((t_fx + t_dx) * 1e-6),
+        "bwd_x_us": round(t_bx, 1),
+        "three_kernel_bwd_us": {"build": round(t_build, 1), "bwd": round(t_bm, 1),
+                                "build_bwd": round(t_bb, 1), "total": round(t_build + t_bm + t_bb, 1)},
+        "bwd_dx_algorithmic_GBs": round(algorithmic_bytes("bwd_dx", S, T, n) / (t_dx * 1e-6) / 1e9, 1),
+        "bwd_dx_frac_hbm": round(algorithmic_bytes("bwd_dx", S, T, n) / (t_dx * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "matrix_util_counted": {"bwd_dx": load_mfma_util(name, "bwd_dx"), "bwd_x": load_mfma_util(name, "bwd_x")},
+    }
     out["data"] = "synthetic, seeded on the GPU (torch.Generator), same scales as the workload"
-    del M, R, P, dM, ws_f, ws_b
+    del M, R, P, dM, ws_f, ws_b, x, dx
     torch.cuda.empty_cache()
     return out
 
@@ -341,6 +438,7 @@ def small_configs(mpp, torch, WORKLOADS, gen_R, gen_x, reps: int = 50):
         ws_b = torch.empty(max(mpp.workspace_bytes(w.B, w.H, w.T, w.n, mpp.DIR_BWD), 256),
                            dtype=torch.uint8, device="cuda")
         fwd = _time(torch, lambda: mpp.scan_fwd_x(x, w.n, out=P, workspace=ws_f), reps)
+        ws_ok(mpp, ws_f, w.B, w.H, w.T, w.n, mpp.DIR_FWD)
         rec = {"workload": f"{name}: B={w.B},H={w.H},T={w.T},n={w.n}",
                "plan": dict(zip(("chunk", "chunks_per_seq", "super", "ws_bytes"),
                                 mpp.scan_plan(w.B, w.H, w.T, w.n, mpp.DIR_FWD))),
@@ -351,6 +449,7 @@ def small_configs(mpp, torch, WORKLOADS, gen_R, gen_x, reps: int = 50):
                 mpp.scan_fwd_x(x, w.n, out=P, workspace=ws_f)
                 mpp.scan_bwd_x(x, P, R, out=dM, workspace=ws_b)
             st = _time(torch, step, reps)
+            ws_ok(mpp, ws_b, w.B, w.H, w.T, w.n, mpp.DIR_BWD)
             rec["step_median_us"] = round(st, 2)
             rec["step_tokens_per_s"] = w.B * w.T / (st * 1e-6)
         out[name] = rec
@@ -596,10 +695,18 @@ def main():
             "frac": dk["frac_hbm"],
             "traffic": dk["traffic"],
             "algorithmic_bytes_per_launch": dk["algorithmic_bytes"],
+            "frac_traffic": dk["frac_hbm_traffic"],
+            "design_bytes_per_launch": dk["design_bytes"],
+            "basis": "achieved = algorithmic bytes per launch (16 n^2 per token-head for the "
+                     "backward: x, P, dL/dP read and dL/dM written) / the kernel's mean launch "
+                     "time; frac_traffic uses the counted HBM bytes instead",
         },
         "kernels": kernels,
         "wall_s_timed": round(wall, 4),
     }
+    # every look-back wait of the timed scans completed (multi-chunk plans only)
+    ws_ok(mpp, ws_f, B, H, T, n, mpp.DIR_FWD)
+    ws_ok(mpp, ws_b, B, H, T, n, mpp.DIR_BWD)
     out["unfused"] = unfused(mpp, torch, x, R, P, dM, ws_f, ws_b, n, S, T, w.name)
     del x, R, P, dM, ws_f, ws_b
     torch.cuda.empty_cache()

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MRU_ABI_VERSION 1
+#define MRU_ABI_VERSION 2
 
 typedef enum mru_status {
     MRU_OK = 0,
@@ -63,8 +63,14 @@ typedef enum mru_status {
     MRU_ERR_ALIAS = 4,      /* an output overlaps an input or another output      */
     MRU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required            */
     MRU_ERR_CHUNK = 6,      /* chunk < 0                                          */
-    MRU_ERR_HIP = 7         /* the HIP runtime reported an error at launch        */
+    MRU_ERR_HIP = 7,        /* the HIP runtime reported an error at launch        */
+    MRU_ERR_TIMEOUT = 8     /* never returned by a call: the code bindings raise
+                               when mru_scan_ws_status reports
+                               MRU_WS_STATUS_SPIN_TIMEOUT                         */
 } mru_status;
+
+/* Bits of the workspace status word (mru_scan_ws_status). */
+#define MRU_WS_STATUS_SPIN_TIMEOUT 1u /* a look-back wait gave up: outputs invalid */
 
 /* Scan direction for the workspace / chunk queries. */
 #define MRU_DIR_FWD 0
@@ -129,9 +135,9 @@ mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int6
                                 int64_t T, int32_t n, void* stream);
 
 /*
- * Chunk length (tokens per scan chunk) that chunk = 0 resolves to for this
- * shape and direction; a pure function of its arguments.  Returns 0 for an
- * invalid shape.
+ * Chunk length (tokens per scan chunk) of the automatic plan for this shape
+ * and direction; a pure function of its arguments.  Returns 0 for an invalid
+ * shape.
  */
 int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction);
 
@@ -148,12 +154,34 @@ int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direct
 
 /*
  * Workspace bytes that mru_scan_fwd (direction MRU_DIR_FWD) or mru_scan_bwd
- * (MRU_DIR_BWD) needs for this shape and chunk (0 = automatic).  May be 0, in
- * which case ws may be NULL.  Returns 0 for an invalid shape as well; callers
- * validate through the scan call itself.
+ * (MRU_DIR_BWD) needs for this shape with the automatic plan; the same size
+ * serves every entry point of that direction (from M or from raw token
+ * vectors, with or without a carried state).  May be 0, in which case ws may
+ * be NULL.  Returns 0 for an invalid shape as well; callers validate through
+ * the scan call itself.
  */
-size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
-                                int32_t chunk);
+size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction);
+
+/* The same for an explicit chunk length (0 = automatic), as taken by the
+ * entry points with a chunk argument. */
+size_t mru_scan_workspace_bytes_chunked(int64_t B, int64_t H, int64_t T, int32_t n,
+                                        int32_t direction, int32_t chunk);
+
+/*
+ * Status word of a scan's workspace, copied in stream order to *status (one
+ * int32 in device memory, 4-byte aligned): 0 when every look-back wait of the
+ * last multi-chunk scan that used ws completed, MRU_WS_STATUS_SPIN_TIMEOUT
+ * when one gave up.  Chunks wait only on chunks whose owners are already
+ * running, so every wait ends; the bounded poll turns a logic error into this
+ * bit instead of a hang, and a scan that sets it has invalid outputs.  Pass
+ * the ws and ws_bytes of that scan, enqueued after it on the same stream.  A
+ * plan with one chunk per sequence (workspace size 0) never waits: with ws
+ * NULL or ws_bytes below 256, *status is set to 0.  A single-chunk scan does
+ * not touch the word, so query right after the scan it concerns.  Returns
+ * MRU_ERR_NULL (status NULL), MRU_ERR_ALIGN, MRU_ERR_ALIAS (status inside the
+ * header) or MRU_ERR_HIP.
+ */
+mru_status mru_scan_ws_status(const void* ws, size_t ws_bytes, int32_t* status, void* stream);
 
 /*
  * Forward scan: every running product of the input state matrices.
@@ -165,15 +193,26 @@ size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int3
  * P      [B][H][T][n][n] fp32, written: P_t = M_1 M_2 ... M_t for every sequence,
  *        inclusive, with P_0 = I (right multiplication, P_t = P_{t-1} M_t).
  *        P viewed as [B][H][T][n*n] is the flattened output vector.
- * chunk  tokens per scan chunk; 0 = automatic (mru_scan_chunk).  Any positive
- *        value gives the same result up to rounding order.
- * ws     device workspace of at least mru_scan_workspace_bytes(..., MRU_DIR_FWD,
- *        chunk) bytes (16-byte aligned), or NULL when that size is 0.  Its
- *        contents on entry are ignored; on exit it holds scratch state only.
+ * ws     device workspace of at least mru_scan_workspace_bytes(B, H, T, n,
+ *        MRU_DIR_FWD) bytes (16-byte aligned), or NULL when that size is 0.
+ *        Its contents on entry are ignored; on exit it holds scratch state and
+ *        the status word (mru_scan_ws_status).
+ * stream a hipStream_t.
  * M and P must not overlap; P must not overlap ws.
  */
 mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
-                        int32_t chunk, void* ws, size_t ws_bytes, void* stream);
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mru_scan_fwd with an explicit plan: chunk = tokens per scan chunk, 0 =
+ * automatic (mru_scan_chunk).  Any positive value gives the same result up to
+ * rounding order; ws as for mru_scan_fwd with
+ * mru_scan_workspace_bytes_chunked(..., MRU_DIR_FWD, chunk).  MRU_ERR_CHUNK
+ * for chunk < 0.
+ */
+mru_status mru_scan_fwd_chunked(const float* M, float* P, int64_t B, int64_t H, int64_t T,
+                                int32_t n, int32_t chunk, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * Forward scan straight from raw token vectors: mru_build_inputs followed by
@@ -183,7 +222,7 @@ mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t 
  * dense product); for n = 16, 32 each token's matrix is formed on chip, in
  * fp32 as by mru_build_inputs (as the unit lower factor times diag(e) U), and
  * fed to the same fp64 chain as mru_scan_fwd.  Results agree with the two-call
- * path up to rounding order.  Arguments as for mru_scan_fwd with x
+ * path up to rounding order.  Arguments as for mru_scan_fwd_chunked with x
  * ([B][H][T][n*n]) in place of M; x and P must not overlap.  n in {4, 8, 16,
  * 32}.
  */
@@ -201,24 +240,37 @@ mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_
  *
  * M   [B][H][T][n][n] fp32, read (the forward inputs).
  * P   [B][H][T][n][n] fp32, read (the forward outputs of mru_scan_fwd on M).
- *     For n in {4, 8} only one prefix in four is read (the one before each
- *     block of four tokens, counted from a chunk's end) and the prefixes in
- *     between are recomputed from it and M, so P must be the forward's output
- *     on this M (up to rounding); n in {16, 32} reads every prefix.
+ *     Every prefix P_{t-1} is read and used as given.
  * dP  [B][H][T][n][n] fp32, read.
  * dM  [B][H][T][n][n] fp32, written.
- * chunk, ws, ws_bytes as for mru_scan_fwd with direction MRU_DIR_BWD.
+ * ws  device workspace of at least mru_scan_workspace_bytes(B, H, T, n,
+ *     MRU_DIR_BWD) bytes (16-byte aligned), or NULL when that size is 0.
  * dM must not overlap M, P, dP or ws.
  */
 mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
-                        int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
-                        size_t ws_bytes, void* stream);
+                        int64_t H, int64_t T, int32_t n, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * mru_scan_bwd with an explicit plan (chunk as for mru_scan_fwd_chunked, ws
+ * sized by mru_scan_workspace_bytes_chunked(..., MRU_DIR_BWD, chunk)).
+ */
+mru_status mru_scan_bwd_chunked(const float* M, const float* P, const float* dP, float* dM,
+                                int64_t B, int64_t H, int64_t T, int32_t n, int32_t chunk,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Backward scan from raw token vectors: dM as from mru_build_inputs followed
  * by mru_scan_bwd, multiplying by the transposed factors of M_{t+1}
- * (U^T, diag(e), L^T) read from x.  Arguments as for mru_scan_bwd with x in
- * place of M.  n in {4, 8}; other n return MRU_ERR_SHAPE.
+ * (U^T, diag(e), L^T) read from x.  Arguments as for mru_scan_bwd_chunked with
+ * x in place of M.  For n in {4, 8} only one prefix in four is read (the one
+ * before each block of four tokens, counted from a chunk's end) and the
+ * prefixes in between are recomputed from it and x, so P must be the
+ * forward's output on this x (mru_scan_fwd_x; equal up to rounding).  For
+ * n = 16, 32 every prefix is read, and each M_{t+1} is formed on chip in fp32
+ * exactly as mru_build_inputs forms it (the same products and sums), so dM is
+ * bit for bit that of mru_build_inputs followed by mru_scan_bwd_chunked.
+ * n in {4, 8, 16, 32}.
  */
 mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float* dM, int64_t B,
                           int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
@@ -246,7 +298,7 @@ mru_status mru_scan_bwd_x(const float* x, const float* P, const float* dP, float
  *            result, and beyond that range the scan keeps going.
  * The carry out of a segment is its last token's (P, P_exp); passing it as
  * the next segment's (carry, carry_exp) continues the scan.
- * chunk, ws, ws_bytes as for mru_scan_fwd (the same workspace size).
+ * chunk, ws, ws_bytes as for mru_scan_fwd_chunked (the same workspace size).
  * Errors: as mru_scan_fwd; MRU_ERR_ALIGN for a misaligned carry (16 bytes)
  * or exponent array (4 bytes); MRU_ERR_ALIAS if P or P_exp overlaps an input,
  * each other or ws.  B*H*T = 0 writes nothing.
@@ -268,7 +320,7 @@ mru_status mru_scan_fwd_ex(const float* in, int32_t from_x, const float* carry,
  * dcarry      [B][H][n][n] fp32, written, or NULL.  For a segmented
  *             sequence, the next segment's dcarry is added into this
  *             segment's dP at its last token.
- * chunk, ws, ws_bytes as for mru_scan_bwd.  Errors as mru_scan_bwd, plus
+ * chunk, ws, ws_bytes as for mru_scan_bwd_chunked.  Errors as mru_scan_bwd, plus
  * MRU_ERR_ALIGN / MRU_ERR_ALIAS for carry and dcarry.  B*H*T = 0 writes
  * nothing (dcarry included).
  */
@@ -284,21 +336,26 @@ mru_status mru_scan_bwd_ex(const float* in, int32_t from_x, const float* carry, 
  * scalar, "Improving Matrix Recurrent Units as an Attention Alternative", Key
  * Points).  The same result as mru_scan_bwd_ex (from_x = 1) followed by
  * mru_build_inputs_bwd on its dM, up to rounding, without writing dM or reading
- * x a second time: per token it reads x, dP and one stored prefix in four and
- * writes dx.  With G = dL/dM_t, H = G U^T and g_k = (L^T G U^T)_kk:
- *   dX_ij = e_j H_ij (i > j),  e_i (L^T G)_ij (i < j),  e_i g_i - mean_k e_k g_k (i = j),
- * where (L^T G) is formed from the rows of P_{t-1} L_t, as G from those of P_{t-1}.
+ * x a second time: per token it reads x, dP and the stored prefixes (n = 4, 8:
+ * one in four) and writes dx.  With G = dL/dM_t, H = G U^T and
+ * g_k = (L^T G U^T)_kk:
+ *   dX_ij = e_j H_ij (i > j),  e_i (L^T G)_ij (i < j),  e_i g_i - mean_k e_k g_k (i = j).
+ * For n = 4, 8, (L^T G) is formed from the rows of P_{t-1} L_t, as G from
+ * those of P_{t-1}; for n = 16, 32 from G itself on the matrix core.
  *
  * x       [B][H][T][n*n] fp32, read (the forward's inputs).
  * carry   [B][H][n][n] fp32 (P_0) or NULL for I; 16-byte aligned.
  * P, dP   [B][H][T][n][n] fp32, read: the forward's outputs on x (mru_scan_fwd_x
- *         or mru_scan_fwd_ex) and dL/dP.  One prefix in four is read, as for
- *         mru_scan_bwd.
+ *         or mru_scan_fwd_ex) and dL/dP.  For n = 4, 8 one prefix in four is
+ *         read, as for mru_scan_bwd_x.
  * dx      [B][H][T][n*n] fp32, written.
  * dcarry  [B][H][n][n] fp32, written (dL/dP_0), or NULL.
- * chunk, ws, ws_bytes as for mru_scan_bwd.  n in {4, 8}; other n return
- * MRU_ERR_SHAPE.  Errors as mru_scan_bwd_ex; dx must not overlap any input,
- * dcarry or ws.  B*H*T = 0 writes nothing.
+ * chunk, ws, ws_bytes as for mru_scan_bwd_chunked.  n in {4, 8, 16, 32}.  For
+ * n = 16, 32 every prefix is read, and each token's dM_t (rounded to fp32)
+ * goes through the same per-token routine as mru_build_inputs_bwd, so dx is
+ * bit for bit mru_build_inputs_bwd applied to mru_scan_bwd_ex's dM.  Errors as
+ * mru_scan_bwd_ex; dx must not overlap any input, dcarry or ws.  B*H*T = 0
+ * writes nothing.
  */
 mru_status mru_scan_bwd_dx(const float* x, const float* carry, const float* P, const float* dP,
                            float* dx, float* dcarry, int64_t B, int64_t H, int64_t T, int32_t n,

@@ -27,24 +27,31 @@ __all__ = [
     "build_inputs", "build_inputs_bwd", "scan_fwd", "mru_layer", "MRUBuild", "scan_bwd", "flatten", "mru_scan", "MRUScan",
     "scan_fwd_x", "scan_bwd_x", "scan_fwd_ex", "scan_bwd_ex", "scan_bwd_dx", "build_orthogonal",
     "scan_plan", "scan_chunk", "workspace_bytes", "library_path", "load_library",
-    "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N", "FUSED_N", "FUSED_FWD_N",
+    "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N", "FUSED_N", "FUSED_FWD_N", "FUSED_BWD_N",
+    "set_checking", "ws_status", "MRU_ERR_TIMEOUT",
 ]
 
 DIR_FWD = 0
 DIR_BWD = 1
 SUPPORTED_N = (4, 8, 16, 32)
 # Sizes whose forward scan can start from raw token vectors (input matrices
-# built on chip), and sizes whose backward scans can too (FUSED_N).
+# built on chip), whose backward scan to dL/dM can too (FUSED_BWD_N), and whose
+# layer backward goes from dL/dP to dL/dx in one pass (FUSED_N).
 FUSED_FWD_N = (4, 8, 16, 32)
-FUSED_N = (4, 8)
+FUSED_BWD_N = (4, 8, 16, 32)
+FUSED_N = (4, 8, 16, 32)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmru.so")
 _LIB = None
 
 _STATUS = {
     0: "MRU_OK", 1: "MRU_ERR_NULL", 2: "MRU_ERR_SHAPE", 3: "MRU_ERR_ALIGN", 4: "MRU_ERR_ALIAS",
-    5: "MRU_ERR_WORKSPACE", 6: "MRU_ERR_CHUNK", 7: "MRU_ERR_HIP",
+    5: "MRU_ERR_WORKSPACE", 6: "MRU_ERR_CHUNK", 7: "MRU_ERR_HIP", 8: "MRU_ERR_TIMEOUT",
 }
+MRU_ERR_TIMEOUT = 8
+# Whether every scan checks its workspace status word after the launch (one
+# device-to-host read, which synchronises the stream); see set_checking().
+_CHECK_ALL = os.environ.get("MRU_CHECK_WS", "0") not in ("", "0")
 
 
 class MRUError(RuntimeError):
@@ -85,11 +92,19 @@ def load_library():
     lib.mru_scan_plan.restype = i32
     lib.mru_scan_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
     lib.mru_scan_workspace_bytes.restype = sz
-    lib.mru_scan_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.mru_scan_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.mru_scan_workspace_bytes_chunked.restype = sz
+    lib.mru_scan_workspace_bytes_chunked.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.mru_scan_ws_status.restype = i32
+    lib.mru_scan_ws_status.argtypes = [vp, sz, vp, vp]
     lib.mru_scan_fwd.restype = i32
-    lib.mru_scan_fwd.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_fwd.argtypes = [vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.mru_scan_fwd_chunked.restype = i32
+    lib.mru_scan_fwd_chunked.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.mru_scan_bwd.restype = i32
-    lib.mru_scan_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.mru_scan_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.mru_scan_bwd_chunked.restype = i32
+    lib.mru_scan_bwd_chunked.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.mru_scan_fwd_x.restype = i32
     lib.mru_scan_fwd_x.argtypes = [vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.mru_scan_bwd_x.restype = i32
@@ -158,7 +173,44 @@ def scan_plan(B: int, H: int, T: int, n: int, direction: int = DIR_FWD, chunk: i
 
 
 def workspace_bytes(B: int, H: int, T: int, n: int, direction: int = DIR_FWD, chunk: int = 0) -> int:
-    return int(load_library().mru_scan_workspace_bytes(B, H, T, n, direction, chunk))
+    lib = load_library()
+    if chunk == 0:
+        return int(lib.mru_scan_workspace_bytes(B, H, T, n, direction))
+    return int(lib.mru_scan_workspace_bytes_chunked(B, H, T, n, direction, chunk))
+
+
+def set_checking(on: bool = True) -> None:
+    """Make every scan of this module read its workspace status word after the
+    launch and raise MRUError(MRU_ERR_TIMEOUT) if a look-back wait gave up.
+    The read synchronises the stream, so it is off by default; the
+    environment variable MRU_CHECK_WS=1 turns it on at import."""
+    global _CHECK_ALL
+    _CHECK_ALL = bool(on)
+
+
+def ws_status(workspace: torch.Tensor | None, stream_device: torch.device | None = None) -> int:
+    """Status word of a scan workspace (mru_scan_ws_status), read back to the
+    host: 0, or MRU_WS_STATUS_SPIN_TIMEOUT (1) when a look-back wait of the
+    last multi-chunk scan that used it gave up.  Synchronises the stream."""
+    dev = workspace.device if workspace is not None else (stream_device or torch.device("cuda"))
+    out = torch.empty(1, dtype=torch.int32, device=dev)
+    lib = load_library()
+    nbytes = workspace.numel() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        st = lib.mru_scan_ws_status(_ptr(workspace), nbytes, _ptr(out), _stream_handle(dev))
+    _check(st, "mru_scan_ws_status")
+    return int(out.item())
+
+
+def _after_scan(ws, check, what, shape, n, direction, chunk):
+    """Raise if the scan that just used ws reported a timed-out look-back (only
+    multi-chunk plans wait, and only they write the status word)."""
+    if not (check or _CHECK_ALL) or ws is None:
+        return
+    if workspace_bytes(*shape, n, direction, chunk) == 0:
+        return
+    if ws_status(ws) != 0:
+        raise MRUError(MRU_ERR_TIMEOUT, what)
 
 
 def _workspace(shape, n, direction, chunk, device, workspace):
@@ -240,8 +292,12 @@ def build_inputs_bwd(x: torch.Tensor, dM: torch.Tensor, out: torch.Tensor | None
 
 
 def scan_fwd(M: torch.Tensor, chunk: int = 0, out: torch.Tensor | None = None,
-             workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """All prefix products P_t = M_1 ... M_t (P_0 = I), [B,H,T,n,n]."""
+             workspace: torch.Tensor | None = None, check: bool = False) -> torch.Tensor:
+    """All prefix products P_t = M_1 ... M_t (P_0 = I), [B,H,T,n,n].
+
+    chunk 0 uses the automatic plan (mru_scan_fwd), a positive chunk forces that
+    chunk length (mru_scan_fwd_chunked).  check: read the workspace status word
+    afterwards and raise if a look-back wait gave up (synchronises)."""
     B, H, T, n = _mshape(M)
     if out is None:
         out = torch.empty_like(M)
@@ -252,15 +308,22 @@ def scan_fwd(M: torch.Tensor, chunk: int = 0, out: torch.Tensor | None = None,
     ws, ws_bytes = _workspace((B, H, T), n, DIR_FWD, chunk, M.device, workspace)
     lib = load_library()
     with torch.cuda.device(M.device):
-        st = lib.mru_scan_fwd(_ptr(M), _ptr(out), B, H, T, n, chunk, _ptr(ws), ws_bytes,
-                              _stream_handle(M.device))
+        if chunk == 0:
+            st = lib.mru_scan_fwd(_ptr(M), _ptr(out), B, H, T, n, _ptr(ws), ws_bytes,
+                                  _stream_handle(M.device))
+        else:
+            st = lib.mru_scan_fwd_chunked(_ptr(M), _ptr(out), B, H, T, n, chunk, _ptr(ws), ws_bytes,
+                                          _stream_handle(M.device))
     _check(st, "mru_scan_fwd")
+    _after_scan(ws, check, "mru_scan_fwd", (B, H, T), n, DIR_FWD, chunk)
     return out
 
 
 def scan_bwd(M: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
-             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Gradient dM of sum_t <dP_t, P_t> where P = scan_fwd(M), [B,H,T,n,n]."""
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+             check: bool = False) -> torch.Tensor:
+    """Gradient dM of sum_t <dP_t, P_t> where P = scan_fwd(M), [B,H,T,n,n]
+    (chunk and check as for scan_fwd)."""
     B, H, T, n = _mshape(M)
     for name, t in (("P", P), ("dP", dP)):
         _require(t, name, 5)
@@ -275,9 +338,14 @@ def scan_bwd(M: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
     ws, ws_bytes = _workspace((B, H, T), n, DIR_BWD, chunk, M.device, workspace)
     lib = load_library()
     with torch.cuda.device(M.device):
-        st = lib.mru_scan_bwd(_ptr(M), _ptr(P), _ptr(dP), _ptr(out), B, H, T, n, chunk, _ptr(ws),
-                              ws_bytes, _stream_handle(M.device))
+        if chunk == 0:
+            st = lib.mru_scan_bwd(_ptr(M), _ptr(P), _ptr(dP), _ptr(out), B, H, T, n, _ptr(ws),
+                                  ws_bytes, _stream_handle(M.device))
+        else:
+            st = lib.mru_scan_bwd_chunked(_ptr(M), _ptr(P), _ptr(dP), _ptr(out), B, H, T, n, chunk,
+                                          _ptr(ws), ws_bytes, _stream_handle(M.device))
     _check(st, "mru_scan_bwd")
+    _after_scan(ws, check, "mru_scan_bwd", (B, H, T), n, DIR_BWD, chunk)
     return out
 
 
@@ -290,7 +358,7 @@ def _xshape(x: torch.Tensor, n: int, allowed=FUSED_N):
 
 
 def scan_fwd_x(x: torch.Tensor, n: int, chunk: int = 0, out: torch.Tensor | None = None,
-               workspace: torch.Tensor | None = None) -> torch.Tensor:
+               workspace: torch.Tensor | None = None, check: bool = False) -> torch.Tensor:
     """scan_fwd(build_inputs(x, n)) in one pass that never writes the input
     matrices (n in FUSED_FWD_N)."""
     B, H, T = _xshape(x, n, FUSED_FWD_N)
@@ -306,15 +374,17 @@ def scan_fwd_x(x: torch.Tensor, n: int, chunk: int = 0, out: torch.Tensor | None
         st = lib.mru_scan_fwd_x(_ptr(x), _ptr(out), B, H, T, n, chunk, _ptr(ws), ws_bytes,
                                 _stream_handle(x.device))
     _check(st, "mru_scan_fwd_x")
+    _after_scan(ws, check, "mru_scan_fwd_x", (B, H, T), n, DIR_FWD, chunk)
     return out
 
 
 def scan_bwd_x(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 0,
-               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """scan_bwd(build_inputs(x, n), P, dP) with the input matrices rebuilt on chip."""
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, check: bool = False) -> torch.Tensor:
+    """scan_bwd(build_inputs(x, n), P, dP) with the input matrices rebuilt on chip
+    (n in FUSED_BWD_N)."""
     _require(P, "P", 5)
     n = P.shape[-1]
-    B, H, T = _xshape(x, n)
+    B, H, T = _xshape(x, n, FUSED_BWD_N)
     for name, t in (("P", P), ("dP", dP)):
         _require(t, name, 5)
         if tuple(t.shape) != (B, H, T, n, n) or t.device != x.device:
@@ -331,6 +401,7 @@ def scan_bwd_x(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor, chunk: int = 
         st = lib.mru_scan_bwd_x(_ptr(x), _ptr(P), _ptr(dP), _ptr(out), B, H, T, n, chunk, _ptr(ws),
                                 ws_bytes, _stream_handle(x.device))
     _check(st, "mru_scan_bwd_x")
+    _after_scan(ws, check, "mru_scan_bwd_x", (B, H, T), n, DIR_BWD, chunk)
     return out
 
 
@@ -354,7 +425,7 @@ def _carry_arg(carry, B, H, n, dev, name="carry"):
 def scan_fwd_ex(inp: torch.Tensor, carry: torch.Tensor | None = None,
                 carry_exp: torch.Tensor | None = None, scaled: bool = False,
                 from_x: bool = False, n: int | None = None, chunk: int = 0,
-                workspace: torch.Tensor | None = None):
+                workspace: torch.Tensor | None = None, check: bool = False):
     """P_t = P_0 M_1 ... M_t with P_0 = 2^carry_exp * carry (I when carry is None).
 
     inp is M [B,H,T,n,n], or x [B,H,T,n*n] with from_x (n in FUSED_FWD_N).
@@ -375,17 +446,18 @@ def scan_fwd_ex(inp: torch.Tensor, carry: torch.Tensor | None = None,
         st = lib.mru_scan_fwd_ex(_ptr(inp), int(from_x), _ptr(carry), _ptr(carry_exp), _ptr(P),
                                  _ptr(E), B, H, T, n, chunk, _ptr(ws), ws_bytes, _stream_handle(dev))
     _check(st, "mru_scan_fwd_ex")
+    _after_scan(ws, check, "mru_scan_fwd_ex", (B, H, T), n, DIR_FWD, chunk)
     return (P, E) if scaled else P
 
 
 def scan_bwd_ex(inp: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
                 carry: torch.Tensor | None = None, want_dcarry: bool = False,
-                from_x: bool = False, chunk: int = 0, workspace: torch.Tensor | None = None):
+                from_x: bool = False, chunk: int = 0, workspace: torch.Tensor | None = None, check: bool = False):
     """dM of sum_t <dP_t, P_t> for P_t = P_0 M_1 ... M_t (P_0 = carry, or I),
     and with want_dcarry also dL/dP_0.  P is the plain (unscaled) forward."""
     _require(P, "P", 5)
     n = P.shape[-1]
-    B, H, T, n = _inshape(inp, from_x, n)
+    B, H, T, n = _inshape(inp, from_x, n, FUSED_BWD_N)
     dev = inp.device
     for name, t in (("P", P), ("dP", dP)):
         _require(t, name, 5)
@@ -400,12 +472,13 @@ def scan_bwd_ex(inp: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
         st = lib.mru_scan_bwd_ex(_ptr(inp), int(from_x), _ptr(carry), _ptr(P), _ptr(dP), _ptr(dM),
                                  _ptr(dC), B, H, T, n, chunk, _ptr(ws), ws_bytes, _stream_handle(dev))
     _check(st, "mru_scan_bwd_ex")
+    _after_scan(ws, check, "mru_scan_bwd_ex", (B, H, T), n, DIR_BWD, chunk)
     return (dM, dC) if want_dcarry else dM
 
 
 def scan_bwd_dx(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
                 carry: torch.Tensor | None = None, want_dcarry: bool = False, chunk: int = 0,
-                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, check: bool = False):
     """dL/dx of sum_t <dP_t, P_t> for P_t = P_0 M_1 ... M_t with M_t built from
     x_t (build_inputs), in one pass: build_inputs_bwd(x, scan_bwd_x(x, P, dP))
     without forming dL/dM.  P is the forward's output on x (scan_fwd_x or
@@ -432,6 +505,7 @@ def scan_bwd_dx(x: torch.Tensor, P: torch.Tensor, dP: torch.Tensor,
         st = lib.mru_scan_bwd_dx(_ptr(x), _ptr(carry), _ptr(P), _ptr(dP), _ptr(out), _ptr(dC),
                                  B, H, T, n, chunk, _ptr(ws), ws_bytes, _stream_handle(dev))
     _check(st, "mru_scan_bwd_dx")
+    _after_scan(ws, check, "mru_scan_bwd_dx", (B, H, T), n, DIR_BWD, chunk)
     return (out, dC) if want_dcarry else out
 
 
@@ -494,34 +568,11 @@ class MRULayerFused(torch.autograd.Function):
         return scan_bwd_dx(x, P, dP.contiguous(), chunk=ctx.chunk), None, None
 
 
-class MRULayerFwdX(torch.autograd.Function):
-    """P = scan_fwd_x(x, n) (n in FUSED_FWD_N but not FUSED_N); the backward
-    rebuilds the input matrices from x, then scan_bwd and build_inputs_bwd.
-    Only x and P are kept between the passes."""
-
-    @staticmethod
-    def forward(ctx, x: torch.Tensor, n: int, chunk: int = 0):
-        x = x.contiguous()
-        P = scan_fwd_x(x, n, chunk)
-        ctx.save_for_backward(x, P)
-        ctx.n, ctx.chunk = n, chunk
-        return P
-
-    @staticmethod
-    def backward(ctx, dP: torch.Tensor):
-        x, P = ctx.saved_tensors
-        M = build_inputs(x, ctx.n)
-        dM = scan_bwd(M, P, dP.contiguous(), ctx.chunk)
-        return build_inputs_bwd(x, dM), None, None
-
-
 def mru_layer(x: torch.Tensor, n: int, chunk: int = 0) -> torch.Tensor:
     """The MRU token mixer up to the output state matrices: x [B,H,T,n*n] ->
     P [B,H,T,n,n] (flatten() gives the output vectors), differentiable in x.
-    For n in FUSED_N both scans build the input matrices on chip; for the
-    other n in FUSED_FWD_N the forward does, and the backward rebuilds them."""
+    Both scans form the input matrices on chip (n in FUSED_N: every n), and
+    the backward goes from dL/dP straight to dL/dx in one pass."""
     if n in FUSED_N:
         return MRULayerFused.apply(x, n, chunk)
-    if n in FUSED_FWD_N:
-        return MRULayerFwdX.apply(x, n, chunk)
     return MRUScan.apply(MRUBuild.apply(x, n), chunk)

@@ -14,6 +14,7 @@
 #include <type_traits>
 
 #include "mru_build.h"
+#include "mru_build_mfma.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
 
@@ -76,12 +77,13 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(const float* __res
 //   dX_ij = e_i (L^T G)_ij               (i < j, through U)
 //   dX_kk = e_k g_k - mean_j e_j g_j     (through e; X_kk also enters the mean)
 // with g_k = (L^T G U^T)_kk = sum_r L_rk H_rk.  One lane per row of dX; the
-// column sums for g go through LDS.
+// column sums for g go through LDS.  n = 4, 8 (n = 16, 32: build_bwd_mfma_kernel).
 template <int N>
 __global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* __restrict__ x,
                                                                   const float* __restrict__ dM,
                                                                   float* __restrict__ dx,
                                                                   int64_t ntok) {
+    static_assert(N == 4 || N == 8, "vector-ALU build backward for n = 4, 8");
     constexpr int NN = N * N;
     constexpr int TPI = kBuildThreads / N;  // tokens per block iteration
     constexpr int XS = NN + 4;
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* _
         __syncthreads();
         // H row i: H_ij = sum_{m >= j} G_im U_jm (U_jj = 1)
         float h[N];
-        if constexpr (N <= 8) {
+        {
             float grow[N];
 #pragma unroll
             for (int m = 0; m < N; ++m) grow[m] = gt[i * N + m];
@@ -148,19 +150,6 @@ __global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* _
                 for (int m = j + 1; m < N; ++m) acc = fmaf(grow[m], xt[j * N + m], acc);
                 h[j] = acc;
             }
-        } else {
-            // m loop kept rolled (register pressure); U's zeros are masked
-#pragma unroll
-            for (int j = 0; j < N; ++j) h[j] = 0.f;
-#pragma unroll 2
-            for (int m = 0; m < N; ++m) {
-                const float gm = gt[i * N + m];
-#pragma unroll
-                for (int j = 0; j < N; ++j) {
-                    const float ujm = (m > j) ? xt[j * N + m] : ((m == j) ? 1.f : 0.f);
-                    h[j] = fmaf(gm, ujm, h[j]);
-                }
-            }
         }
         // row i's terms of g_k = sum_r L_rk H_rk (L_ik = X_ik for k < i, L_ii = 1)
 #pragma unroll
@@ -169,7 +158,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_bwd_kernel(const float* _
         float u[N];
 #pragma unroll
         for (int j = 0; j < N; ++j) u[j] = 0.f;
-#pragma unroll(N <= 8 ? N : 2)
+#pragma unroll
         for (int m = 0; m < N; ++m) {
             const float coef = (m > i) ? xt[m * N + i] : ((m == i) ? 1.f : 0.f);
 #pragma unroll
@@ -225,71 +214,56 @@ hipError_t run_build_bwd(const float* x, const float* dM, float* dx, int64_t nto
 }
 
 // n = 16, 32 on the matrix cores.  M = Lt W, Lt the unit lower factor and
-// W = diag(e) U, as fp32 16x16x4 products (v_mfma_f32_16x16x4f32: A[i][k] in
-// lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane j + 16(i/4), register
-// i%4); tile (I, J) sums the k-tiles K <= min(I, J) (the others are zero).  One
-// wave per token: the token is staged in LDS, its diagonal summed over a
-// 16-lane row with DPP (each lane adds N/16 entries first), e formed by lanes
-// 0..N-1, then every lane reads its operand entries of Lt and W.  The lanes of
-// a row read the same k; everything else is registers.
-__device__ inline float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    return v;
-}
-
+// W = diag(e) U, as fp64 16x16x4 products (ldu_tile_f64) with e in fp64, so
+// each entry is the exact product up to fp64 rounding and is rounded to fp32
+// once: M is the correctly rounded LDU product (an fp32 accumulation here was
+// three times the rounding error, mostly the fp32 exponential on the diagonal,
+// and the gradient of a long scan amplifies exactly that input error).  One
+// wave per token: the token is staged in LDS, its diagonal summed in fp64 over
+// a 16-lane row with DPP, e formed by lanes 0..N-1, then every lane reads its
+// operand entries of Lt and W; tile (I, J) sums the k-tiles K <= min(I, J).
 template <int N>
 __global__ __launch_bounds__(64) void build_mfma_kernel(const float* __restrict__ x,
                                                        float* __restrict__ M, int64_t ntok) {
     static_assert(N == 16 || N == 32, "matrix-core build for n = 16, 32");
-    typedef float f4 __attribute__((ext_vector_type(4)));
     constexpr int NT = N / 16;
     constexpr int NN = N * N;
     constexpr int LS = N + 4;       // LDS row stride (floats)
     constexpr int NV = NN / 256;    // float4 pieces per lane and token
     __shared__ __align__(16) float xs[N * LS];
-    __shared__ float es[N];
+    __shared__ __align__(16) float ms[N * LS];  // the token's M, row-major, for whole-row stores
+    __shared__ double ed[N];
+    __shared__ float ef[N];
+    // native vector type: an array of HIP's float4 (a union) kept across the
+    // barrier was not promoted to registers and went through scratch memory
+    typedef float f4 __attribute__((ext_vector_type(4)));
     const int l = threadIdx.x;
     for (int64_t tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
-        float4 v[NV];
+        f4 v[NV];
 #pragma unroll
-        for (int q = 0; q < NV; ++q) v[q] = reinterpret_cast<const float4*>(x + tok * NN)[q * 64 + l];
+        for (int q = 0; q < NV; ++q) v[q] = reinterpret_cast<const f4*>(x + tok * NN)[q * 64 + l];
         __syncthreads();  // the previous token's reads are done
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
             const int f = q * 64 + l;
-            *reinterpret_cast<float4*>(xs + (f / (N / 4)) * LS + 4 * (f % (N / 4))) = v[q];
+            *reinterpret_cast<f4*>(xs + (f / (N / 4)) * LS + 4 * (f % (N / 4))) = v[q];
         }
         __syncthreads();
-        float dsum = 0.f;
-#pragma unroll
-        for (int m = 0; m < NT; ++m) dsum += xs[((l & 15) + 16 * m) * (LS + 1)];
-        const float mean = row16_sum(dsum) * (1.0f / N);  // exact scaling by 1/n
-        if (l < N) es[l] = expf(xs[l * (LS + 1)] - mean);
+        token_e_f64<N>(xs, ed, ef);
         __syncthreads();
-        float* out = M + tok * NN;
 #pragma unroll
         for (int I = 0; I < NT; ++I)
 #pragma unroll
             for (int J = 0; J < NT; ++J) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-                const int i = 16 * I + (l & 15);
-                const int j = 16 * J + (l & 15);
+                // D[i][j] = M[16I + i][16J + j]: lane l, register r holds row 4r + l/16
+                const f64x4 acc = ldu_tile_f64<N, false>(
+                    xs, ed, I, J, [&](int i) { return 16 * I + i; }, [&](int j) { return 16 * J + j; });
 #pragma unroll
-                for (int K = 0; K <= (I < J ? I : J); ++K)
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const int k = 16 * K + 4 * s4 + (l >> 4);
-                        const float a = k < i ? xs[i * LS + k] : (k == i ? 1.f : 0.f);
-                        const float ek = es[k];
-                        const float b = j > k ? ek * xs[k * LS + j] : (j == k ? ek : 0.f);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-                    }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) out[(16 * I + 4 * (l >> 4) + r) * N + j] = acc[r];
+                for (int r = 0; r < 4; ++r)
+                    ms[(16 * I + 4 * r + (l >> 4)) * LS + 16 * J + (l & 15)] = float(acc[r]);
             }
+        __syncthreads();
+        store_rows_from_lds<N>(M + tok * NN, ms);
     }
 }
 
@@ -318,104 +292,38 @@ __global__ __launch_bounds__(64) void build_bwd_mfma_kernel(const float* __restr
                                                            const float* __restrict__ dM,
                                                            float* __restrict__ dx, int64_t ntok) {
     static_assert(N == 16 || N == 32, "matrix-core build backward for n = 16, 32");
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    constexpr int NT = N / 16;
     constexpr int NN = N * N;
     constexpr int LS = N + 4;
     constexpr int NV = NN / 256;
     __shared__ __align__(16) float xs[N * LS];
     __shared__ __align__(16) float gs[N * LS];
+    __shared__ __align__(16) float ds[N * LS];  // the token's dx, row-major, for whole-row stores
+    __shared__ double ed[N];
     __shared__ float es[N];
     __shared__ float part[4];
+    typedef float f4 __attribute__((ext_vector_type(4)));  // (registers, as above)
     const int l = threadIdx.x;
-    const int m = l >> 4;  // lane row: accumulator rows 4m .. 4m+3 of each tile
     for (int64_t tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
-        float4 vx[NV], vg[NV];
+        f4 vx[NV], vg[NV];
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
-            vx[q] = reinterpret_cast<const float4*>(x + tok * NN)[q * 64 + l];
-            vg[q] = reinterpret_cast<const float4*>(dM + tok * NN)[q * 64 + l];
+            vx[q] = reinterpret_cast<const f4*>(x + tok * NN)[q * 64 + l];
+            vg[q] = reinterpret_cast<const f4*>(dM + tok * NN)[q * 64 + l];
         }
         __syncthreads();  // the previous token's reads are done
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
             const int f = q * 64 + l;
             const int off = (f / (N / 4)) * LS + 4 * (f % (N / 4));
-            *reinterpret_cast<float4*>(xs + off) = vx[q];
-            *reinterpret_cast<float4*>(gs + off) = vg[q];
+            *reinterpret_cast<f4*>(xs + off) = vx[q];
+            *reinterpret_cast<f4*>(gs + off) = vg[q];
         }
         __syncthreads();
-        float dsum = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) dsum += xs[((l & 15) + 16 * t) * (LS + 1)];
-        const float mean = row16_sum(dsum) * (1.0f / N);
-        if (l < N) es[l] = expf(xs[l * (LS + 1)] - mean);
+        token_e_f64<N>(xs, ed, es);  // e as the build forms it, rounded to fp32
         __syncthreads();
-        f4 h[NT][NT], u[NT][NT];  // H and L^T G, accumulator layout
-        float eg = 0.f;           // sum over this lane row's diagonal entries of e_i g_i
-#pragma unroll
-        for (int I = 0; I < NT; ++I)
-#pragma unroll
-            for (int J = 0; J < NT; ++J) {
-                const int i = 16 * I + (l & 15);  // A-operand row
-                const int j = 16 * J + (l & 15);  // B-operand column
-                f4 ah = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int K = J; K < NT; ++K)  // H = G U^T: U[j][k] = 0 for k < j
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const int k = 16 * K + 4 * s4 + m;
-                        const float a = gs[i * LS + k];
-                        const float b = k > j ? xs[j * LS + k] : (k == j ? 1.f : 0.f);
-                        ah = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, ah, 0, 0, 0);
-                    }
-#pragma unroll
-                for (int K = I; K < NT; ++K)  // L^T G: L[k][i] = 0 for k < i
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const int k = 16 * K + 4 * s4 + m;
-                        const float a = k > i ? xs[k * LS + i] : (k == i ? 1.f : 0.f);
-                        const float b = gs[k * LS + j];
-                        au = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, au, 0, 0, 0);
-                    }
-                h[I][J] = ah;
-                u[I][J] = au;
-            }
-        // g_i for this lane row's rows i = 16I + 4m + r
-        float g[NT][4];
-#pragma unroll
-        for (int I = 0; I < NT; ++I)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * m + r;
-                float p = 0.f;
-#pragma unroll
-                for (int J = 0; J < NT; ++J) {
-                    const int j = 16 * J + (l & 15);
-                    const float uij = j > i ? xs[i * LS + j] : (j == i ? 1.f : 0.f);
-                    p = fmaf(u[I][J][r], uij, p);
-                }
-                g[I][r] = row16_sum(p);
-                eg += es[i] * g[I][r];
-            }
-        if ((l & 15) == 0) part[m] = eg;
+        build_vjp_token<N>(xs, gs, es, part, ds);
         __syncthreads();
-        const float meaneg = (((part[0] + part[1]) + part[2]) + part[3]) * (1.0f / N);
-        float* out = dx + tok * NN;
-#pragma unroll
-        for (int I = 0; I < NT; ++I)
-#pragma unroll
-            for (int J = 0; J < NT; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * m + r;
-                    const int j = 16 * J + (l & 15);
-                    float v;
-                    if (i > j) v = es[j] * h[I][J][r];
-                    else if (i < j) v = es[i] * u[I][J][r];
-                    else v = es[i] * g[I][r] - meaneg;
-                    out[i * N + j] = v;
-                }
+        store_rows_from_lds<N>(dx + tok * NN, ds);
     }
 }
 
@@ -437,19 +345,12 @@ hipError_t run_build_mfma(const float* x, float* M, int64_t ntok, hipStream_t st
     return hipGetLastError();
 }
 
-// Rows per lane of the vector-ALU build (n = 4, 8; overridable at build time for
-// tuning sweeps).
-#ifndef MRU_BUILD_R4
-#define MRU_BUILD_R4 1
-#endif
-#ifndef MRU_BUILD_R8
-#define MRU_BUILD_R8 1
-#endif
+// The vector-ALU build (n = 4, 8) gives each lane one row of M (measured best).
 
 hipError_t launch_build(const float* x, float* M, int64_t ntok, int n, hipStream_t stream) {
     switch (n) {
-        case 4: return run_build<4, MRU_BUILD_R4>(x, M, ntok, stream);
-        case 8: return run_build<8, MRU_BUILD_R8>(x, M, ntok, stream);
+        case 4: return run_build<4, 1>(x, M, ntok, stream);
+        case 8: return run_build<8, 1>(x, M, ntok, stream);
         case 16: return run_build_mfma<16>(x, M, ntok, stream);
         case 32: return run_build_mfma<32>(x, M, ntok, stream);
         default: return hipErrorInvalidValue;

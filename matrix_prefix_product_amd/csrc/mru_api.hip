@@ -15,6 +15,11 @@ __global__ void ws_reset_kernel(uint32_t* words, int64_t nwords) {
         words[i] = 0u;
 }
 
+// Copies the status word of a workspace header to *out (0 without a header).
+__global__ void ws_status_kernel(const WsHeader* hdr, int32_t* out) {
+    if (threadIdx.x == 0) *out = hdr ? int32_t(ws_load(&hdr->status)) : 0;
+}
+
 namespace {
 
 constexpr int64_t kMaxT = int64_t(1) << 30;
@@ -155,6 +160,7 @@ const char* mru_status_string(int32_t status) {
         case MRU_ERR_WORKSPACE: return "MRU_ERR_WORKSPACE: workspace missing or too small";
         case MRU_ERR_CHUNK: return "MRU_ERR_CHUNK: chunk must be >= 0";
         case MRU_ERR_HIP: return "MRU_ERR_HIP: the HIP runtime reported a launch error";
+        case MRU_ERR_TIMEOUT: return "MRU_ERR_TIMEOUT: a look-back wait of a scan timed out; its outputs are invalid";
         default: return "unknown mru_status";
     }
 }
@@ -205,11 +211,27 @@ int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direc
     return int32_t(auto_chunk_len(S, T, n, direction == MRU_DIR_BWD ? 1 : 0));
 }
 
-size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
-                                int32_t chunk) {
+size_t mru_scan_workspace_bytes_chunked(int64_t B, int64_t H, int64_t T, int32_t n,
+                                        int32_t direction, int32_t chunk) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems) || elems == 0 || chunk < 0) return 0;
     return make_plan(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, chunk).ws;
+}
+
+size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction) {
+    return mru_scan_workspace_bytes_chunked(B, H, T, n, direction, 0);
+}
+
+mru_status mru_scan_ws_status(const void* ws, size_t ws_bytes, int32_t* status, void* stream) {
+    if (!status) return MRU_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return MRU_ERR_ALIGN;
+    const bool has_header = ws && ws_bytes >= sizeof(WsHeader);
+    if (has_header && !aligned16(ws)) return MRU_ERR_ALIGN;
+    if (has_header && overlap(ws, sizeof(WsHeader), status, 4)) return MRU_ERR_ALIAS;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ws_status_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       has_header ? static_cast<const WsHeader*>(ws) : nullptr, status);
+    return launched(hipGetLastError());
 }
 
 int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction,
@@ -281,7 +303,6 @@ mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float*
                          bool to_dx = false) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
-    if ((from_x || to_dx) && n > 8) return MRU_ERR_SHAPE;
     if (chunk < 0) return MRU_ERR_CHUNK;
     if (elems == 0) return MRU_OK;
     if (!M || !P || !dP || !dM) return MRU_ERR_NULL;
@@ -317,7 +338,7 @@ mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float*
     if (n <= 8)
         return launched(
             launch_bwd_valu(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, to_dx, cy));
-    return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, cy));
+    return launched(launch_bwd_mfma(M, P, dP, dM, S, T, n, p.K, p.nch, p.Z, ws, s, from_x, to_dx, cy));
 }
 
 }  // namespace
@@ -325,7 +346,13 @@ mru_status scan_bwd_impl(const float* M, const float* P, const float* dP, float*
 extern "C" {
 
 mru_status mru_scan_fwd(const float* M, float* P, int64_t B, int64_t H, int64_t T, int32_t n,
-                        int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+                        void* ws, size_t ws_bytes, void* stream) {
+    return scan_fwd_impl(M, P, B, H, T, n, 0, ws, ws_bytes, stream, false, ScanCarry{});
+}
+
+mru_status mru_scan_fwd_chunked(const float* M, float* P, int64_t B, int64_t H, int64_t T,
+                                int32_t n, int32_t chunk, void* ws, size_t ws_bytes,
+                                void* stream) {
     return scan_fwd_impl(M, P, B, H, T, n, chunk, ws, ws_bytes, stream, false, ScanCarry{});
 }
 
@@ -335,8 +362,14 @@ mru_status mru_scan_fwd_x(const float* x, float* P, int64_t B, int64_t H, int64_
 }
 
 mru_status mru_scan_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t B,
-                        int64_t H, int64_t T, int32_t n, int32_t chunk, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        int64_t H, int64_t T, int32_t n, void* ws, size_t ws_bytes,
+                        void* stream) {
+    return scan_bwd_impl(M, P, dP, dM, B, H, T, n, 0, ws, ws_bytes, stream, false, ScanCarry{});
+}
+
+mru_status mru_scan_bwd_chunked(const float* M, const float* P, const float* dP, float* dM,
+                                int64_t B, int64_t H, int64_t T, int32_t n, int32_t chunk,
+                                void* ws, size_t ws_bytes, void* stream) {
     return scan_bwd_impl(M, P, dP, dM, B, H, T, n, chunk, ws, ws_bytes, stream, false, ScanCarry{});
 }
 

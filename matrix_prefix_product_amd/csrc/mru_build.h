@@ -35,35 +35,22 @@ __device__ inline float ldu_mean_diag(const float (&d)[N]) {
     return sum * (1.0f / N);
 }
 
-// acc[j] = M_ij for j = 0..N-1, given e[k] = exp(X_kk - mean).  The k loop is
-// fully unrolled for N <= 16 (U's zero pattern resolved at compile time) and
-// kept rolled with U's zeros masked for N = 32 (register pressure); both add
-// the same products in the same order.
+// acc[j] = M_ij for j = 0..N-1, given e[k] = exp(X_kk - mean); n = 4, 8 (the
+// matrix-core build covers n = 16, 32).  The k loop is fully unrolled, so U's
+// zero pattern is resolved at compile time.
 template <int N, class E>
 __device__ inline void ldu_row(const float* X, int i, const E& e, float (&acc)[N]) {
+    static_assert(N == 4 || N == 8, "vector-ALU rows for n = 4, 8");
 #pragma unroll
     for (int j = 0; j < N; ++j) acc[j] = 0.f;
-    if constexpr (N <= 16) {
 #pragma unroll
-        for (int k = 0; k < N; ++k) {
-            const float ek = e(k);
-            const float coef = (k < i) ? X[i * N + k] * ek : ((k == i) ? ek : 0.f);
+    for (int k = 0; k < N; ++k) {
+        const float ek = e(k);
+        const float coef = (k < i) ? X[i * N + k] * ek : ((k == i) ? ek : 0.f);
 #pragma unroll
-            for (int j = k; j < N; ++j) {
-                const float u = (j == k) ? 1.f : X[k * N + j];
-                acc[j] = fmaf(coef, u, acc[j]);
-            }
-        }
-    } else {
-#pragma unroll 2
-        for (int k = 0; k < N; ++k) {
-            const float ek = e(k);
-            const float coef = (k < i) ? X[i * N + k] * ek : ((k == i) ? ek : 0.f);
-#pragma unroll
-            for (int j = 0; j < N; ++j) {
-                const float u = (j > k) ? X[k * N + j] : ((j == k) ? 1.f : 0.f);
-                acc[j] = fmaf(coef, u, acc[j]);
-            }
+        for (int j = k; j < N; ++j) {
+            const float u = (j == k) ? 1.f : X[k * N + j];
+            acc[j] = fmaf(coef, u, acc[j]);
         }
     }
 }

@@ -83,56 +83,29 @@ __device__ inline void store_flag(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Publishing protocol of the look-back workspace.
-//
-// MRU_WS_COHERENT = 1 (default): every published matrix entry and every flag is
-// written and read with agent-scope atomic accesses, which the compiler makes
-// coherent across all XCDs of the device (they bypass the per-XCD L2 for this
-// data).  A writer waits for its data stores to complete (vmcnt 0) before it
-// stores the flag; a reader only issues its data loads after it has seen the
-// flag.  No cache-wide write-back or invalidate is needed, so other waves'
-// streaming traffic through L2 is not disturbed.
-// MRU_WS_COHERENT = 0: plain accesses with agent-scope release / acquire
-// fences (L2 write-back and invalidate).
-#ifndef MRU_WS_COHERENT
-#define MRU_WS_COHERENT 1
-#endif
-
+// Publishing protocol of the look-back workspace: every published matrix entry
+// and every flag is written and read with agent-scope atomic accesses, which
+// the compiler makes coherent across all XCDs of the device (they bypass the
+// per-XCD L2 for this data).  A writer waits for its data stores to complete
+// (vmcnt 0) before it stores the flag; a reader only issues its data loads
+// after it has seen the flag.  No cache-wide write-back or invalidate is
+// needed, so other waves' streaming traffic through L2 is not disturbed.
 template <class T>
 __device__ inline void ws_store(T* p, T v) {
-#if MRU_WS_COHERENT
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-    *p = v;
-#endif
 }
 
 template <class T>
 __device__ inline T ws_load(const T* p) {
-#if MRU_WS_COHERENT
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-    return *p;
-#endif
 }
 
 // Between a writer's data stores and its flag store.
-__device__ inline void fence_release() {
-#if MRU_WS_COHERENT
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#else
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-#endif
-}
+__device__ inline void fence_release() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Between a reader's flag loads and its data loads.
-__device__ inline void fence_acquire() {
-#if MRU_WS_COHERENT
-    __asm__ volatile("" ::: "memory");
-#else
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#endif
-}
+// Between a reader's flag loads and its data loads (the data loads are issued
+// only after the flag value is known; this keeps the compiler from hoisting them).
+__device__ inline void fence_acquire() { __asm__ volatile("" ::: "memory"); }
 
 // Ticket order of a multi-chunk scan: ticket t takes chunk group t / S of
 // sequence t % S, i.e. sequences are interleaved.  Chunks that run at the same

@@ -35,8 +35,8 @@ struct ScanCarry {
 // sequence (possibly padded with empty chunks), supers of Z chunks.  nch == 1
 // runs without workspace; nch > 1 needs a cleared workspace header and flags.
 // from_x: the first array holds raw token vectors and the kernel builds the
-// input matrices on the fly (never writing them); forward n = 4, 8, 16, 32,
-// backward n = 4, 8.  to_dx (backward, with
+// input matrices on the fly (never writing them); n = 4, 8, 16, 32.  to_dx
+// (backward, with
 // from_x): the output is dL/dx, the gradient through the build, instead of dL/dM.
 hipError_t launch_fwd_valu(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
                            int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
@@ -49,7 +49,7 @@ hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n
                            const ScanCarry& cy);
 hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream, const ScanCarry& cy);
+                           hipStream_t stream, bool from_x, bool to_dx, const ScanCarry& cy);
 
 // Tokens per chunk the matrix-core forward kernel keeps in registers between
 // its two passes (0 = none): chunks of at most this length read M once.

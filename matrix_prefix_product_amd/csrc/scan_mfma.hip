@@ -22,13 +22,12 @@
 #include "mru_device.h"
 #include "mru_kernels.h"
 #include "mru_build.h"
+#include "mru_build_mfma.h"
 #include "mru_mfma.h"
 
 // Prefetch depth of the retained n = 16 aggregate pass (tokens in flight; the
 // whole chunk is held in registers anyway, so depth costs no registers).
-#ifndef MRU_PFR16
-#define MRU_PFR16 16
-#endif
+constexpr int kPfRetain16 = 16;
 
 namespace mru {
 namespace {
@@ -251,26 +250,35 @@ __device__ inline void operand_from(typename Mf<N>::aop_t& a, const float (&o)[4
 // diagonal) and W = diag(e) U (W_kc = e_k X_kc for k < c, e_k on the diagonal),
 // e_k = exp(X_kk - mean_j X_jj) ("Improving Matrix Recurrent Units as an
 // Attention Alternative", Key Points: LDU fill, determinant-correcting
-// scalar).  The product runs on the matrix core in fp32 (four
-// v_mfma_f32_16x16x4f32, D[i][j] in lane j + 16(i/4), register i%4): taking
-// W's columns in the order tacol, lane l's results are exactly its A-operand
-// entries M[16K + trow(l, b)][16I + tacol(l)] of the fp64 chain.  Three phases,
-// separated by barriers and spread between the chain's products:
+// scalar).  The product runs on the matrix core in fp64 and is rounded once to
+// fp32, exactly as the build kernel forms M (ldu_tile_f64): taking M's rows in
+// the order pi and its columns in the order tacol, lane l's results are
+// exactly its A-operand entries M[16K + trow(l, b)][16I + tacol(l)] of the fp64
+// chain.  Three phases, separated by barriers and spread between the chain's
+// products:
 //   stage:   every lane writes its 16-byte piece of X row-major to the slot;
-//   factors: every lane reads X_kk for k = l%16, sums the 16 over its row of
-//            lanes (DPP butterfly: each step adds two values in either order,
-//            so every lane gets the same bits), forms e_{l%16}; lanes 0..15
-//            write e to the slot;
-//   read:    every lane reads its 4 entries of Lt and of W from X and e and
-//            issues the four fp32 products.
+//   factors: every lane sums X_kk in fp64 over its 16-lane row (DPP butterfly:
+//            each step adds two values in either order, so every lane gets the
+//            same bits) and forms e; lanes 0..n-1 write e to the slot (fp64,
+//            and rounded to fp32 for the gradient's fp32 arithmetic);
+//   read:    every lane reads its entries of Lt and of W from X and e and
+//            issues the fp64 products.
 // A slot (X, e) per token parity, as the transpose buffers.
 template <int N>
 struct StageX {
-    static_assert(N == 16 || N == 32, "the forward from raw token vectors: n = 16, 32");
+    static_assert(N == 16 || N == 32, "the scans from raw token vectors: n = 16, 32");
     static constexpr int LS = Stage<N>::LS;
-    static constexpr int BUF = Stage<N>::BUF;
-    static constexpr int SLOT = BUF + N;  // floats: X (row stride LS), e
+    static constexpr int BUF = Stage<N>::BUF;      // X (row stride LS)
+    static constexpr int ED = BUF;                 // e in fp64 (N doubles)
+    static constexpr int EF = BUF + 2 * N;         // e rounded to fp32 (N floats)
+    static constexpr int SLOT = BUF + 3 * N;       // floats per slot
+    static_assert(BUF % 4 == 0 && SLOT % 4 == 0, "16-byte aligned rows, 8-byte aligned e");
 };
+
+template <int N>
+__device__ inline const double* slot_ed(const float* slot) {
+    return reinterpret_cast<const double*>(slot + StageX<N>::ED);
+}
 
 template <int N>
 __device__ inline void xop_stage(const float (&v)[4 * Stage<N>::NV], float* slot) {
@@ -284,60 +292,53 @@ __device__ inline void xop_stage(const float (&v)[4 * Stage<N>::NV], float* slot
     }
 }
 
-// Sum over each row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
-// row_half_mirror, row_mirror).
-__device__ inline float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    return v;
-}
-
 template <int N>
 __device__ inline void xop_factors(float* slot) {
-    using SX = StageX<N>;
-    constexpr int NT = N / 16;
-    const int l = threadIdx.x & 63;
-    float dsum = 0.f;  // X_kk for k = l%16 (+ 16, n = 32)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dsum += slot[((l & 15) + 16 * t) * (SX::LS + 1)];
-    const float mean = row16_sum(dsum) * (1.0f / N);  // exact scaling by 1/n
-    const int k = l & (N - 1);
-    const float ek = expf(slot[k * (SX::LS + 1)] - mean);
-    if (l < N) slot[SX::BUF + l] = ek;
+    token_e_f64<N>(slot, reinterpret_cast<double*>(slot + StageX<N>::ED), slot + StageX<N>::EF);
 }
 
-// Operand entries o[(I * NT + K) * 4 + b] = M[16K + trow(l, b)][16I + tacol(l)]:
-// output tile (K, I) of Lt W with W's columns in the order tacol, summing the
-// k-tiles T <= min(K, I) (the others are zero).
+// pi(i) = 4(i%4) + i/4: the row relabelling of the f64 accumulator tile (a
+// lane of row group q holds rows 4q .. 4q+3 of the chain's operand).
+__device__ inline int pirow(int i) { return 4 * (i & 3) + (i >> 2); }
+
+// Operand entries o[(I * NT + K) * 4 + b] = M[16K + trow(l, b)][16I + tacol(l)]
+// of the forward chain (A operand of M^T): tile (K, I) of M with its rows taken
+// in the order pi and its columns in the order tacol, so that lane l's four
+// accumulator entries are exactly these (ldu_tile_f64, rounded to fp32 as the
+// build rounds M).
 template <int N>
 __device__ inline void xop_read(float (&o)[4 * Stage<N>::NV], const float* slot) {
-    using SX = StageX<N>;
     constexpr int NT = N / 16;
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const int l = threadIdx.x & 63;
 #pragma unroll
     for (int I = 0; I < NT; ++I)
 #pragma unroll
         for (int K = 0; K < NT; ++K) {
-            const int i = 16 * K + (l & 15);  // row of Lt this lane supplies (A operand)
-            const int c = 16 * I + tacol(l);  // column of W this lane supplies (B operand)
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            const f64x4 acc = ldu_tile_f64<N, false>(
+                slot, slot_ed<N>(slot), K, I, [&](int i) { return 16 * K + pirow(i); },
+                [&](int j) { return 16 * I + tacol(j); });
 #pragma unroll
-            for (int T = 0; T <= (K < I ? K : I); ++T)
+            for (int r = 0; r < 4; ++r) o[(I * NT + K) * 4 + r] = float(acc[r]);
+        }
+}
+
+// The backward's A operand of M itself (not M^T): o[(I * NT + K) * 4 + b] =
+// M[16I + tacol(l)][16K + trow(l, b)], as load_a_direct reads it: the
+// transposed form of tile (I, K) (ldu_tile_f64 with TR), rows in the order
+// tacol, columns in the order pi.  Every entry of M is the same sum of the same
+// products as in xop_read and in the build kernel, so M is bit for bit the
+// matrix the build writes.
+template <int N>
+__device__ inline void xop_read_direct(float (&o)[4 * Stage<N>::NV], const float* slot) {
+    constexpr int NT = N / 16;
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int k = 16 * T + 4 * s4 + (l >> 4);
-                    const float xik = slot[i * SX::LS + k];
-                    const float xkc = slot[k * SX::LS + c];
-                    const float ek = slot[SX::BUF + k];
-                    const float a = k < i ? xik : (k == i ? 1.f : 0.f);
-                    const float b = c > k ? ek * xkc : (c == k ? ek : 0.f);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-                }
+    for (int I = 0; I < NT; ++I)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[(I * NT + K) * 4 + r] = acc[r];
+        for (int K = 0; K < NT; ++K) {
+            const f64x4 acc = ldu_tile_f64<N, true>(
+                slot, slot_ed<N>(slot), I, K, [&](int j) { return 16 * I + tacol(j); },
+                [&](int i) { return 16 * K + pirow(i); });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[(I * NT + K) * 4 + r] = float(acc[r]);
         }
 }
 
@@ -581,13 +582,12 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(typename Mf<N>::
     if (len > 0) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
 }
 
-// Waves per SIMD the forward kernel is register-budgeted for (tuning knob).
-#ifndef MRU_MFMA_FWD_WAVES
-#define MRU_MFMA_FWD_WAVES 1
-#endif
+// One wave per SIMD: the forward keeps a chunk's operands (n = 16) or a deep
+// operand ring (n = 32) in the whole register file.  Register-capped variants
+// at two waves per SIMD were measured no faster.
 
 template <int N, int PF, int KR, bool FX, bool SC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MRU_MFMA_FWD_WAVES)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
@@ -629,7 +629,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0)
-        fwd_pass_retain<N, KR, (N == 16 ? MRU_PFR16 : PF), FX, SC>(X, ex, M, ch.base, ch.len, buf, tlds, xlds);
+        fwd_pass_retain<N, KR, (N == 16 ? kPfRetain16 : PF), FX, SC>(X, ex, M, ch.base, ch.len, buf, tlds, xlds);
     else
         fwd_sweep<N, PF, false, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
     const int a_ex = ex;
@@ -705,21 +705,59 @@ void fwd_mfma_kernel(const float* __restrict__ M,
 
 // ---------------------------------------------------------------------------- backward
 
+// A operand of M (load_a_direct's layout) from the raw token vector at xt: the
+// token is loaded, staged in LDS slot xs and multiplied out on the matrix core
+// (xop_stage, xop_factors, xop_read_direct).  Wave-uniform; xs is free on entry.
+template <int N>
+__device__ inline void x_operand_direct(typename Mf<N>::aop_t& a, const float* xt, float* xs) {
+    constexpr int NA = 4 * Stage<N>::NV;
+    const int l = threadIdx.x & 63;
+    float v[NA], o[NA];
+#pragma unroll
+    for (int q = 0; q < Stage<N>::NV; ++q) {
+        const float4 w = reinterpret_cast<const float4*>(xt)[q * 64 + l];
+        v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+    __syncthreads();
+    xop_stage<N>(v, xs);
+    __syncthreads();
+    xop_factors<N>(xs);
+    __syncthreads();
+    xop_read_direct<N>(o, xs);
+    operand_from<N>(a, o);
+}
+
 // Reverse sweep over the chunk (positions len-1 .. 0).
 //   AGG:  G <- dP_t^T + M_{t+1} G from G = 0 and W <- M_{t+1} W from W = I.
 //   GRAD: G <- dP_t^T + M_{t+1} G from the carry; dM_t^T = G_t P_{t-1}.
 // At the last token of a sequence there is no M_{t+1}: G <- dP_t^T.
-template <int N, int PF, bool GRAD>
-__device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
+// FX: M holds raw token vectors and each input matrix is formed on chip (the
+// LDU factors of the build, "Improving Matrix Recurrent Units as an Attention
+// Alternative", Key Points) from the token staged in the LDS slots xs (two,
+// alternating by step).  Step i stages its own token x_t and forms from it the
+// A operand of M_t, which is the next step's M_{t+1}: every token is staged
+// once, and the operand is ready a whole step before the chain needs it (the
+// chunk's first step takes the operand of the token after the chunk from the
+// prologue).
+// DX (with FX and GRAD): the output is dL/dx_t instead of dM_t.  dM_t, rounded
+// to fp32 as the backward to dM stores it, goes through LDS (gs) with the
+// staged x_t and its e into build_vjp_token, the same routine as the build's
+// gradient kernel, so dx is bit for bit build_inputs_bwd(x, dM); dxl holds gs,
+// the dx staging ds (both row stride n + 4) and 4 floats for the mean.
+template <int N, int PF, bool GRAD, bool FX, bool DX>
+__device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                           const float* __restrict__ M, const float* __restrict__ P,
                           const float* __restrict__ dP, float* __restrict__ dM, double* tr,
-                          int64_t base, int64_t t0, int len, int64_t T, const ScanCarry& cy) {
+                          float* xs, float* dxl, int64_t base, int64_t t0, int len, int64_t T,
+                          const ScanCarry& cy) {
+    static_assert(!DX || (FX && GRAD), "the gradient to x starts from raw token vectors");
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NT = F::NT;
     constexpr int NN = F::NN;
     constexpr int NA = NT * NT * 4;
     constexpr int TS = N + 1;  // LDS row stride of the transpose buffer
+    constexpr int LS = N + 4;  // row stride of the token and gradient staging
     if (len <= 0) return;
     const int l = threadIdx.x & 63;
     const int c = tcol(l);
@@ -732,23 +770,35 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
     const float* Pb = P + base * NN;
     const float* Rb = dP + base * NN;
 
-    // ring of prefetched operands per token: M_{t+1} (A operand, runs of 4),
-    // dP_t (C operand, runs of 4), P_{t-1} (B operand of the dM product).  (Read
-    // non-temporally the backward was faster launch after launch, but slower
-    // right after the forward, as in a training step: ordinary accesses.)
+    // ring of prefetched operands per token: M_{t+1} (A operand, runs of 4; FX:
+    // the raw token x_t itself), dP_t (C operand, runs of 4), P_{t-1} (B operand
+    // of the dM product).  (Read non-temporally the backward was faster launch
+    // after launch, but slower right after the forward, as in a training step:
+    // ordinary accesses.)
     float rm[PF][NA], rr[PF][NA], rp[PF][GRAD ? NA : 1];
     auto fetch = [&](int slot, int i) {
         const int pos = max(len - 1 - i, 0);
-        const int pm = min(pos, hi_m - 1) + 1;  // clamped: only used when pos < hi_m
+        if constexpr (FX) {
+            // the raw token x_t, row-major 16-byte pieces (as load_token)
 #pragma unroll
-        for (int I = 0; I < NT; ++I)
-#pragma unroll
-            for (int K = 0; K < NT; ++K) {
-                const float4 v = *reinterpret_cast<const float4*>(
-                    Mb + int64_t(hi_m > 0 ? pm : pos) * NN + (16 * I + ac) * N + 16 * K + trow(l, 0));
-                float* d = &rm[slot][(I * NT + K) * 4];
+            for (int q = 0; q < Stage<N>::NV; ++q) {
+                const float4 v = reinterpret_cast<const float4*>(Mb + int64_t(pos) * NN)[q * 64 + l];
+                float* d = &rm[slot][4 * q];
                 d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
             }
+        } else {
+            const int pm = min(pos, hi_m - 1) + 1;  // clamped: only used when pos < hi_m
+            const float* mt = Mb + int64_t(hi_m > 0 ? pm : pos) * NN;
+#pragma unroll
+            for (int I = 0; I < NT; ++I)
+#pragma unroll
+                for (int K = 0; K < NT; ++K) {
+                    const float4 v = *reinterpret_cast<const float4*>(
+                        mt + (16 * I + ac) * N + 16 * K + trow(l, 0));
+                    float* d = &rm[slot][(I * NT + K) * 4];
+                    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+                }
+        }
 #pragma unroll
         for (int I = 0; I < NT; ++I)
 #pragma unroll
@@ -770,16 +820,35 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                             Pb[int64_t(pp) * NN + (16 * K + trow(l, b)) * N + 16 * J + c];
         }
     };
+    // FX: A operand of M_{t+1} for the coming step (from the previous step, or
+    // the prologue: the token after the chunk, when the sequence has one)
+    typename F::aop_t a_next;
+    if constexpr (FX) {
+        if (hi_m == len) x_operand_direct<N>(a_next, Mb + int64_t(len) * NN, xs);
+        else a_next = typename F::aop_t{};
+    }
     auto step = [&](int p, int i, bool refill) {
         const int pos = len - 1 - i;
         const bool has_next = pos < hi_m;
         typename F::aop_t a;
         vec_t cr, bv;
+        float* xsl = xs + (i & 1) * xslot<N, FX>();  // FX: this step's token slot
+        if constexpr (FX) {
+            a = a_next;
+            // x_t: stage, factors, and M_t's operand for the next step
+            float o[NA];
+            xop_stage<N>(rm[p], xsl);
+            __syncthreads();
+            xop_factors<N>(xsl);
+            __syncthreads();
+            xop_read_direct<N>(o, xsl);
+            operand_from<N>(a_next, o);
+        } else {
 #pragma unroll
-        for (int e = 0; e < NA; ++e) {
-            a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rm[p][e]);
-            cr.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rr[p][e]);
+            for (int e = 0; e < NA; ++e) a.v[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rm[p][e]);
         }
+#pragma unroll
+        for (int e = 0; e < NA; ++e) cr.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rr[p][e]);
         if constexpr (GRAD) {
 #pragma unroll
             for (int e = 0; e < NA; ++e) bv.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rp[p][e]);
@@ -805,6 +874,7 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                         for (int b = 0; b < 4; ++b)
                             bv.t[K][J][b] = double(cs[(16 * K + trow(l, b)) * N + 16 * J + c]);
             }
+            vec_t D;
             if (pos >= lo_p || cy.carry) {
                 // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
                 __syncthreads();
@@ -824,15 +894,36 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
 #pragma unroll
                         for (int b = 0; b < 4; ++b)
                             ag.v[I][K][b] = tr[(16 * I + ac) * TS + 16 * K + trow(l, b)];
-                const vec_t D = chain_step<N>(ag, bv, vzero<N>());
-                store_acc_rows<N, float>(out, D);
+                D = chain_step<N>(ag, bv, vzero<N>());
             } else {
-                store_acc_rows<N, float>(out, G);  // t = 0: P_{-1} = I
+                D = G;  // t = 0: P_{-1} = I
+            }
+            if constexpr (DX) {
+                // dM_t (fp32, row-major) into gs, then the build's gradient
+                float* gs = dxl;
+                float* ds = dxl + N * LS;
+                float* part = dxl + 2 * N * LS;
+                typedef float f4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J) {
+                        const d4 x = D.t[I][J];
+                        *reinterpret_cast<f4v*>(gs + (16 * J + tcol(l)) * LS + 16 * I + trow(l, 0)) =
+                            f4v{float(x[0]), float(x[1]), float(x[2]), float(x[3])};
+                    }
+                __syncthreads();
+                build_vjp_token<N>(xsl, gs, xsl + StageX<N>::EF, part, ds);
+                __syncthreads();
+                store_rows_from_lds<N>(out, ds);
+            } else {
+                store_acc_rows<N, float>(out, D);
             }
             if (pos < lo_p && cy.dcarry) {
                 // dL/dP_{-1} = Q_0 M_0^T, i.e. its transpose is M_0 G_0
                 typename F::aop_t am;
-                load_a_direct<N, float>(am, Mb + int64_t(pos) * NN);
+                if constexpr (FX) am = a_next;  // M_0's operand, formed from x_0 in this step
+                else load_a_direct<N, float>(am, Mb + int64_t(pos) * NN);
                 store_acc_rows<N, float>(cy.dcarry + (s0 / T) * NN, chain_step<N>(am, G, vzero<N>()));
             }
         }
@@ -849,7 +940,7 @@ __device__ void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
         if (i0 + p < len) step(p, i0 + p, false);
 }
 
-template <int N, int PF>
+template <int N, int PF, bool FX, bool DX>
 __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ P,
                                                       const float* __restrict__ dP,
@@ -862,6 +953,8 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     constexpr int NN = N * N;
     __shared__ double tr[N * (N + 1)];
     __shared__ double xl[NN];
+    __shared__ __align__(16) float xs[FX ? 2 * StageX<N>::SLOT : 4];  // FX: token slots
+    __shared__ __align__(16) float dxl[DX ? 2 * N * (N + 4) + 4 : 4];  // DX: gradient staging
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -874,7 +967,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     vec_t G = vzero<N>();
     vec_t W = videntity<N>(l);
     if (!multi) {
-        bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
+        bwd_sweep<N, PF, true, FX, DX>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy);
         return;
     }
     // Chunks run in reverse token order (position r = 0 is the sequence's last
@@ -891,7 +984,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     const bool later = r >= Z;
 
     // 1. affine aggregate
-    bwd_sweep<N, PF, false>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
+    bwd_sweep<N, PF, false, FX, false>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy);
     ws_store_acc_rows<N>(sbl + c * NN, G);
     ws_store_acc_rows<N>(swt + c * NN, W);
     fence_release();
@@ -939,7 +1032,7 @@ __global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ 
     }
 
     // 4. re-run from the carry, writing dM
-    bwd_sweep<N, PF, true>(G, W, M, P, dP, dM, tr, ch.base, ch.t0, ch.len, T, cy);
+    bwd_sweep<N, PF, true, FX, DX>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy);
 }
 
 template <int N, int PF, int KR, bool FX>
@@ -954,25 +1047,21 @@ hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, in
     return hipGetLastError();
 }
 
-template <int N, int PF>
+template <int N, int PF, bool FX, bool DX>
 hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                    int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream,
                    const ScanCarry& cy) {
-    hipLaunchKernelGGL((bwd_mfma_kernel<N, PF>), dim3(unsigned(S * nch)), dim3(64), 0, stream, M,
-                       P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
+    hipLaunchKernelGGL((bwd_mfma_kernel<N, PF, FX, DX>), dim3(unsigned(S * nch)), dim3(64), 0,
+                       stream, M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#ifndef MRU_RETAIN16
-#define MRU_RETAIN16 64
-#endif
-#ifndef MRU_PF16
-#define MRU_PF16 16
-#endif
-// Tokens of one chunk kept in registers by the n = 16 forward kernel.
-constexpr int kRetain16 = MRU_RETAIN16;
+// Tokens of one chunk kept in registers by the n = 16 forward kernel, and the
+// operand prefetch depth of its streamed sweeps (tokens in flight).
+constexpr int kRetain16 = 64;
+constexpr int kPf16 = 16;
 
 int mfma_retain_tokens(int n) { return n == 16 ? kRetain16 : 0; }
 
@@ -982,11 +1071,11 @@ hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n
     if (n == 16) {
         const bool retain = kRetain16 > 0 && nch > 1 && K <= kRetain16;
         if (from_x) {
-            if (retain) return run_fwd<16, MRU_PF16, kRetain16, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
-            return run_fwd<16, MRU_PF16, 0, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+            if (retain) return run_fwd<16, kPf16, kRetain16, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
+            return run_fwd<16, kPf16, 0, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
         }
-        if (retain) return run_fwd<16, MRU_PF16, kRetain16, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
-        return run_fwd<16, MRU_PF16, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        if (retain) return run_fwd<16, kPf16, kRetain16, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
+        return run_fwd<16, kPf16, 0, false>(M, P, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 32) {
         if (from_x) return run_fwd<32, 4, 0, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
@@ -997,9 +1086,19 @@ hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n
 
 hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
-                           hipStream_t stream, const ScanCarry& cy) {
-    if (n == 16) return run_bwd<16, 8>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
-    if (n == 32) return run_bwd<32, 2>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+                           hipStream_t stream, bool from_x, bool to_dx, const ScanCarry& cy) {
+    if (to_dx && !from_x) return hipErrorInvalidValue;
+    // the n = 32 instances from raw token vectors prefetch one token (two spill)
+    if (n == 16) {
+        if (to_dx) return run_bwd<16, 8, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        if (from_x) return run_bwd<16, 8, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        return run_bwd<16, 8, false, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+    }
+    if (n == 32) {
+        if (to_dx) return run_bwd<32, 1, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        if (from_x) return run_bwd<32, 1, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        return run_bwd<32, 2, false, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -13,8 +13,9 @@
 // Backward (gradient of sum_t <dP_t, P_t>): the chain state is R rows of
 // Q_t = dP_t + Q_{t+1} M_{t+1}^T, swept from the last token to the first, and
 // dM_t = P_{t-1}^T Q_t needs all rows of Q_t and of P_{t-1}, exchanged through
-// LDS.  The backward reads one stored prefix per TB tokens and recomputes the
-// others from it (VALU work is cheap here, HBM bytes are not).
+// LDS.  From M the backward reads every stored prefix; from raw token vectors
+// it reads one stored prefix per TB tokens and recomputes the others from it
+// (VALU work is cheap here, HBM bytes are not).
 #include <type_traits>
 
 #include "mru_build.h"
@@ -696,14 +697,16 @@ __device__ inline void dx_rows(float (&out)[R][N], const float (&d)[R][N], const
 //             q = 0, w = I; afterwards q is the chunk's local adjoint at its first
 //             token and w the rows of (M_{a+1} ... M_{b+1})^T.
 //   GRAD pass (GRAD = true):  q <- dP_t + q M_{t+1}^T from the carry, and
-//             dM_t = P_{t-1}^T Q_t written for the lane's rows.  Of P only the
-//             prefix just before each block's lowest token is read; the block's
-//             other P_{t-1} are recomputed from it by the forward recurrence
-//             P_t = P_{t-1} M_t, with the same products as the forward scan
-//             (bit for bit the stored prefixes when the forward ran one chunk per
-//             sequence, equal up to rounding otherwise).  This reads n^2 floats per
-//             block instead of per token.  With DX the output is dL/dx_t instead
-//             of dM_t (dx_rows), from the exchanged rows of P_{t-1} L_t as well.
+//             dM_t = P_{t-1}^T Q_t written for the lane's rows.  From M (FX
+//             false) every P_{t-1} is read from P, which is an input of the
+//             call.  From raw token vectors (FX) only the prefix just before
+//             each block's lowest token is read; the block's other P_{t-1} are
+//             recomputed from it by the forward recurrence P_t = P_{t-1} M_t,
+//             with the same products as the forward scan (bit for bit the
+//             stored prefixes when the forward ran one chunk per sequence, equal
+//             up to rounding otherwise).  This reads n^2 floats per block
+//             instead of per token.  With DX the output is dL/dx_t instead of
+//             dM_t (dx_rows), from the exchanged rows of P_{t-1} L_t as well.
 // At the last token of a sequence there is no M_{t+1}: q <- dP_t.
 template <int N, int R, int TB, bool GRAD, bool FX, bool DX>
 __device__ __attribute__((always_inline)) void bwd_sweep(
@@ -711,6 +714,8 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
     const float* __restrict__ dP, float* __restrict__ dM, float* lds, float* nx, float* qx,
     const ChainInfo* info, int g, int li, int maxlen, int64_t T, const ScanCarry& cy) {
     using V = Valu<N, R, TB>;
+    constexpr bool RP = !FX;     // read every prefix (else one per block)
+    constexpr int NCK = RP ? TB : 1;
     const ChainInfo me = info[g];
     const int64_t s0 = me.base - me.t0;  // token index of the sequence's first token
     const int64_t seq = s0 / T;          // its sequence
@@ -721,20 +726,30 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
     float* const pxg = qx + (V::G + g) * V::QX_STRIDE;                 // P_{t-1} rows
     float* const lxg = qx + (2 * V::G + g) * V::QX_STRIDE;             // DX: P_{t-1} L_t rows
     float4 rm[V::LD], rr[V::LD];
-    float ck[R][N];  // rows of P just before the lowest token of the next block
-    bool ck_id = false;
-    // Rows of that prefix: P itself inside the sequence, else P_0 (the carried-in
-    // state, or I).  The load is unconditional from a valid address.
-    auto load_checkpoint = [&](int blk) {
-        const int lo = max(me.len - blk - TB, 0);
-        const int64_t tc = int64_t(me.t0) + lo - 1;
+    // rows of the prefixes of the next block: RP, P_{t-1} of its tokens
+    // tau = 0 .. TB-1; else the prefix just before its lowest token
+    float ck[NCK][R][N];
+    bool ck_id[NCK];
+    // Rows of P_{tc} at token tc of the sequence: P itself inside the sequence,
+    // else P_0 (the carried-in state, or I).  The load is unconditional from a
+    // valid address.
+    auto load_prefix = [&](int u, int rel) {  // rel: token position in the chunk (>= 0)
+        const int64_t tc = int64_t(me.t0) + rel - 1;
         const float* src = P;  // idle chains (a padding chunk may lie past the array)
         if (me.len > 0) {
-            if (tc >= 0) src = P + (me.base + lo - 1) * V::NN;
+            if (tc >= 0) src = P + (me.base + rel - 1) * V::NN;
             else if (cy.carry) src = cy.carry + seq * V::NN;
         }
-        ck_id = tc < 0 && !cy.carry;
-        load_rows<N, R>(ck, src + li * R * N);
+        ck_id[u] = tc < 0 && !cy.carry;
+        load_rows<N, R>(ck[u], src + li * R * N);
+    };
+    auto load_checkpoint = [&](int blk) {
+        if constexpr (RP) {
+#pragma unroll
+            for (int tau = 0; tau < TB; ++tau) load_prefix(tau, max(me.len - 1 - blk - tau, 0));
+        } else {
+            load_prefix(0, max(me.len - blk - TB, 0));
+        }
     };
     auto load_block = [&](int blk) {
         stage_load<N, R, TB, true>(rm, M, info, blk, 0, T);
@@ -771,15 +786,15 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
         __syncthreads();
         stage_store<N, R, TB>(lds, rm);
         stage_store<N, R, TB>(lds + V::G * V::CH_STRIDE, rr);
-        float cur[R][N];
+        float cur[NCK][R][N];
         if constexpr (GRAD) {
-            if (ck_id)
-                set_identity_rows<N, R>(cur, li * R);
-            else
+#pragma unroll
+            for (int u = 0; u < NCK; ++u)
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int j = 0; j < N; ++j) cur[r][j] = ck[r][j];
+                    for (int j = 0; j < N; ++j)
+                        cur[u][r][j] = ck_id[u] ? (li * R + r == j ? 1.f : 0.f) : ck[u][r][j];
         }
         __syncthreads();
         if (FULL || blk + TB < maxlen) load_block(blk + TB);
@@ -790,14 +805,21 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
         // rp[tau]: the lane's rows of P_{t-1} for the block's token tau, from the
         // block's lowest live token (tau = min(TB-1, hi)) upward
         float rp[GRAD ? TB : 1][R][N];
-        if constexpr (GRAD) {
+        if constexpr (GRAD && RP) {
+#pragma unroll
+            for (int tau = 0; tau < TB; ++tau)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < N; ++j) rp[tau][r][j] = cur[tau][r][j];
+        } else if constexpr (GRAD) {
             const int hi = me.len - 1 - blk;
 #pragma unroll
             for (int tau = TB - 1; tau >= 0; --tau) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int j = 0; j < N; ++j) rp[tau][r][j] = tau == TB - 1 ? cur[r][j] : rp[tau + 1][r][j];
+                    for (int j = 0; j < N; ++j) rp[tau][r][j] = tau == TB - 1 ? cur[0][r][j] : rp[tau + 1][r][j];
                 if (tau < TB - 1) {
                     // P_{t-1} of token tau = P_{t-1} of token tau+1 times M_t of token tau+1
                     const float* slot = xl + (tau + 1) * V::NN;
@@ -812,7 +834,7 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
 #pragma unroll
                         for (int r = 0; r < R; ++r)
 #pragma unroll
-                            for (int j = 0; j < N; ++j) rp[tau][r][j] = cur[r][j];
+                            for (int j = 0; j < N; ++j) rp[tau][r][j] = cur[0][r][j];
                 }
             }
         }
@@ -1136,20 +1158,13 @@ hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, i
 
 }  // namespace
 
-// Row split and staging depth per n: (n, rows per lane R, tokens per staged
-// block TB).  Overridable at build time for tuning sweeps.
-#ifndef MRU_VALU_CFG4
+// Row split and staging depth per n and direction: one row of the state per
+// lane (R = 1: more waves for the same vector work, measured best) and TB
+// tokens per staged block (forward 8 at n = 4, 4 at n = 8; backward 4).
 #define MRU_VALU_CFG4 4, 1, 8
-#endif
-#ifndef MRU_VALU_CFG8
 #define MRU_VALU_CFG8 8, 1, 4
-#endif
-#ifndef MRU_VALU_BWD_CFG4
 #define MRU_VALU_BWD_CFG4 4, 1, 4
-#endif
-#ifndef MRU_VALU_BWD_CFG8
 #define MRU_VALU_BWD_CFG8 8, 1, 4
-#endif
 
 int valu_chains_per_wave(int n, int dir) {
     if (n == 4) return dir == 0 ? Valu<MRU_VALU_CFG4>::G : Valu<MRU_VALU_BWD_CFG4>::G;

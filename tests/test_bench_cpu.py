@@ -19,15 +19,26 @@ def test_more_than_one_gpu_is_refused():
 def test_algorithmic_bytes_per_kernel():
     import bench
     S, T, n = 8192, 256, 8
-    # n <= 8 backward: x (or M), dP, dM per token plus one stored prefix per 4 tokens
-    per_entry = {"fwd_x": 8, "bwd_x": 13, "build": 8, "fwd": 8, "bwd": 13, "build_bwd": 12}
+    # the definition's bytes per entry and token-head: the backward reads x (or M),
+    # P and dP and writes dM (or dx)
+    per_entry = {"fwd_x": 8, "bwd_x": 16, "build": 8, "fwd": 8, "bwd": 16, "build_bwd": 12,
+                 "bwd_dx": 16}
     for kind, b in per_entry.items():
         assert bench.algorithmic_bytes(kind, S, T, n) == b * n * n * S * T
-    # one C2L forward launch moves exactly 1 GiB, the backward 1.625 GiB
+    # one C2L forward launch moves exactly 1 GiB, the backward 2 GiB
     assert bench.algorithmic_bytes("fwd_x", S, T, n) == 2 ** 30
-    assert bench.algorithmic_bytes("bwd_x", S, T, n) == 13 * 2 ** 27
+    assert bench.algorithmic_bytes("bwd_x", S, T, n) == 2 ** 31
+    # by design the n <= 8 backwards from x read one stored prefix per 4 tokens
+    assert bench.design_bytes("bwd_x", S, T, n) == 13 * 2 ** 27
+    assert bench.design_bytes("bwd_dx", S, T, n) == 13 * 2 ** 27
+    assert bench.design_bytes("bwd", S, T, n) == 2 ** 31
     # the matrix-core backward (n = 16, 32) reads every prefix
-    assert bench.algorithmic_bytes("bwd", 64, 1024, 16) == 16 * 256 * 64 * 1024
+    assert bench.design_bytes("bwd_x", 64, 1024, 16) == 16 * 256 * 64 * 1024
+
+
+def test_cpu_model_is_named():
+    import bench
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
 
 
 def test_traffic_record_is_tied_to_the_sources():
@@ -53,6 +64,7 @@ def test_cpu_leg_and_parity_sample():
     w = WORKLOADS["c2"].with_(T=32)
     rec, ref = bench.cpu_leg(w, 0.0, max_workers=2)
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["value"] > 0
+    assert rec["cpu_model"] and rec["parallel"]["cpu_model"] == rec["cpu_model"]
     assert rec["parallel"]["cores"] >= 1 and rec["parallel"]["value"] > 0
     P, dM = ref
     assert 1 <= P.shape[0] <= bench.PARITY_ROWS and P.shape[1:] == (w.H, 32, w.n, w.n)

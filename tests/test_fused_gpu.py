@@ -78,7 +78,7 @@ def test_fused_bwd(mpp, n, B, H, T, chunk):
     say(f"  max {err.max():.3e} median {np.median(err):.3e}")
     assert err.max() <= BWD_TOL
     if plan[3] > 0:
-        assert int(host(ws[4:8].view(torch.int32))[0]) == 0, "a flag wait timed out"
+        assert mpp.ws_status(ws) == 0, "a flag wait timed out"
 
 
 @pytest.mark.parametrize("n", [4, 8])
@@ -135,7 +135,7 @@ def test_layer_bwd_dx(mpp, n, B, H, T, chunk):
     assert err.max() <= BWD_TOL
     assert rel_fro_err(host(dx).reshape(shape), two.reshape(shape)).max() <= 1e-4
     if plan[3] > 0:
-        assert int(host(ws[4:8].view(torch.int32))[0]) == 0, "a flag wait timed out"
+        assert mpp.ws_status(ws) == 0, "a flag wait timed out"
 
 
 @pytest.mark.parametrize("n,chunk", [(4, 0), (8, 0), (8, 7), (4, 16)])
@@ -203,12 +203,31 @@ def test_bwd_reads_one_prefix_in_four(mpp, n, chunk):
     for fn in (lambda PP: mpp.scan_bwd_x(xd, PP, Rd, chunk), lambda PP: mpp.scan_bwd_dx(xd, PP, Rd, chunk=chunk)):
         a, b = fn(P), fn(poisoned)
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
-    M = mpp.build_inputs(xd, n)
-    Pm = mpp.scan_fwd(M)
-    pm = Pm.clone()
-    pm[:, :, ~keep] = float("nan")
-    assert torch.equal(mpp.scan_bwd(M, Pm, Rd, chunk).view(torch.int32),
-                       mpp.scan_bwd(M, pm, Rd, chunk).view(torch.int32))
+
+
+@pytest.mark.parametrize("n,chunk", [(4, 0), (8, 0), (8, 12), (16, 0), (32, 7)])
+def test_bwd_from_M_uses_every_prefix_as_given(mpp, n, chunk):
+    # From M the backward takes P as an input: dM_t = P_{t-1}^T Q_t reads the
+    # stored P_{t-1} of every token and Q does not depend on P.  With every
+    # other prefix replaced by NaN, exactly the tokens after a poisoned prefix
+    # turn NaN and all others keep their bits.
+    B, H, T = 2, 2, 96
+    say(f"[bwd from M, P as given] n={n} chunk={chunk}")
+    x = _x(B, H, T, n, seed=91)
+    R = gen_R(B, H, T, n, seed=92)
+    M = mpp.build_inputs(dev(x), n)
+    Rd = dev(R)
+    P = mpp.scan_fwd(M)
+    poisoned = P.clone()
+    bad = torch.zeros(T, dtype=torch.bool)
+    bad[1::2] = True
+    poisoned[:, :, bad] = float("nan")
+    a = host(mpp.scan_bwd(M, P, Rd, chunk))
+    b = host(mpp.scan_bwd(M, poisoned, Rd, chunk))
+    after_bad = np.zeros(T, dtype=bool)
+    after_bad[1:] = bad.numpy()[:-1]          # token t reads P_{t-1}
+    assert np.isnan(b[:, :, after_bad]).all(axis=(-1, -2)).all()
+    assert np.array_equal(a[:, :, ~after_bad].view(np.uint32), b[:, :, ~after_bad].view(np.uint32))
 
 
 @pytest.mark.parametrize("n", [4, 8])
@@ -227,21 +246,28 @@ def test_fused_layer_autograd(mpp, n):
     assert err.max() <= BWD_TOL
 
 
-def test_fused_rejects_matrix_core_sizes(mpp):
-    # the forward from x covers every n, the backward n = 4, 8
-    import ctypes
-    lib = mpp.load_library()
-    for n in (16, 32):
-        x = torch.zeros(1, 1, 4, n * n, device="cuda")
-        P = torch.zeros(1, 1, 4, n, n, device="cuda")
-        with pytest.raises(ValueError):
-            mpp.scan_bwd_x(x, P, P)
-        with pytest.raises(ValueError):
-            mpp.scan_bwd_dx(x, P, P)
-        st = lib.mru_scan_bwd_x(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(P.data_ptr()),
-                                ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(x.data_ptr() + 4096),
-                                1, 1, 4, n, 0, None, 0, None)
-        assert st == 2
+N16_DX_CASES = [(16, 64, 64, 24, 0), (16, 4, 4, 700, 0), (16, 2, 3, 203, 5), (16, 3, 1, 1, 0),
+                (32, 32, 32, 12, 0), (32, 1, 4, 500, 0), (32, 2, 1, 301, 37), (32, 2, 1, 1, 0)]
+
+
+@pytest.mark.parametrize("n,B,H,T,chunk", N16_DX_CASES)
+def test_layer_bwd_dx_n16(mpp, n, B, H, T, chunk):
+    # the one-pass layer backward at n = 16, 32: bit for bit the build's gradient
+    # applied to the backward from x, and against the oracle's build VJP of its
+    # fp64 backward
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_BWD, chunk)
+    say(f"[layer bwd dx n={n}] B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    x = _x(B, H, T, n, seed=T + 13)
+    R = gen_R(B, H, T, n, seed=T + 14)
+    xd, Rd = dev(x), dev(R)
+    P = mpp.scan_fwd_x(xd, n)
+    dx = mpp.scan_bwd_dx(xd, P, Rd, chunk=chunk, check=True)
+    two = mpp.build_inputs_bwd(xd, mpp.scan_bwd_x(xd, P, Rd, chunk))
+    assert torch.equal(dx.view(torch.int32), two.view(torch.int32)), "differs from the two-kernel path"
+    ref = build_vjp_ref(x, bwd_ref(build_ref(x, n), R), n)
+    err = rel_fro_err(host(dx).reshape(B, H, T, n, n), ref.reshape(B, H, T, n, n))
+    say(f"  max {err.max():.3e} median {np.median(err):.3e}")
+    assert err.max() <= BWD_TOL
 
 
 # n = 16, 32 from raw token vectors: every plan shape of the matrix-core
@@ -270,6 +296,55 @@ def test_fused_fwd_n16(mpp, n, B, H, T, chunk):
     # outputs are the same bits
     P_two = mpp.scan_fwd(mpp.build_inputs(xd, n), chunk)
     assert torch.equal(P.view(torch.int32), P_two.view(torch.int32)), "differs from build + scan"
+
+
+# The backward from raw token vectors at n = 16, 32 over the plan shapes of the
+# matrix-core backward: one chunk per sequence, automatic multi-chunk plans,
+# ragged forced chunks, a single token.
+N16_BWD_CASES = [(16, 64, 64, 24, 0), (16, 4, 4, 1000, 0), (16, 2, 3, 203, 5), (16, 1, 2, 300, 100),
+                 (16, 3, 1, 1, 0), (32, 32, 32, 12, 0), (32, 1, 4, 700, 0), (32, 2, 1, 301, 37),
+                 (32, 2, 1, 1, 0)]
+
+
+@pytest.mark.parametrize("n,B,H,T,chunk", N16_BWD_CASES)
+def test_fused_bwd_n16(mpp, n, B, H, T, chunk):
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_BWD, chunk)
+    say(f"[fused bwd n={n}] B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
+    x = _x(B, H, T, n, seed=T + 9)
+    R = gen_R(B, H, T, n, seed=T + 10)
+    xd, Rd = dev(x), dev(R)
+    P = mpp.scan_fwd_x(xd, n)
+    ws = torch.empty(max(plan[3], 256), dtype=torch.uint8, device="cuda")
+    dM = mpp.scan_bwd_x(xd, P, Rd, chunk, workspace=ws)
+    if plan[3] > 0:
+        assert mpp.ws_status(ws) == 0, "a flag wait timed out"
+    again = mpp.scan_bwd_x(xd, P, Rd, chunk)
+    assert torch.equal(dM.view(torch.int32), again.view(torch.int32)), "not deterministic"
+    ref = bwd_ref(build_ref(x, n), R)
+    err = rel_fro_err(host(dM), ref)
+    say(f"  max {err.max():.3e} median {np.median(err):.3e}")
+    assert err.max() <= BWD_TOL
+    # against build then the backward from M on the same P: each M_{t+1} is
+    # formed with the build's own products, so dM carries the same bits
+    dM_two = mpp.scan_bwd(mpp.build_inputs(xd, n), P, Rd, chunk)
+    assert torch.equal(dM.view(torch.int32), dM_two.view(torch.int32)), "differs from build + backward"
+
+
+@pytest.mark.parametrize("n", [16, 32])
+def test_fused_bwd_n16_zero_input(mpp, n):
+    # x = 0: every M_t = I, so Q_t is the reverse cumulative sum of dL/dP and
+    # dM_t = P_{t-1}^T Q_t = Q_t (P = I), exactly as the backward from M gives it
+    T = 90
+    xd = torch.zeros(1, 2, T, n * n, device="cuda")
+    R = gen_R(1, 2, T, n, seed=5)
+    P = mpp.scan_fwd_x(xd, n)
+    for chunk in (0, 7):
+        dM = host(mpp.scan_bwd_x(xd, P, dev(R), chunk))
+        ref = np.cumsum(R[:, :, ::-1].astype(np.float64), axis=2)[:, :, ::-1]
+        assert rel_fro_err(dM, ref).max() <= BWD_TOL
+        eye = torch.eye(n, device="cuda").expand(1, 2, T, n, n).contiguous()
+        dM_m = host(mpp.scan_bwd(eye, P, dev(R), chunk))
+        assert np.array_equal(dM.view(np.uint32), dM_m.view(np.uint32))
 
 
 @pytest.mark.parametrize("n,chunk", [(16, 0), (16, 9), (16, 100), (32, 0), (32, 21)])

@@ -32,7 +32,7 @@ def test_full_forward(mpp, name):
     say(f"[full fwd] {name}: B={w.B} H={w.H} T={w.T} n={w.n} plan={mpp.scan_plan(w.B, w.H, w.T, w.n)}")
     x, M32, _ = inputs(name)
     Md = dev(M32)
-    P = host(mpp.scan_fwd(Md))
+    P = host(mpp.scan_fwd(Md, check=True))
     P_ref = scan_ref(M32)
     dom = representable(P_ref)
     err = rel_fro_err(P, P_ref)
@@ -52,7 +52,7 @@ def test_full_forward_c4_streamed(mpp):
     for h in range(w.H):
         x = gen_x(w.B, w.H, w.T, w.n, w.sigma_off, w.sigma_diag, w.seed, h_idx=[h])
         M32[:, h:h + 1] = build_ref(x, w.n).astype(np.float32)
-    P = mpp.scan_fwd(dev(M32))
+    P = mpp.scan_fwd(dev(M32), check=True)
     torch.cuda.synchronize()
     worst = 0.0
     graded = outside = 0
@@ -88,8 +88,8 @@ def test_full_backward(mpp, name):
     if R is None:
         R = gen_R(w.B, w.H, w.T, w.n, w.seed)
     Md = dev(M32)
-    P = mpp.scan_fwd(Md)
-    dM = host(mpp.scan_bwd(Md, P, dev(R)))
+    P = mpp.scan_fwd(Md, check=True)
+    dM = host(mpp.scan_bwd(Md, P, dev(R), check=True))
     ref = bwd_ref(M32, R)
     assert np.all(np.isfinite(ref))
     err = rel_fro_err(dM, ref)
@@ -104,12 +104,29 @@ def test_full_backward_c2l_sampled(mpp):
     x, M32, _ = inputs("c2l")
     R = gen_R(w.B, w.H, w.T, w.n, w.seed)
     Md = dev(M32)
-    P = mpp.scan_fwd(Md)
-    dM = mpp.scan_bwd(Md, P, dev(R))
+    P = mpp.scan_fwd(Md, check=True)
+    dM = mpp.scan_bwd(Md, P, dev(R), check=True)
     torch.cuda.synchronize()
     sel = np.arange(0, w.B, 64)
     got = host(dM[sel])
     ref = bwd_ref(M32[sel], R[sel])
     err = rel_fro_err(got, ref)
     say(f"  sampled {len(sel) * w.H} sequences: max {err.max():.3e}")
+    assert err.max() <= BWD_TOL
+
+
+def test_full_backward_from_x_c5(mpp):
+    # the n = 16 training workload from the raw token vectors: forward and
+    # backward both form every input matrix on chip, against the oracle's fp64
+    # build, forward and backward (every dM_t graded)
+    w = WORKLOADS["c5"]
+    say(f"[full bwd from x] c5: plan={mpp.scan_plan(w.B, w.H, w.T, w.n, mpp.DIR_BWD)}")
+    x, _, R = inputs("c5")
+    xd = dev(x)
+    P = mpp.scan_fwd_x(xd, w.n, check=True)
+    dM = host(mpp.scan_bwd_x(xd, P, dev(R), check=True))
+    from oracle import build_ref
+    ref = bwd_ref(build_ref(x, w.n), R)
+    err = rel_fro_err(dM, ref)
+    say(f"  max {err.max():.3e} p99.9 {np.quantile(err, 0.999):.3e} median {np.median(err):.3e}")
     assert err.max() <= BWD_TOL

@@ -60,6 +60,22 @@ def test_build_parity(mpp, n):
     assert np.array_equal(Mz, np.broadcast_to(np.eye(n, dtype=np.float32), Mz.shape))
 
 
+@pytest.mark.parametrize("n", [16, 32])
+def test_build_matrix_core_is_correctly_rounded(mpp, n):
+    # n = 16, 32 accumulate the LDU product in fp64 and round once: every entry is
+    # the fp32 rounding of the oracle's fp64 build, bar entries whose exact value
+    # lies within fp64 error of a rounding boundary (none expected at this size;
+    # at most one ulp apart in any case)
+    so, sd = SIGMA[n]
+    x = gen_x(4, 4, 128, n, so, sd, seed=21)
+    M = host(mpp.build_inputs(dev(x), n))
+    ref32 = build_ref(x, n).astype(np.float32)
+    diff = np.abs(M.view(np.int32).astype(np.int64) - ref32.view(np.int32).astype(np.int64))
+    say(f"[build rounding] n={n}: entries off by one ulp {int((diff == 1).sum())} of {diff.size}")
+    assert diff.max() <= 1
+    assert (diff != 0).sum() <= diff.size * 1e-6
+
+
 @pytest.mark.parametrize("n", [4, 8, 16, 32])
 def test_build_fibonacci_exact(mpp, n):
     X = np.zeros((n, n), np.float32)
@@ -95,7 +111,7 @@ def test_fwd_parity(mpp, n, B, H, T, chunk):
     assert dom.all()
     assert err.max() <= FWD_TOL
     if plan[3] > 0:
-        assert int(host(ws[4:8].view(torch.int32))[0]) == 0, "a flag wait timed out"
+        assert mpp.ws_status(ws) == 0, "a flag wait timed out"
 
 
 @pytest.mark.parametrize("n", [4, 8, 16, 32])
@@ -223,7 +239,7 @@ def test_bwd_parity(mpp, n, B, H, T, chunk):
     say(f"  max {err.max():.3e} median {np.median(err):.3e}")
     assert err.max() <= BWD_TOL
     if plan[3] > 0:
-        assert int(host(ws[4:8].view(torch.int32))[0]) == 0, "a flag wait timed out"
+        assert mpp.ws_status(ws) == 0, "a flag wait timed out"
 
 
 @pytest.mark.parametrize("n", [4, 8, 16, 32])
@@ -345,3 +361,25 @@ def test_layer_autograd_to_token_vectors(mpp, n):
     err = rel_fro_err(g.reshape(1, 2, T, n, n), ref.reshape(1, 2, T, n, n))
     say(f"  max rel err {err.max():.3e}")
     assert err.max() <= BWD_TOL
+
+
+def test_ws_status_reports_the_header_word(mpp):
+    """The status query returns the word a multi-chunk scan leaves in its
+    workspace header (0 when every look-back wait completed), and the binding
+    raises MRU_ERR_TIMEOUT when that word carries the timeout bit (set here from
+    the host, as a timed-out wait would leave it)."""
+    say("[ws_status] n=8 B=1 H=1 T=300 chunk=16")
+    B, H, T, n, chunk = 1, 1, 300, 8, 16
+    need = mpp.workspace_bytes(B, H, T, n, mpp.DIR_FWD, chunk)
+    assert need > 0
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # garbage before the scan
+    M = dev(_M(B, H, T, n, seed=3))
+    mpp.scan_fwd(M, chunk, workspace=ws, check=True)
+    assert mpp.ws_status(ws) == 0
+    ws[4:8].view(torch.int32).fill_(1)
+    assert mpp.ws_status(ws) == 1
+    with pytest.raises(mpp.MRUError) as e:
+        mpp._after_scan(ws, True, "mru_scan_fwd", (B, H, T), n, mpp.DIR_FWD, chunk)
+    assert e.value.status == mpp.MRU_ERR_TIMEOUT
+    # no workspace (one chunk per sequence): nothing to wait on, status 0
+    assert mpp.ws_status(None) == 0
