@@ -361,6 +361,27 @@ mru_status mru_scan_bwd_dx(const float* x, const float* carry, const float* P, c
                            float* dx, float* dcarry, int64_t B, int64_t H, int64_t T, int32_t n,
                            int32_t chunk, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * mru_scan_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels and results as mru_scan_fwd (bitwise), but the
+ * look-back workspace is a static array inside the library, one per device
+ * (MRU_NOALLOC_SCRATCH_BYTES, held from the library's load on that device
+ * until the process ends), so the call takes no ws argument and allocates
+ * nothing.  The caller still passes M and P.
+ * Returns MRU_ERR_WORKSPACE, before launching anything, when the automatic
+ * plan for this shape needs more than MRU_NOALLOC_SCRATCH_BYTES (query with
+ * mru_scan_workspace_bytes(B, H, T, n, MRU_DIR_FWD)); MRU_ERR_HIP if the
+ * array's device address cannot be found; otherwise as mru_scan_fwd.
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (each call clears what must start at zero): two calls that
+ * may run at the same time on one device, on different streams or from
+ * different threads, race and give wrong results; order them on one stream.
+ */
+#define MRU_NOALLOC_SCRATCH_BYTES (64u << 20)
+mru_status mru_scan_fwd_noalloc(const float* M, float* P, int64_t B, int64_t H, int64_t T,
+                                int32_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mru.h"
 #include "mru_device.h"
 #include "mru_kernels.h"
@@ -410,3 +412,60 @@ mru_status mru_scan_bwd_dx(const float* x, const float* carry, const float* P, c
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------
+// Allocation-free forward scan (mru_scan_fwd_noalloc).  Its look-back
+// workspace is this file-scope array: one copy per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device copy, so its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is ever
+// passed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(MRU_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device dev (looked up on first use).
+hipError_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return e;
+        if (g != hipSuccess) return g;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" mru_status mru_scan_fwd_noalloc(const float* M, float* P, int64_t B, int64_t H,
+                                           int64_t T, int32_t n, void* stream) {
+    int64_t S, elems;
+    if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
+    if (elems == 0) return MRU_OK;
+    const size_t need = make_plan(S, T, n, 0, 0).ws;
+    if (need > kScratchBytes) return MRU_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        // validate first, so that a rejected call has no side effects at all
+        if (!M || !P) return MRU_ERR_NULL;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        int dev = 0;
+        hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess || scratch_address(dev, &ws) != hipSuccess) return MRU_ERR_HIP;
+    }
+    return scan_fwd_impl(M, P, B, H, T, n, 0, ws, kScratchBytes, stream, false, ScanCarry{});
+}
