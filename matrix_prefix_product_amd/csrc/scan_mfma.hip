@@ -32,6 +32,8 @@ constexpr int kPfRetain16 = 16;
 namespace mru {
 namespace {
 
+typedef float f4v32 __attribute__((ext_vector_type(4)));
+
 // Scaled state (scaled forward scan): the accumulators hold S^T with
 // P = 2^ex S.  renorm_acc multiplies S by a power of two (exact) so that its
 // largest entry has magnitude in [0.5, 1) and adds the shift to ex (the same in
@@ -473,21 +475,70 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
     if (WRITE) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
 }
 
-// Retained chunk (KR > 0): the aggregate pass loads the chunk's tokens into a
+// Retained chunk (KR > 0).  The aggregate pass loads the chunk's tokens into a
 // register buffer of KR tokens (loads issued PF tokens ahead, clamped into the
-// chunk), converts each to its operand entries in place, and the apply pass
-// reuses them, so each input matrix is read from HBM once even when the chunk
-// needs a carry.
+// chunk) and converts each to its operand entries in place; once a token's
+// product is done, its slot is overwritten with the chunk-local prefix
+// L_t = M_a ... M_t (the chain state, transposed through LDS into A-operand
+// entries of L_t^T, rounded to fp32).  The apply pass then needs no chain: with
+// the carry C of the chunk, P_t^T = L_t^T C^T is one independent product per
+// token, so the matrix core takes consecutive tokens back to back instead of
+// waiting for each product's result.  Each input matrix is read from HBM once.
+// The fp32 rounding of L_t enters P_t amplified by at most the condition number
+// of the chunk-local product (measured with the oracle on the n = 16 workloads:
+// 1.4e-7 relative, against 3.6e-8 for rounding P_t itself).
+// The prefix transpose of token t-1 runs between the products of token t
+// (written in the first hook, read back in the second, after the barrier the
+// step has there anyway); the chunk's last token is transposed after its step.
+// SC: the chain is renormalised every step; the slot holds the normalised
+// L~_t and exl[t] its exponent (P_t = 2^(e_C + exl[t]) C~ L~_t).
+template <int N>
+__device__ inline void prefix_write(const typename Mf<N>::vec_t& X, float* pl) {
+    constexpr int NT = Mf<N>::NT;
+    constexpr int LS = N + 4;
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pl[(16 * I + trow(l, r)) * LS + 16 * J + tcol(l)] = float(X.t[I][J][r]);
+}
+
+// A-operand entries of X for the apply's fp32 products, from its transpose
+// buffer: o[(I * NT + K) * 4 + b] = X[16I + l%16][16K + trow(l, b)].  (The rows
+// are in natural order, not the fp64 chain's tacol order: the fp32 accumulator
+// keeps rows 4(l/16) .. 4(l/16)+3 in lane l, which is then exactly the fp64
+// accumulator's layout of the result.)
+template <int N>
+__device__ inline void prefix_read(float (&o)[4 * Stage<N>::NV], const float* pl) {
+    constexpr int NT = Mf<N>::NT;
+    constexpr int LS = N + 4;
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int K = 0; K < NT; ++K) {
+            const f4v w = *reinterpret_cast<const f4v*>(pl + (16 * I + (l & 15)) * LS + 16 * K + trow(l, 0));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) o[(I * NT + K) * 4 + b] = w[b];
+        }
+}
+
 template <int N, int KR, int PF, bool FX, bool SC>
 __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
                                 int64_t base, int len, float (&buf)[KR][4 * Stage<N>::NV],
-                                float* tlds, float* xlds) {
+                                float* tlds, float* xlds, float* plds, int* exl) {
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NN = F::NN;
     constexpr int NA = 4 * Stage<N>::NV;
+    constexpr int PB = N * (N + 4);  // floats per prefix transpose buffer
     if (len <= 0) return;
     const float* Mb = M + base * NN;
+    const int l = threadIdx.x & 63;
 #pragma unroll
     for (int p = 0; p < PF && p < KR; ++p) load_token<N>(buf[p], Mb + int64_t(min(p, len - 1)) * NN);
     {
@@ -521,65 +572,172 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
             operand_from<N>(a, buf[t]);
             float* tb = tlds + ((t + 1) & 1) * Stage<N>::BUF;
             float* xb = xlds + ((t + 1) & 1) * xslot<N, FX>();
+            float* pl = plds + (t & 1) * PB;  // token t-1's prefix
             const bool next = t + 1 < KR && t + 1 < len;
             vec_t Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
-                if constexpr (t + 1 < KR) {  // buf[t + 1] exists
-                    if constexpr (FX) {
+                if constexpr (FX) {
+                    if constexpr (t + 1 < KR) {  // buf[t + 1] exists
                         if (k == 0 && next) {
                             float o[NA];
                             xop_read<N>(o, xb);
 #pragma unroll
                             for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
                         }
-                        if constexpr (t + 2 < KR) {  // buf[t + 2] exists
-                            float* x2 = xlds + (t & 1) * xslot<N, FX>();
-                            const bool next2 = t + 2 < len;
-                            if (k == 1 && next2) xop_stage<N>(buf[t + 2], x2);
-                            if (k == 2 && next2) {
-                                __syncthreads();
-                                xop_factors<N>(x2);
-                            }
-                            if (k == 3 && next2) __syncthreads();
-                        }
-                    } else {
-                        if (k == 0 && next) operand_write<N>(buf[t + 1], tb);
-                        if (k == 1 && next) {
-                            float o[NA];
+                    }
+                    if constexpr (t > 0)
+                        if (k == 1) prefix_write<N>(X, pl);
+                    if constexpr (t + 2 < KR) {  // buf[t + 2] exists
+                        float* x2 = xlds + (t & 1) * xslot<N, FX>();
+                        const bool next2 = t + 2 < len;
+                        if (k == 1 && next2) xop_stage<N>(buf[t + 2], x2);
+                        if (k == 2 && next2) {
                             __syncthreads();
-                            operand_read<N>(o, tb);
-#pragma unroll
-                            for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+                            xop_factors<N>(x2);
                         }
+                    }
+                    if (k == 3) {
+                        __syncthreads();
+                        if constexpr (t > 0) prefix_read<N>(buf[t - 1], pl);
+                    }
+                } else {
+                    if constexpr (t > 0)
+                        if (k == 0) prefix_write<N>(X, pl);
+                    if constexpr (t + 1 < KR)
+                        if (k == 0 && next) operand_write<N>(buf[t + 1], tb);
+                    if (k == 1) {
+                        __syncthreads();
+                        if constexpr (t + 1 < KR) {
+                            if (next) {
+                                float o[NA];
+                                operand_read<N>(o, tb);
+#pragma unroll
+                                for (int e = 0; e < NA; ++e) buf[t + 1][e] = o[e];
+                            }
+                        }
+                        if constexpr (t > 0) prefix_read<N>(buf[t - 1], pl);
                     }
                 }
             });
             __builtin_amdgcn_sched_barrier(0);
             X = Xn;
-            if constexpr (SC) renorm_acc<N>(X, ex);
+            if constexpr (SC) {
+                renorm_acc<N>(X, ex);
+                if (l == 0) exl[t] = ex;
+            }
+            if (t + 1 == len) {
+                // the chunk's last prefix: transposed right away
+                float* pn = plds + ((t + 1) & 1) * PB;
+                __syncthreads();
+                prefix_write<N>(X, pn);
+                __syncthreads();
+                prefix_read<N>(buf[t], pn);
+            }
         }
     });
 }
 
-template <int N, int KR, bool SC>
-__device__ __attribute__((always_inline)) void fwd_apply_retain(typename Mf<N>::vec_t& X, int& ex, float* __restrict__ P,
-                                 int32_t* __restrict__ pexp, int64_t base, int len,
-                                 const float (&buf)[KR][4 * Stage<N>::NV]) {
-    using F = Mf<N>;
-    using vec_t = typename F::vec_t;
+// P_t^T = L_t^T C^T for every token of a retained chunk, on the fp32 matrix
+// cores: X holds the carry C^T (SC: C~^T with exponent ex), buf the prefixes.
+// The carry is scaled by an exact power of two 2^-s to largest |entry| in
+// [0.5, 1) and rounded to fp32 once, every token is one fp32 product
+// (v_mfma_f32_16x16x4f32, four per 16x16 tile), and the result is scaled back
+// by 2^s (exact; IEEE overflow to inf where P_t leaves the fp32 range).  The
+// running state of the sequence (the aggregate pass's chain, aggregates and
+// carries) stays fp64; only this last product of each token is fp32, and its
+// error does not propagate (measured with the oracle on the n = 16 workloads:
+// 2.7e-7 relative).  Two tokens at a time, their products interleaved.
+template <int N>
+__device__ inline void store_f4_rows(float* __restrict__ p, const f4v32 (&D)[Mf<N>::NT][Mf<N>::NT]) {
+    const int l = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < KR; ++t) {
-        if (t < len) {
-            typename F::aop_t a;
-            operand_from<N>(a, buf[t]);
-            vec_t Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
-                if (k == 0 && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
-            });
-            __builtin_amdgcn_sched_barrier(0);
-            X = Xn;
-            if constexpr (SC) renorm_acc<N>(X, ex);
+    for (int I = 0; I < Mf<N>::NT; ++I)
+#pragma unroll
+        for (int J = 0; J < Mf<N>::NT; ++J) {
+            float* q = p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0);
+            if constexpr (N == 16) __builtin_nontemporal_store(D[I][J], reinterpret_cast<f4v32*>(q));
+            else *reinterpret_cast<f4v32*>(q) = D[I][J];
         }
-    }
-    if (len > 0) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
+}
+
+template <int N, int KR, bool SC>
+__device__ __attribute__((always_inline)) void fwd_apply_retain(const typename Mf<N>::vec_t& X, int ex, float* __restrict__ P,
+                                 int32_t* __restrict__ pexp, int64_t base, int len,
+                                 const float (&buf)[KR][4 * Stage<N>::NV], const int* exl) {
+    constexpr int NT = Mf<N>::NT;
+    constexpr int NN = N * N;
+    static_assert(KR % 2 == 0, "tokens in pairs");
+    if constexpr (SC) __syncthreads();  // the prefixes' exponents in exl
+    // the carry, scaled and rounded once: B entries cb[K][J][b]
+    int s = kNoExp;
+#pragma unroll
+    for (int K = 0; K < NT; ++K)
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) s = max_exp(s, X.t[K][J][b]);
+    s = group_max<64>(s);
+    if (s == kNoExp) s = 0;
+    float cb[NT][NT][4];
+#pragma unroll
+    for (int K = 0; K < NT; ++K)
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) cb[K][J][b] = float(ldexp(X.t[K][J][b], -s));
+    static_for(std::make_integer_sequence<int, KR / 2>{}, [&](auto pc) {
+        constexpr int t = 2 * decltype(pc)::value;
+        if (t < len) {
+            f4v32 D0[NT][NT], D1[NT][NT];
+#pragma unroll
+            for (int I = 0; I < NT; ++I)
+#pragma unroll
+                for (int J = 0; J < NT; ++J) {
+                    f4v32 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int K = 0; K < NT; ++K)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(buf[t][(I * NT + K) * 4 + b], cb[K][J][b], c0, 0, 0, 0);
+                            c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(buf[t + 1][(I * NT + K) * 4 + b], cb[K][J][b], c1, 0, 0, 0);
+                        }
+                    D0[I][J] = c0;
+                    D1[I][J] = c1;
+                }
+            // 2^s back (SC: renormalised, the shift into the exponent)
+            auto finish = [&](f4v32 (&D)[NT][NT], int tok) {
+                int e = s;
+                if constexpr (SC) {
+                    int m = kNoExp;
+#pragma unroll
+                    for (int I = 0; I < NT; ++I)
+#pragma unroll
+                        for (int J = 0; J < NT; ++J)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) m = max_exp(m, D[I][J][r]);
+                    m = group_max<64>(m);
+                    const int shift = m == kNoExp ? 0 : m;
+#pragma unroll
+                    for (int I = 0; I < NT; ++I)
+#pragma unroll
+                        for (int J = 0; J < NT; ++J)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) D[I][J][r] = ldexpf(D[I][J][r], -shift);
+                    e = ex + exl[tok] + s + shift;
+                    if ((threadIdx.x & 63) == 0) pexp[base + tok] = e;
+                } else {
+#pragma unroll
+                    for (int I = 0; I < NT; ++I)
+#pragma unroll
+                        for (int J = 0; J < NT; ++J)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) D[I][J][r] = ldexpf(D[I][J][r], s);
+                }
+                store_f4_rows<N>(P + (base + tok) * NN, D);
+            };
+            finish(D0, t);
+            if (t + 1 < len) finish(D1, t + 1);
+        }
+    });
 }
 
 // One wave per SIMD: the forward keeps a chunk's operands (n = 16) or a deep
@@ -599,6 +757,9 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     __shared__ double xl[NN];
     __shared__ __align__(16) float tlds[2 * Stage<N>::BUF];
     __shared__ __align__(16) float xlds[FX ? 2 * xslot<N, FX>() : 4];  // FX: the token factors
+    // retained chunks: the prefix transpose buffers, and (SC) the prefixes' exponents
+    __shared__ __align__(16) float plds[KR > 0 ? 2 * N * (N + 4) : 4];
+    __shared__ int exl[KR > 0 && SC ? KR : 1];
     const int l = threadIdx.x & 63;
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
@@ -629,7 +790,8 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0)
-        fwd_pass_retain<N, KR, (N == 16 ? kPfRetain16 : PF), FX, SC>(X, ex, M, ch.base, ch.len, buf, tlds, xlds);
+        fwd_pass_retain<N, KR, (N == 16 ? kPfRetain16 : PF), FX, SC>(X, ex, M, ch.base, ch.len, buf, tlds,
+                                                                      xlds, plds, exl);
     else
         fwd_sweep<N, PF, false, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
     const int a_ex = ex;
@@ -698,7 +860,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
 
     // 4. re-run from the carry
     if constexpr (KR > 0)
-        fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf);
+        fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf, exl);
     else
         fwd_sweep<N, PF, true, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
 }
@@ -940,8 +1102,18 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
         if (i0 + p < len) step(p, i0 + p, false);
 }
 
+// The n = 16 instances from raw token vectors run two waves per SIMD (a
+// shallower prefetch ring fits them in half the register file): forming each
+// input matrix on chip lengthens a step, and the second wave's products fill
+// the first one's waits (C5 backward from x 653 -> 457 us, the layer backward
+// to dx 907 -> 579 us); the backward from M gained nothing and keeps one wave
+// with the deeper ring.
+template <int N, bool FX>
+constexpr int bwd_waves() { return (N == 16 && FX) ? 2 : 1; }
+
 template <int N, int PF, bool FX, bool DX>
-__global__ __launch_bounds__(64) void bwd_mfma_kernel(const float* __restrict__ M,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_waves<N, FX>(), bwd_waves<N, FX>())))
+void bwd_mfma_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ P,
                                                       const float* __restrict__ dP,
                                                       float* __restrict__ dM, int64_t S, int64_t T,
@@ -1088,10 +1260,11 @@ hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, floa
                            int64_t T, int n, int64_t K, int64_t nch, int64_t Z, void* ws,
                            hipStream_t stream, bool from_x, bool to_dx, const ScanCarry& cy) {
     if (to_dx && !from_x) return hipErrorInvalidValue;
-    // the n = 32 instances from raw token vectors prefetch one token (two spill)
+    // prefetch depth: the n = 16 instances from raw token vectors 4 tokens (two
+    // waves per SIMD), the n = 32 ones 1 (two spill)
     if (n == 16) {
-        if (to_dx) return run_bwd<16, 8, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
-        if (from_x) return run_bwd<16, 8, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        if (to_dx) return run_bwd<16, 2, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        if (from_x) return run_bwd<16, 4, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
         return run_bwd<16, 8, false, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 32) {
