@@ -42,6 +42,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -55,26 +56,21 @@ METRIC = "MRU prefix-scan tokens/s + achieved HBM GB/s (frac of peak), n=8 and n
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-# The sources the counted kernels (the n <= 8 build and vector-unit scans) are
-# compiled and launched from; the matrix-core scans and the orthogonal builds
-# live in other files and do not invalidate the counters.
-COUNTED_SOURCES = ("mru_api.hip", "mru_build.h", "mru_device.h", "mru_kernels.h",
-                   "build_inputs.hip", "scan_valu.hip")
-
-
-# The sources of the matrix-core kernels (n = 16, 32) whose counted utilisation
-# profiles/mfma_util.json records.
-MFMA_SOURCES = ("mru_api.hip", "mru_build.h", "mru_device.h", "mru_kernels.h", "mru_mfma.h",
-                "build_inputs.hip", "scan_mfma.hip")
+# Counter records under profiles/, each workload's entry stamped with the hash of
+# the library sources it was taken on (every .hip and .h of the package's csrc):
+# a figure taken on other sources is not reported.
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
+CSRC = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+XCDS = 8
+NOMINAL_CLOCK_HZ = 2.4e9
 
 
-def source_hash(files=COUNTED_SOURCES) -> str:
+def source_hash() -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
-    for p in sorted(os.path.join(csrc, f) for f in files):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for p in sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h"))):
+        with open(os.path.join(CSRC, p), "rb") as f:
+            h.update(p.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -105,31 +101,188 @@ def algorithmic_flops(kind: str, S: int, T: int, n: int) -> int:
             "fwd_x": 2 * n ** 3, "bwd_x": 4 * n ** 3}[kind] * S * T
 
 
-def load_traffic(workload: str, kernel: str):
+def _record(path: str, workload: str, kind: str):
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != source_hash():
+    w = rec.get("workloads", {}).get(workload)
+    if not w or w.get("source_hash") != source_hash():
         return None
-    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
-    if not k:
-        return None
-    return int(k["fetch_bytes"] + k["write_bytes"])
+    return w.get("kernels", {}).get(kind)
 
 
-def load_mfma_util(workload: str, kernel: str):
-    """Matrix-core utilisation counted by rocprofv3 (SQ_VALU_MFMA_BUSY_CYCLES
-    over GRBM_GUI_ACTIVE x 1024 SIMDs) for this workload's kernel, when the
-    record was taken on the current matrix-core sources; else None."""
+def load_traffic(workload: str, kind: str):
+    """Counted HBM bytes (read + written) per launch of this workload's kernel,
+    when the record was taken on the current sources; else None."""
+    k = _record(TRAFFIC_FILE, workload, kind)
+    return None if not k else int(k["read_bytes"] + k["write_bytes"])
+
+
+def load_mfma_util(workload: str, kind: str):
+    """Matrix-core and vector-ALU busy fractions counted by rocprofv3 for this
+    workload's kernel, when the record was taken on the current sources; else None."""
+    return _record(MFMA_FILE, workload, kind)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries: `bench.py --summarize {trace,traffic,mfma} --profile-workload W
+# DIR...` reads the CSV files rocprofv3 wrote under DIR (kernel_stats.csv of a
+# --kernel-trace --stats run, counter_collection.csv of --pmc runs), prints the
+# text summary kept under profiles/, and (traffic, mfma) updates the JSON record
+# bench.py reports from.
+
+def short_kernel(name: str) -> str:
+    s = name.replace("void ", "").replace("mru::(anonymous namespace)::", "").replace("mru::", "")
+    return re.sub(r"\(.*$", "", s).strip()
+
+
+def kernel_kind(short: str):
+    """The step a library kernel runs: build, fwd, fwd_x, bwd, bwd_x, bwd_dx,
+    build_bwd (fwd*_scaled for the scaled forward), copy for the runtime's
+    buffer copy; None for anything else."""
+    if short.startswith("__amd_rocclr_copyBuffer"):
+        return "copy"
+    m = re.match(r"(\w+)<([^>]*)>", short)
+    if not m:
+        return None
+    fam, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    if fam in ("fwd_valu_kernel", "fwd_mfma_kernel"):
+        return ("fwd_x" if args[-2] == "true" else "fwd") + ("_scaled" if args[-1] == "true" else "")
+    if fam in ("bwd_valu_kernel", "bwd_mfma_kernel"):
+        return "bwd_dx" if args[-1] == "true" else ("bwd_x" if args[-2] == "true" else "bwd")
+    if fam in ("build_kernel", "build_mfma_kernel"):
+        return "build"
+    if fam in ("build_bwd_kernel", "build_bwd_mfma_kernel"):
+        return "build_bwd"
+    return None
+
+
+def _csvs(dirs, suffix):
+    out = []
+    for d in dirs:
+        for root, _, files in os.walk(d):
+            out += [os.path.join(root, f) for f in files if f.endswith(suffix)]
+    if not out:
+        sys.exit(f"no *{suffix} under {dirs}")
+    return sorted(out)
+
+
+def read_counters(dirs):
+    """{(kernel, grid): {"dur_ns": [...], counter: [per-dispatch values]}}"""
+    import csv
+    from collections import defaultdict
+    per = defaultdict(lambda: defaultdict(dict))  # (kernel, grid) -> dispatch -> counter -> value
+    dur = defaultdict(dict)
+    for path in _csvs(dirs, "counter_collection.csv"):
+        for r in csv.DictReader(open(path)):
+            key = (short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]))
+            d = (path, r["Dispatch_Id"])
+            c = per[key][d]
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            dur[key][d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = {}
+    for key, disp in per.items():
+        rec = {"dur_ns": [dur[key][d] for d in disp]}
+        for d, cs in disp.items():
+            for c, v in cs.items():
+                rec.setdefault(c, []).append(v)
+        out[key] = rec
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def summarize(what: str, dirs, workload: str, commands) -> None:
+    head = [f"# {what} summary of the {workload} kernels, rocprofv3 on one MI355X",
+            f"# library source hash {source_hash()}",
+            "# commands (run from /tmp with TMPDIR=/tmp; REPO = repository root):"]
+    head += [f"#   {c}" for c in commands]
+    if what == "trace":
+        import csv
+        print("\n".join(head))
+        print(f"{'kernel':56s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        for path in _csvs(dirs, "kernel_stats.csv"):
+            for r in csv.DictReader(open(path)):
+                print(f"{short_kernel(r['Name'])[:56]:56s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                      f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
+        return
+    data = read_counters(dirs)
+    path = TRAFFIC_FILE if what == "traffic" else MFMA_FILE
     try:
-        rec = json.load(open(MFMA_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
-        return None
-    if rec.get("source_hash") != source_hash(MFMA_SOURCES):
-        return None
-    k = rec.get("workloads", {}).get(workload, {}).get(kernel)
-    return None if not k else k
+        rec = {}
+    kernels = {}
+    if what == "traffic":
+        # scale: the runtime's copy of a known size (1 GiB read + 1 GiB written) in
+        # the same runs; without one, the factors of the record's last copy
+        cal = rec.get("copy_kernel")
+        for (k, grid), v in data.items():
+            if kernel_kind(k) == "copy" and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+                f, w = _median(v["FETCH_SIZE"]), _median(v["WRITE_SIZE"])
+                cal = {"name": f"{k} (torch copy_ of 1 GiB)", "bytes_read": 2 ** 30, "bytes_written": 2 ** 30,
+                       "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
+                       "fetch_scale": round(2 ** 30 / (f * 1024), 3), "write_scale": round(2 ** 30 / (w * 1024), 3)}
+        if cal is None:
+            sys.exit("no copy kernel in these runs and no earlier scale on record")
+        rec["copy_kernel"] = cal
+        rec["counters"] = "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch, median)"
+        head += [f"# scale: {cal['name']} reads FETCH_SIZE {cal['FETCH_SIZE_KiB']:.1f} KiB and WRITE_SIZE "
+                 f"{cal['WRITE_SIZE_KiB']:.1f} KiB per 1 GiB,",
+                 f"#   so read bytes = {cal['fetch_scale']} x FETCH_SIZE x 1024 and write bytes = "
+                 f"{cal['write_scale']} x WRITE_SIZE x 1024"]
+        cols = f"{'kernel':48s} {'grid':>9s} {'us':>9s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'read_bytes':>13s} {'write_bytes':>13s}"
+        lines = []
+        for (k, grid), v in sorted(data.items(), key=lambda kv: -_median(kv[1]["dur_ns"])):
+            if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
+                continue
+            f, w = _median(v["FETCH_SIZE"]), _median(v["WRITE_SIZE"])
+            rb, wb = int(cal["fetch_scale"] * f * 1024), int(cal["write_scale"] * w * 1024)
+            lines.append(f"{k[:48]:48s} {grid:9d} {_median(v['dur_ns']) / 1e3:9.1f} {f:12.1f} {w:12.1f} {rb:13d} {wb:13d}")
+            kind = kernel_kind(k)
+            if kind and kind != "copy":
+                kernels[kind] = {"kernel": k, "grid": grid, "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
+                                 "read_bytes": rb, "write_bytes": wb}
+    else:
+        # matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of the
+        # kernel, with GRBM_GUI_ACTIVE (summed over the XCDs) as the kernel's
+        # cycles; vector ALU: SQ_ACTIVE_INST_VALU (cycles a wave issues VALU
+        # work, 4 per instruction) over the same SIMD-cycles
+        head += ["# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);",
+                 "# valu_busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / 8 x 1024); the *_clk figures use the",
+                 "# kernel's duration x 2.4 GHz as its cycles instead; medians over the dispatches"]
+        cols = (f"{'kernel':48s} {'grid':>9s} {'us':>9s} {'mfma_busy':>10s} {'mfma_clk':>9s} {'valu_busy':>10s} "
+                f"{'valu_clk':>9s} {'MFMA_BUSY':>14s} {'GRBM_ACTIVE':>12s}")
+        lines = []
+        for (k, grid), v in sorted(data.items(), key=lambda kv: -_median(kv[1]["dur_ns"])):
+            if "SQ_VALU_MFMA_BUSY_CYCLES" not in v or "GRBM_GUI_ACTIVE" not in v:
+                continue
+            mb, gr, us = _median(v["SQ_VALU_MFMA_BUSY_CYCLES"]), _median(v["GRBM_GUI_ACTIVE"]), _median(v["dur_ns"]) / 1e3
+            va = _median(v.get("SQ_ACTIVE_INST_VALU", [0.0]))
+            simd_cyc = gr / XCDS * SIMDS
+            clk_cyc = us * 1e-6 * NOMINAL_CLOCK_HZ * SIMDS
+            r = {"kernel": k, "grid": grid, "us": round(us, 1),
+                 "mfma_busy": round(mb / simd_cyc, 4), "mfma_busy_clk": round(mb / clk_cyc, 4),
+                 "valu_busy": round(va / simd_cyc, 4), "valu_busy_clk": round(va / clk_cyc, 4),
+                 "SQ_VALU_MFMA_BUSY_CYCLES": mb, "SQ_ACTIVE_INST_VALU": va, "GRBM_GUI_ACTIVE": gr}
+            for c in ("SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F64", "SQ_INSTS_MFMA",
+                      "SQ_INSTS_VALU", "SQ_ACTIVE_INST_LDS"):
+                if c in v:
+                    r[c] = _median(v[c])
+            lines.append(f"{k[:48]:48s} {grid:9d} {us:9.1f} {r['mfma_busy']:10.4f} {r['mfma_busy_clk']:9.4f} "
+                         f"{r['valu_busy']:10.4f} {r['valu_busy_clk']:9.4f} {mb:14.0f} {gr:12.0f}")
+            kind = kernel_kind(k)
+            if kind and kind != "copy":
+                kernels[kind] = r
+    rec.setdefault("workloads", {})[workload] = {"source_hash": source_hash(), "kernels": kernels,
+                                                 "commands": list(commands)}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print("\n".join(head + [f"# machine-readable copy: profiles/{os.path.basename(path)}", cols] + lines))
 
 
 def cpu_model() -> str:
@@ -579,7 +732,20 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the n=16 / n=32 forward figures")
     ap.add_argument("--extra-only", action="store_true",
                     help="only the n=16 / n=32 and next-row figures (for profiling those kernels)")
+    ap.add_argument("--only", choices=("c3", "c4", "c5"),
+                    help="with --extra-only: just this workload's figures (one workload per profile)")
+    ap.add_argument("--summarize", choices=("trace", "traffic", "mfma"),
+                    help="print the summary of the rocprofv3 CSVs under DIR... (no GPU work)")
+    ap.add_argument("--profile-workload", help="with --summarize: the workload the runs covered")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize: a command that produced DIR (repeatable)")
+    ap.add_argument("dirs", nargs="*", help="with --summarize: rocprofv3 output folders")
     args = ap.parse_args()
+    if args.summarize:
+        if not args.profile_workload or not args.dirs:
+            sys.exit("--summarize needs --profile-workload and at least one folder")
+        summarize(args.summarize, args.dirs, args.profile_workload, args.command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -606,13 +772,20 @@ def main():
     torch.cuda.set_device(dev)
     if args.extra_only:
         c3, c4, c5 = WORKLOADS["c3"], WORKLOADS["c4"], WORKLOADS["c5"]
-        extra = {
-            "n16": fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3),
-            "n32": fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4),
-            "n16_fwd_bwd": fwd_bwd(mpp, torch, "c5", c5.B, c5.H, c5.T, c5.n, c5.sigma_off, c5.sigma_diag, 10, 5),
-            "small": small_configs(mpp, torch, WORKLOADS, gen_R, gen_x),
-            "next": next_rows(mpp, torch),
+        runs = {
+            "n16": lambda: fwd_only(mpp, torch, "c3", c3.B, c3.H, c3.T, c3.n, c3.sigma_off, c3.sigma_diag, 10, 3),
+            "n32": lambda: fwd_only(mpp, torch, "c4", c4.B, c4.H, c4.T, c4.n, c4.sigma_off, c4.sigma_diag, 5, 4),
+            "n16_fwd_bwd": lambda: fwd_bwd(mpp, torch, "c5", c5.B, c5.H, c5.T, c5.n, c5.sigma_off,
+                                           c5.sigma_diag, 10, 5),
+            "small": lambda: small_configs(mpp, torch, WORKLOADS, gen_R, gen_x),
+            "next": lambda: next_rows(mpp, torch),
         }
+        if args.only:
+            runs = {k: v for k, v in runs.items() if k == {"c3": "n16", "c4": "n32", "c5": "n16_fwd_bwd"}[args.only]}
+        extra = {}
+        for k, fn in runs.items():
+            extra[k] = fn()
+            print(f"# {k} done", file=sys.stderr, flush=True)
         print(json.dumps(extra), flush=True)
         return
 

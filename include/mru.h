@@ -75,6 +75,9 @@ typedef enum mru_status {
 /* Scan direction for the workspace / chunk queries. */
 #define MRU_DIR_FWD 0
 #define MRU_DIR_BWD 1
+/* The forward from raw token vectors, for mru_scan_chunk and mru_scan_plan (its
+ * automatic plan may differ from the scan from M's). */
+#define MRU_DIR_FWD_X 2
 
 /* Orthogonal input constructions (mru_build_orthogonal). */
 #define MRU_ORTHO_CAYLEY 0
@@ -136,13 +139,16 @@ mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int6
 
 /*
  * Chunk length (tokens per scan chunk) of the automatic plan for this shape
- * and direction; a pure function of its arguments.  Returns 0 for an invalid
- * shape.
+ * and direction (MRU_DIR_FWD, MRU_DIR_BWD, or MRU_DIR_FWD_X for the forward
+ * from raw token vectors, which at n = 16 plans 32-token chunks where the scan
+ * from M takes up to 64: it runs two waves per SIMD); a pure function of its
+ * arguments.  Returns 0 for an invalid shape.
  */
 int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction);
 
 /*
- * The scan plan for this shape, direction and chunk (0 = automatic), as
+ * The scan plan for this shape, direction (as for mru_scan_chunk) and chunk
+ * (0 = automatic), as
  * out4[0] = chunk length K, out4[1] = chunks per sequence (the token chunks,
  * rounded up with empty chunks to a multiple of the chains a wave runs),
  * out4[2] = chunks per super (the unit of the carry chain), out4[3] = workspace
@@ -156,7 +162,7 @@ int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direct
  * Workspace bytes that mru_scan_fwd (direction MRU_DIR_FWD) or mru_scan_bwd
  * (MRU_DIR_BWD) needs for this shape with the automatic plan; the same size
  * serves every entry point of that direction (from M or from raw token
- * vectors, with or without a carried state).  May be 0, in which case ws may
+ * vectors, with or without a carried state: the largest of their plans).  May be 0, in which case ws may
  * be NULL.  Returns 0 for an invalid shape as well; callers validate through
  * the scan call itself.
  */
@@ -370,7 +376,7 @@ mru_status mru_scan_bwd_dx(const float* x, const float* carry, const float* P, c
  * until the process ends), so the call takes no ws argument and allocates
  * nothing.  The caller still passes M and P.
  * Returns MRU_ERR_WORKSPACE, before launching anything, when the automatic
- * plan for this shape needs more than MRU_NOALLOC_SCRATCH_BYTES (query with
+ * plan for this shape needs more than MRU_NOALLOC_SCRATCH_BYTES (at most
  * mru_scan_workspace_bytes(B, H, T, n, MRU_DIR_FWD)); MRU_ERR_HIP if the
  * array's device address cannot be found; otherwise as mru_scan_fwd.
  * Every call on a device shares that device's array, which keeps the last

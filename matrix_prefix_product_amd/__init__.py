@@ -27,12 +27,13 @@ __all__ = [
     "build_inputs", "build_inputs_bwd", "scan_fwd", "mru_layer", "MRUBuild", "scan_bwd", "flatten", "mru_scan", "MRUScan",
     "scan_fwd_x", "scan_bwd_x", "scan_fwd_ex", "scan_bwd_ex", "scan_bwd_dx", "build_orthogonal",
     "scan_plan", "scan_chunk", "workspace_bytes", "library_path", "load_library",
-    "MRUError", "DIR_FWD", "DIR_BWD", "SUPPORTED_N", "FUSED_N", "FUSED_FWD_N", "FUSED_BWD_N",
+    "MRUError", "DIR_FWD", "DIR_BWD", "DIR_FWD_X", "SUPPORTED_N", "FUSED_N", "FUSED_FWD_N", "FUSED_BWD_N",
     "set_checking", "ws_status", "MRU_ERR_TIMEOUT",
 ]
 
 DIR_FWD = 0
 DIR_BWD = 1
+DIR_FWD_X = 2  # plan queries: the forward from raw token vectors
 SUPPORTED_N = (4, 8, 16, 32)
 # Sizes whose forward scan can start from raw token vectors (input matrices
 # built on chip), whose backward scan to dL/dM can too (FUSED_BWD_N), and whose
@@ -374,7 +375,7 @@ def scan_fwd_x(x: torch.Tensor, n: int, chunk: int = 0, out: torch.Tensor | None
         st = lib.mru_scan_fwd_x(_ptr(x), _ptr(out), B, H, T, n, chunk, _ptr(ws), ws_bytes,
                                 _stream_handle(x.device))
     _check(st, "mru_scan_fwd_x")
-    _after_scan(ws, check, "mru_scan_fwd_x", (B, H, T), n, DIR_FWD, chunk)
+    _after_scan(ws, check, "mru_scan_fwd_x", (B, H, T), n, DIR_FWD_X, chunk)
     return out
 
 

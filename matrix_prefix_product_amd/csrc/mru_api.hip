@@ -59,7 +59,7 @@ struct Plan {
 // Chunk length used when the caller passes chunk = 0.  Single-chunk scans need
 // no carries at all (one product per token); they are chosen when the
 // sequences alone give the GPU enough independent chains.
-int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir) {
+int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir, bool from_x = false) {
     if (T <= 0) return 0;
     int64_t target;
     if (n <= 8) {
@@ -83,15 +83,15 @@ int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir) {
     const int64_t kmin = (n <= 8 && dir == 1) ? 8 : 16;
     if (K < kmin) K = kmin;
     // a forward chunk that fits the register buffer reads its inputs once
-    const int64_t keep = dir == 0 ? mfma_retain_tokens(n) : 0;
+    const int64_t keep = dir == 0 ? mfma_retain_tokens(n, from_x) : 0;
     if (keep > 0 && K > keep) K = keep;
     return K < T ? K : T;
 }
 
-Plan make_plan(int64_t S, int64_t T, int n, int dir, int64_t chunk) {
+Plan make_plan(int64_t S, int64_t T, int n, int dir, int64_t chunk, bool from_x = false) {
     Plan p;
     if (S <= 0 || T <= 0) return p;
-    p.K = chunk > 0 ? (chunk < T ? chunk : T) : auto_chunk_len(S, T, n, dir);
+    p.K = chunk > 0 ? (chunk < T ? chunk : T) : auto_chunk_len(S, T, n, dir, from_x);
     p.nch = (T + p.K - 1) / p.K;
     if (p.nch <= 1) {
         p.nch = 1;
@@ -210,14 +210,19 @@ mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int6
 int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems) || elems == 0) return 0;
-    return int32_t(auto_chunk_len(S, T, n, direction == MRU_DIR_BWD ? 1 : 0));
+    return int32_t(auto_chunk_len(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, direction == MRU_DIR_FWD_X));
 }
 
 size_t mru_scan_workspace_bytes_chunked(int64_t B, int64_t H, int64_t T, int32_t n,
                                         int32_t direction, int32_t chunk) {
     int64_t S, elems;
     if (!shape_ok(B, H, T, n, &S, &elems) || elems == 0 || chunk < 0) return 0;
-    return make_plan(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, chunk).ws;
+    const int dir = direction == MRU_DIR_BWD ? 1 : 0;
+    if (direction == MRU_DIR_FWD_X) return make_plan(S, T, n, 0, chunk, true).ws;
+    // one workspace serves the scan from M and from raw token vectors, whose
+    // automatic plans may differ
+    const size_t a = make_plan(S, T, n, dir, chunk).ws, b = make_plan(S, T, n, dir, chunk, true).ws;
+    return a > b ? a : b;
 }
 
 size_t mru_scan_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction) {
@@ -242,7 +247,7 @@ int32_t mru_scan_plan(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direct
     if (!out4) return MRU_ERR_NULL;
     if (!shape_ok(B, H, T, n, &S, &elems)) return MRU_ERR_SHAPE;
     if (chunk < 0) return MRU_ERR_CHUNK;
-    const Plan p = make_plan(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, chunk);
+    const Plan p = make_plan(S, T, n, direction == MRU_DIR_BWD ? 1 : 0, chunk, direction == MRU_DIR_FWD_X);
     out4[0] = p.K;
     out4[1] = p.nch;
     out4[2] = p.Z;
@@ -268,7 +273,7 @@ mru_status scan_fwd_impl(const float* M, float* P, int64_t B, int64_t H, int64_t
     if ((cy.carry && !aligned16(cy.carry)) || (cy.carry_exp && !aligned4(cy.carry_exp)) ||
         (cy.out_exp && !aligned4(cy.out_exp)))
         return MRU_ERR_ALIGN;
-    const Plan p = make_plan(S, T, n, 0, chunk);
+    const Plan p = make_plan(S, T, n, 0, chunk, from_x);
     if (!grid_ok(p, n, 0)) return MRU_ERR_SHAPE;
     const size_t bytes = size_t(elems) * sizeof(float);
     const size_t cbytes = size_t(S) * n * n * sizeof(float);

@@ -53,7 +53,7 @@ hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, floa
 
 // Tokens per chunk the matrix-core forward kernel keeps in registers between
 // its two passes (0 = none): chunks of at most this length read M once.
-int mfma_retain_tokens(int n);
+int mfma_retain_tokens(int n, bool from_x);
 
 // Chains per wave of the vector-ALU kernels (n = 4, 8) for direction dir.
 int valu_chains_per_wave(int n, int dir);

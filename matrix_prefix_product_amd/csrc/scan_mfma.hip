@@ -527,10 +527,12 @@ __device__ inline void prefix_read(float (&o)[4 * Stage<N>::NV], const float* pl
         }
 }
 
-template <int N, int KR, int PF, bool FX, bool SC>
+template <int N, int KR, int PF, bool FX, bool SC, bool FULL>
 __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
-                                int64_t base, int len, float (&buf)[KR][4 * Stage<N>::NV],
+                                int64_t base, int len_in, float (&buf)[KR][4 * Stage<N>::NV],
                                 float* tlds, float* xlds, float* plds, int* exl) {
+    // FULL: a whole chunk, every per-token test resolved at compile time
+    const int len = FULL ? KR : len_in;
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NN = F::NN;
@@ -684,6 +686,44 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
         for (int J = 0; J < NT; ++J)
 #pragma unroll
             for (int b = 0; b < 4; ++b) cb[K][J][b] = float(ldexp(X.t[K][J][b], -s));
+    // token t's product, P_t^T up to the power of two
+    auto product = [&](f4v32 (&D)[NT][NT], const float (&a)[4 * Stage<N>::NV]) {
+#pragma unroll
+        for (int I = 0; I < NT; ++I)
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+                f4v32 c0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int K = 0; K < NT; ++K)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(I * NT + K) * 4 + b], cb[K][J][b], c0, 0, 0, 0);
+                D[I][J] = c0;
+            }
+    };
+    if constexpr (!SC) {
+        if (len == KR && s >= -64 && s <= 64) {
+            // a whole chunk whose carry is well inside the fp32 range: the carry
+            // rounded to fp32 as it is (scaling by 2^-s and back by 2^s changes no
+            // bit of a result unless an intermediate leaves the normal range), and
+            // each product stored straight from the matrix-core accumulators,
+            // branch-free, token t+1's products issued before token t is stored
+#pragma unroll
+            for (int K = 0; K < NT; ++K)
+#pragma unroll
+                for (int J = 0; J < NT; ++J)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) cb[K][J][b] = float(X.t[K][J][b]);
+            f4v32 D[2][NT][NT];
+            product(D[0], buf[0]);
+            static_for(std::make_integer_sequence<int, KR>{}, [&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                if constexpr (t + 1 < KR) product(D[(t + 1) & 1], buf[t + 1]);
+                store_f4_rows<N>(P + (base + t) * NN, D[t & 1]);
+            });
+            return;
+        }
+    }
     static_for(std::make_integer_sequence<int, KR / 2>{}, [&](auto pc) {
         constexpr int t = 2 * decltype(pc)::value;
         if (t < len) {
@@ -741,11 +781,15 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
 }
 
 // One wave per SIMD: the forward keeps a chunk's operands (n = 16) or a deep
-// operand ring (n = 32) in the whole register file.  Register-capped variants
-// at two waves per SIMD were measured no faster.
+// operand ring (n = 32) in the whole register file.  The 32-token retained
+// chunks run two waves per SIMD: a wave's own vector-ALU instructions do not
+// overlap its matrix-core products (measured: each adds its issue time to the
+// product chain), another wave's do.
+template <int KR>
+constexpr int fwd_waves() { return KR == 32 ? 2 : 1; }
 
 template <int N, int PF, int KR, bool FX, bool SC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fwd_waves<KR>(), fwd_waves<KR>())))
 void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
@@ -789,10 +833,13 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised matrix)
     vec_t X = videntity<N>(l);
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
-    if constexpr (KR > 0)
-        fwd_pass_retain<N, KR, (N == 16 ? kPfRetain16 : PF), FX, SC>(X, ex, M, ch.base, ch.len, buf, tlds,
-                                                                      xlds, plds, exl);
-    else
+    if constexpr (KR > 0) {
+        constexpr int PFR = N == 16 ? kPfRetain16 : PF;
+        if (ch.len == KR)
+            fwd_pass_retain<N, KR, PFR, FX, SC, true>(X, ex, M, ch.base, ch.len, buf, tlds, xlds, plds, exl);
+        else
+            fwd_pass_retain<N, KR, PFR, FX, SC, false>(X, ex, M, ch.base, ch.len, buf, tlds, xlds, plds, exl);
+    } else
         fwd_sweep<N, PF, false, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
     const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
@@ -1233,9 +1280,13 @@ hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, i
 // Tokens of one chunk kept in registers by the n = 16 forward kernel, and the
 // operand prefetch depth of its streamed sweeps (tokens in flight).
 constexpr int kRetain16 = 64;
+// from raw token vectors: 32-token chunks at two waves per SIMD (the token
+// build's vector-ALU work of one wave runs while the other's products run on
+// the matrix cores; measured faster than 64-token chunks at one wave)
+constexpr int kRetain16x = 32;
 constexpr int kPf16 = 16;
 
-int mfma_retain_tokens(int n) { return n == 16 ? kRetain16 : 0; }
+int mfma_retain_tokens(int n, bool from_x) { return n == 16 ? (from_x ? kRetain16x : kRetain16) : 0; }
 
 hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n, int64_t K,
                            int64_t nch, int64_t Z, void* ws, hipStream_t stream, bool from_x,
@@ -1243,6 +1294,10 @@ hipError_t launch_fwd_mfma(const float* M, float* P, int64_t S, int64_t T, int n
     if (n == 16) {
         const bool retain = kRetain16 > 0 && nch > 1 && K <= kRetain16;
         if (from_x) {
+            // chunks of up to 64 tokens keep their prefixes (the same arithmetic
+            // at either buffer size, so the same bits as the scan from M)
+            if (nch > 1 && K <= kRetain16x)
+                return run_fwd<16, kPf16, kRetain16x, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
             if (retain) return run_fwd<16, kPf16, kRetain16, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
             return run_fwd<16, kPf16, 0, true>(M, P, S, T, K, nch, Z, ws, stream, cy);
         }

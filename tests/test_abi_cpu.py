@@ -73,6 +73,16 @@ def test_plans_single_and_multi(mpp):
             assert (ws == 0) == (nch == 1)
             assert mpp.workspace_bytes(2, 3, 203, n, mpp.DIR_BWD, chunk) == ws
     assert mpp.scan_chunk(1024, 8, 256, 8) == 256
+    # n = 16 from raw token vectors: 32-token chunks (two waves per SIMD) where the
+    # scan from M takes 64; one workspace size covers both
+    assert mpp.scan_chunk(4, 16, 8192, 16) == 64
+    assert mpp.scan_chunk(4, 16, 8192, 16, mpp.DIR_FWD_X) == 32
+    Kx, nchx, _, wsx = mpp.scan_plan(4, 16, 8192, 16, mpp.DIR_FWD_X)
+    assert (Kx, nchx) == (32, 256)
+    assert mpp.workspace_bytes(4, 16, 8192, 16) == wsx > mpp.scan_plan(4, 16, 8192, 16)[3]
+    assert mpp.workspace_bytes(4, 16, 8192, 16, mpp.DIR_FWD_X) == wsx
+    # the same explicit chunk gives the same plan either way
+    assert mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD_X, 5) == mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD, 5)
 
 
 def test_plan_rejects_bad_arguments(mpp):
@@ -232,7 +242,10 @@ def test_survey_boundary_calls(mpp):
     for n in (4, 8, 16, 32):
         for direction in (mpp.DIR_FWD, mpp.DIR_BWD):
             need = lib.mru_scan_workspace_bytes(1, 2, 777, n, direction)
-            assert need == mpp.scan_plan(1, 2, 777, n, direction)[3]
+            plans = [mpp.scan_plan(1, 2, 777, n, direction)[3]]
+            if direction == mpp.DIR_FWD:
+                plans.append(mpp.scan_plan(1, 2, 777, n, mpp.DIR_FWD_X)[3])
+            assert need == max(plans)
             assert need == lib.mru_scan_workspace_bytes_chunked(1, 2, 777, n, direction, 0)
             assert need > 0   # two sequences of 777 tokens: several chunks each
         # a missing workspace is reported by the boundary forms themselves

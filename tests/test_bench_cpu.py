@@ -47,13 +47,69 @@ def test_traffic_record_is_tied_to_the_sources():
     assert len(h) == 16 and h == bench.source_hash()
     # a record taken on other sources is ignored
     assert bench.load_traffic("c2l", "no_such_kernel") is None
+    assert bench.load_mfma_util("c3", "no_such_kernel") is None
+
+
+def test_kernel_kinds():
+    import bench
+    name = ("void mru::(anonymous namespace)::fwd_mfma_kernel<16, 16, 64, true, false>(float const*, "
+            "float*, long, long, long, long, long, unsigned char*, mru::ScanCarry)")
+    short = bench.short_kernel(name)
+    assert short == "fwd_mfma_kernel<16, 16, 64, true, false>"
+    kinds = {
+        short: "fwd_x",
+        "fwd_mfma_kernel<32, 4, 0, false, true>": "fwd_scaled",
+        "fwd_valu_kernel<8, 1, 4, false, false>": "fwd",
+        "bwd_valu_kernel<8, 1, 4, true, false>": "bwd_x",
+        "bwd_mfma_kernel<16, 2, true, true>": "bwd_dx",
+        "bwd_mfma_kernel<16, 8, false, false>": "bwd",
+        "build_mfma_kernel<32>": "build",
+        "build_kernel<8, 1>": "build",
+        "build_bwd_mfma_kernel<16>": "build_bwd",
+        "__amd_rocclr_copyBuffer": "copy",
+        "at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>": None,
+    }
+    for k, v in kinds.items():
+        assert bench.kernel_kind(k) == v, k
+
+
+def test_counter_summary(tmp_path, capsys):
+    """The summarizer's arithmetic on a hand-made counter file."""
+    import json as js
+
+    import bench
+    d = tmp_path / "run"
+    d.mkdir()
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size",'
+           '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+           '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
+    k = '"void mru::(anonymous namespace)::bwd_mfma_kernel<16, 8, false, false>(float const*)"'
+    rows = [hdr]
+    for disp, (busy, grbm) in enumerate(((1024e6, 8e6), (512e6, 8e6), (768e6, 8e6)), 1):
+        for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", grbm), ("SQ_ACTIVE_INST_VALU", busy / 4)):
+            rows.append(f'{disp},{disp},"Agent 1",1,1,1,262144,7,{k},64,0,0,256,80,32,"{c}",{v},0,2000000')
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    saved = bench.MFMA_FILE
+    bench.MFMA_FILE = str(tmp_path / "mfma.json")
+    try:
+        bench.summarize("mfma", [str(d)], "c5", ["cmd"])
+        rec = js.load(open(bench.MFMA_FILE))["workloads"]["c5"]
+        r = rec["kernels"]["bwd"]
+        # median busy 768e6 over 1e6 cycles per XCD x 1024 SIMDs
+        assert r["mfma_busy"] == round(768e6 / (1e6 * 1024), 4)
+        assert r["valu_busy"] == round(192e6 / (1e6 * 1024), 4)
+        # the 2 ms dispatches at 2.4 GHz
+        assert r["mfma_busy_clk"] == round(768e6 / (2e-3 * 2.4e9 * 1024), 4)
+        assert rec["source_hash"] == bench.source_hash()
+        assert bench._record(bench.MFMA_FILE, "c5", "bwd")["grid"] == 262144
+    finally:
+        bench.MFMA_FILE = saved
+    assert "bwd_mfma_kernel<16, 8, false, false>" in capsys.readouterr().out
 
 
 def test_counted_sources_exist():
     import bench
-    csrc = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
-    for f in bench.COUNTED_SOURCES:
-        assert os.path.isfile(os.path.join(csrc, f)), f
+    assert any(f.endswith(".hip") for f in os.listdir(bench.CSRC))
 
 
 def test_cpu_leg_and_parity_sample():

@@ -281,7 +281,7 @@ N16_CASES = [(16, 128, 16, 40, 0), (16, 4, 4, 1000, 0), (16, 2, 3, 203, 5), (16,
 
 @pytest.mark.parametrize("n,B,H,T,chunk", N16_CASES)
 def test_fused_fwd_n16(mpp, n, B, H, T, chunk):
-    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD, chunk)
+    plan = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD_X, chunk)
     say(f"[fused fwd n={n}] B={B} H={H} T={T} chunk={chunk} plan(K,nch,Z,ws)={plan}")
     x = _x(B, H, T, n, seed=T + 7)
     xd = dev(x)
@@ -293,8 +293,10 @@ def test_fused_fwd_n16(mpp, n, B, H, T, chunk):
     assert dom.all() and err.max() <= FWD_TOL
     # against build + scan on the same tokens: the matrix-core build forms each
     # token matrix with the same fp32 products, and the chain is the same, so the
-    # outputs are the same bits
-    P_two = mpp.scan_fwd(mpp.build_inputs(xd, n), chunk)
+    # outputs are the same bits on the same chunks (the automatic plans may
+    # differ: the scan from x's chunk length is passed to the scan from M)
+    kx = mpp.scan_plan(B, H, T, n, mpp.DIR_FWD_X, chunk)[0]
+    P_two = mpp.scan_fwd(mpp.build_inputs(xd, n), kx)
     assert torch.equal(P.view(torch.int32), P_two.view(torch.int32)), "differs from build + scan"
 
 
