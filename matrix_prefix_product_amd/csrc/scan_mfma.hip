@@ -475,6 +475,284 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
     if (WRITE) store_prefix<N, SC>(P, pexp, base + len - 1, X, ex);
 }
 
+// The apply pass of a chunk in fp32 (n = 32): from the carry, computed in fp64
+// by the look-back and rounded once, the chain runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32, half the cycles of the fp64 product).  Its rounding
+// error grows with the chunk length only, since the carry is exact to fp64 at
+// every chunk start (chunks of at most kF32ChainMax tokens; measured with the
+// oracle on the n = 32 workload's inputs, 512-token chunks: 3.1e-6 relative).
+// The state is kept as 2^ex Y with Y in fp32: the carry is scaled by a power
+// of two into range first; every fourth step the largest |entry| of the state
+// the step consumes is found (while the step's products run) and, if its
+// exponent has left [-60, 60], the step's result is rescaled by that power of
+// two (exact).  Each P_t is stored as 2^ex Y (IEEE overflow to inf where P_t
+// leaves the fp32 range, as the fp64 pass stores it).  If the state ever holds
+// an inf, a NaN or only subnormal values the pass gives up (returns false) and
+// the caller re-runs the chunk with the fp64 pass, which overwrites every P_t
+// of the chunk.  The scaled scans (SC) renormalise exactly after every step,
+// as the fp64 pass does.
+// Layouts: the fp32 accumulator tile holds the same entries per lane and
+// register as the fp64 one (Y[16I + trow(l, r)][16J + tcol(l)], Y = P^T),
+// with the natural row order instead of pi, so the A-operand entries of M_t^T
+// are M_t[16K + trow(l, b)][16I + tcol(l)]: the same LDS transpose read at
+// column tcol instead of tacol, and for raw token vectors the same fp64 LDU
+// tile (ldu_tile_f64) with its columns in natural order, entry for entry the
+// same bits as the build.
+constexpr int kF32ChainMax = 1024;
+
+template <int N>
+struct Mf32 {
+    static constexpr int NT = N / 16;
+    struct vec_t {
+        f4v32 t[NT][NT];
+    };
+};
+
+template <int N>
+__device__ inline void operand_read_f32(float (&o)[4 * Stage<N>::NV], const float* tb) {
+    constexpr int NT = N / 16;
+    constexpr int LS = Stage<N>::LS;
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int K = 0; K < NT; ++K) {
+            const float4 w =
+                *reinterpret_cast<const float4*>(tb + (16 * I + tcol(l)) * LS + 16 * K + trow(l, 0));
+            float* d = &o[(I * NT + K) * 4];
+            d[0] = w.x; d[1] = w.y; d[2] = w.z; d[3] = w.w;
+        }
+}
+
+template <int N>
+__device__ inline void xop_read_f32(float (&o)[4 * Stage<N>::NV], const float* slot) {
+    constexpr int NT = N / 16;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int K = 0; K < NT; ++K) {
+            const f64x4 acc = ldu_tile_f64<N, false>(
+                slot, slot_ed<N>(slot), K, I, [&](int i) { return 16 * K + pirow(i); },
+                [&](int j) { return 16 * I + j; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[(I * NT + K) * 4 + r] = float(acc[r]);
+        }
+}
+
+template <int N, class Between>
+__device__ inline typename Mf32<N>::vec_t chain_step_f32_with(const float (&a)[4 * Stage<N>::NV],
+                                                              const typename Mf32<N>::vec_t& Y,
+                                                              Between&& between) {
+    constexpr int NT = N / 16;
+    typename Mf32<N>::vec_t out;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+            f4v32 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int K = 0; K < NT; ++K)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(I * NT + K) * 4 + b], Y.t[K][J][b], acc, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    between(((I * NT + J) * NT + K) * 4 + b);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            out.t[I][J] = acc;
+        }
+    return out;
+}
+
+// Largest |entry| of Y over the wave, as the bits of |x| (monotonic in |x|;
+// >= 0x7f800000: inf or NaN present; 0: all zero).  The lane maxima are
+// combined with DPP within each 16-lane row and across the four rows through
+// scalar registers (no LDS round trips).
+__device__ inline uint32_t dpp_max16(uint32_t k) {
+    k = max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0xB1, 0xF, 0xF, false)));
+    k = max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x4E, 0xF, 0xF, false)));
+    k = max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x141, 0xF, 0xF, false)));
+    k = max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x140, 0xF, 0xF, false)));
+    return k;
+}
+
+template <int N>
+__device__ inline uint32_t f32_key(const typename Mf32<N>::vec_t& Y) {
+    uint32_t k = 0;
+#pragma unroll
+    for (int I = 0; I < N / 16; ++I)
+#pragma unroll
+        for (int J = 0; J < N / 16; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) k = max(k, __float_as_uint(Y.t[I][J][r]) & 0x7fffffffu);
+    k = dpp_max16(k);
+    const uint32_t a = __builtin_amdgcn_readlane(int(k), 0), b = __builtin_amdgcn_readlane(int(k), 16);
+    const uint32_t c = __builtin_amdgcn_readlane(int(k), 32), d = __builtin_amdgcn_readlane(int(k), 48);
+    return max(max(a, b), max(c, d));
+}
+
+template <int N>
+__device__ inline void scale_f32(typename Mf32<N>::vec_t& Y, int e) {
+#pragma unroll
+    for (int I = 0; I < N / 16; ++I)
+#pragma unroll
+        for (int J = 0; J < N / 16; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y.t[I][J][r] = ldexpf(Y.t[I][J][r], e);
+}
+
+template <int N, bool SC>
+__device__ inline void store_prefix_f32(float* __restrict__ P, int32_t* __restrict__ pexp, int64_t tok,
+                                        const typename Mf32<N>::vec_t& Y, int ex) {
+    const int l = threadIdx.x & 63;
+    float* p = P + tok * N * N;
+    if (SC || ex == 0) {
+#pragma unroll
+        for (int I = 0; I < N / 16; ++I)
+#pragma unroll
+            for (int J = 0; J < N / 16; ++J)
+                *reinterpret_cast<f4v32*>(p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0)) = Y.t[I][J];
+    } else {
+#pragma unroll
+        for (int I = 0; I < N / 16; ++I)
+#pragma unroll
+            for (int J = 0; J < N / 16; ++J) {
+                f4v32 v = Y.t[I][J];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = ldexpf(v[r], ex);
+                *reinterpret_cast<f4v32*>(p + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0)) = v;
+            }
+    }
+    if (SC && l == 0) pexp[tok] = ex;
+}
+
+// The apply pass in fp32 from the fp64 carry X (SC: normalised, exponent ex);
+// false if it gave up (see above).
+template <int N, int PF, bool FX, bool SC>
+__device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N>::vec_t& X, int ex,
+                                                             const float* __restrict__ M, float* __restrict__ P,
+                                                             int32_t* __restrict__ pexp, int64_t base, int len,
+                                                             float* tlds, float* xlds) {
+    using vec_t = typename Mf32<N>::vec_t;
+    constexpr int NN = N * N;
+    constexpr int NA = 4 * Stage<N>::NV;
+    if (len <= 0) return true;
+    // the carry scaled by 2^-e0 (its largest |entry| into [0.5, 1)), then rounded
+    int e0 = kNoExp;
+#pragma unroll
+    for (int I = 0; I < N / 16; ++I)
+#pragma unroll
+        for (int J = 0; J < N / 16; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e0 = max_exp(e0, X.t[I][J][r]);
+    e0 = __builtin_amdgcn_readfirstlane(group_max<64>(e0));
+    if (e0 == kNoExp) e0 = 0;
+    vec_t Y;
+#pragma unroll
+    for (int I = 0; I < N / 16; ++I)
+#pragma unroll
+        for (int J = 0; J < N / 16; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y.t[I][J][r] = float(ldexp(X.t[I][J][r], -e0));
+    ex += e0;
+    bool ok = true;
+    const float* Mb = M + base * NN;
+    float ring[PF][NA];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_token<N>(ring[p], Mb + int64_t(min(p, len - 1)) * NN);
+    float o[NA];
+    if constexpr (FX) {
+        static_assert(PF >= 3, "two tokens ahead of the chain");
+        xop_stage<N>(ring[0], xlds);
+        __syncthreads();
+        xop_factors<N>(xlds);
+        __syncthreads();
+        xop_read_f32<N>(o, xlds);
+        if (len > 1) {
+            float* x1 = xlds + xslot<N, FX>();
+            xop_stage<N>(ring[1], x1);
+            __syncthreads();
+            xop_factors<N>(x1);
+            __syncthreads();
+        }
+        load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
+        load_token<N>(ring[1], Mb + int64_t(min(PF + 1, len - 1)) * NN);
+    } else {
+        operand_write<N>(ring[0], tlds);
+        __syncthreads();
+        operand_read_f32<N>(o, tlds);
+        load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
+    }
+    auto step = [&](int p, int t, bool refill) {
+        float a[NA];
+#pragma unroll
+        for (int e = 0; e < NA; ++e) a[e] = o[e];
+        vec_t Yn;
+        uint32_t kprev = 0;  // the consumed state's largest |entry| (checked steps)
+        if constexpr (FX) {
+            const int p2 = (p + 2) % PF;
+            float* x1 = xlds + ((t + 1) & 1) * xslot<N, FX>();
+            float* x2 = xlds + (t & 1) * xslot<N, FX>();
+            Yn = chain_step_f32_with<N>(a, Y, [&](int k) {
+                if (k == 0 && t + 1 < len) xop_read_f32<N>(o, x1);
+                if (k == 1 && t + 2 < len) xop_stage<N>(ring[p2], x2);
+                if (k == 2) {
+                    if (t > 0) store_prefix_f32<N, SC>(P, pexp, base + t - 1, Y, ex);
+                    if (t + 2 < len) {
+                        __syncthreads();
+                        xop_factors<N>(x2);
+                    }
+                }
+                if (k == 3 && t + 2 < len) {
+                    __syncthreads();
+                    if (refill) load_token<N>(ring[p2], Mb + int64_t(min(t + 2 + PF, len - 1)) * NN);
+                }
+                if (k == 8 && !SC && (t & 3) == 3) kprev = f32_key<N>(Y);
+            });
+        } else {
+            const int pn = (p + 1) % PF;
+            float* tb = tlds + ((t + 1) & 1) * Stage<N>::BUF;
+            Yn = chain_step_f32_with<N>(a, Y, [&](int k) {
+                if (k == 0 && t + 1 < len) operand_write<N>(ring[pn], tb);
+                if (k == 1 && t + 1 < len) {
+                    __syncthreads();
+                    operand_read_f32<N>(o, tb);
+                }
+                if (k == 2 && t > 0) store_prefix_f32<N, SC>(P, pexp, base + t - 1, Y, ex);
+                if (k == 3 && t + 1 < len && refill)
+                    load_token<N>(ring[pn], Mb + int64_t(min(t + 1 + PF, len - 1)) * NN);
+                if (k == 8 && !SC && (t & 3) == 3) kprev = f32_key<N>(Y);
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        Y = Yn;
+        if (SC || (t & 3) == 3) {
+            const uint32_t k = SC ? f32_key<N>(Y) : kprev;
+            if (k >= 0x7f800000u || (k != 0 && k < 0x00800000u)) {
+                ok = false;  // inf / NaN, or nothing but subnormals: the fp64 pass redoes the chunk
+            } else if (k != 0) {
+                const int e = int(k >> 23) - 126;  // largest |entry| in [2^(e-1), 2^e)
+                if (SC || e > 60 || e < -60) {
+                    scale_f32<N>(Y, -e);
+                    ex += e;
+                }
+            }
+        }
+    };
+    int t0 = 0;
+    for (; t0 + PF <= len && ok; t0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) step(p, t0 + p, true);
+    }
+    if (!ok) return false;
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (t0 + p < len) step(p, t0 + p, false);
+    if (!ok) return false;
+    store_prefix_f32<N, SC>(P, pexp, base + len - 1, Y, ex);
+    return true;
+}
+
 // Retained chunk (KR > 0).  The aggregate pass loads the chunk's tokens into a
 // register buffer of KR tokens (loads issued PF tokens ahead, clamped into the
 // chunk) and converts each to its operand entries in place; once a token's
@@ -832,6 +1110,8 @@ void fwd_mfma_kernel(const float* __restrict__ M,
 
     // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised matrix)
     vec_t X = videntity<N>(l);
+    // n = 32: the apply pass runs in fp32 (fwd_sweep_f32)
+    constexpr bool kF32Apply = N == 32 && KR == 0;
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0) {
         constexpr int PFR = N == 16 ? kPfRetain16 : PF;
@@ -839,8 +1119,9 @@ void fwd_mfma_kernel(const float* __restrict__ M,
             fwd_pass_retain<N, KR, PFR, FX, SC, true>(X, ex, M, ch.base, ch.len, buf, tlds, xlds, plds, exl);
         else
             fwd_pass_retain<N, KR, PFR, FX, SC, false>(X, ex, M, ch.base, ch.len, buf, tlds, xlds, plds, exl);
-    } else
+    } else {
         fwd_sweep<N, PF, false, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
+    }
     const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
     if (SC && l == 0) ws_store(&agg_exp[c], int32_t(a_ex));
@@ -906,10 +1187,16 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     }
 
     // 4. re-run from the carry
-    if constexpr (KR > 0)
+    if constexpr (KR > 0) {
         fwd_apply_retain<N, KR, SC>(X, ex, P, cy.out_exp, ch.base, ch.len, buf, exl);
-    else
-        fwd_sweep<N, PF, true, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
+    } else {
+        bool done = false;
+        if constexpr (kF32Apply)
+            if (ch.len <= kF32ChainMax)
+                done = fwd_sweep_f32<N, PF, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
+        if (!done)
+            fwd_sweep<N, PF, true, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
+    }
 }
 
 // ---------------------------------------------------------------------------- backward
