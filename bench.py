@@ -248,33 +248,39 @@ def summarize(what: str, dirs, workload: str, commands) -> None:
                 kernels[kind] = {"kernel": k, "grid": grid, "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
                                  "read_bytes": rb, "write_bytes": wb}
     else:
-        # matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of the
-        # kernel, with GRBM_GUI_ACTIVE (summed over the XCDs) as the kernel's
-        # cycles; vector ALU: SQ_ACTIVE_INST_VALU (cycles a wave issues VALU
-        # work, 4 per instruction) over the same SIMD-cycles
-        head += ["# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);",
-                 "# valu_busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / 8 x 1024); the *_clk figures use the",
-                 "# kernel's duration x 2.4 GHz as its cycles instead; medians over the dispatches"]
+        # matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs; an
+        # f64 16x16x4 product counts 64 cycles, an f32 one 32) over the SIMD-cycles
+        # of the kernel, with GRBM_GUI_ACTIVE (summed over the 8 XCDs) as the
+        # kernel's cycles; vector ALU: SQ_INSTS_VALU wave instructions at 4 issue
+        # cycles each (wave64 on a 16-lane SIMD) over the same SIMD-cycles
+        head += ["# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)",
+                 "#   (the counter sums SIMD-cycles: 64 per f64 16x16x4 product, 32 per f32 one; the n = 16",
+                 "#   build reads exactly 4 x 64 per token);",
+                 "# valu_busy = 4 x SQ_INSTS_VALU / (GRBM_GUI_ACTIVE / 8 x 1024) (4 issue cycles per wave64",
+                 "#   instruction); the *_clk figures take the kernel's duration x 2.4 GHz as its cycles;",
+                 "# clock_GHz = GRBM_GUI_ACTIVE / 8 / duration; medians over the dispatches"]
         cols = (f"{'kernel':48s} {'grid':>9s} {'us':>9s} {'mfma_busy':>10s} {'mfma_clk':>9s} {'valu_busy':>10s} "
-                f"{'valu_clk':>9s} {'MFMA_BUSY':>14s} {'GRBM_ACTIVE':>12s}")
+                f"{'valu_clk':>9s} {'clock_GHz':>9s} {'MFMA_BUSY':>14s} {'VALU_INSTS':>12s} {'GRBM_ACTIVE':>12s}")
         lines = []
         for (k, grid), v in sorted(data.items(), key=lambda kv: -_median(kv[1]["dur_ns"])):
             if "SQ_VALU_MFMA_BUSY_CYCLES" not in v or "GRBM_GUI_ACTIVE" not in v:
                 continue
             mb, gr, us = _median(v["SQ_VALU_MFMA_BUSY_CYCLES"]), _median(v["GRBM_GUI_ACTIVE"]), _median(v["dur_ns"]) / 1e3
-            va = _median(v.get("SQ_ACTIVE_INST_VALU", [0.0]))
+            vi = _median(v.get("SQ_INSTS_VALU", [0.0]))
             simd_cyc = gr / XCDS * SIMDS
             clk_cyc = us * 1e-6 * NOMINAL_CLOCK_HZ * SIMDS
             r = {"kernel": k, "grid": grid, "us": round(us, 1),
                  "mfma_busy": round(mb / simd_cyc, 4), "mfma_busy_clk": round(mb / clk_cyc, 4),
-                 "valu_busy": round(va / simd_cyc, 4), "valu_busy_clk": round(va / clk_cyc, 4),
-                 "SQ_VALU_MFMA_BUSY_CYCLES": mb, "SQ_ACTIVE_INST_VALU": va, "GRBM_GUI_ACTIVE": gr}
+                 "valu_busy": round(4 * vi / simd_cyc, 4), "valu_busy_clk": round(4 * vi / clk_cyc, 4),
+                 "clock_GHz": round(gr / XCDS / (us * 1e-6) / 1e9, 3),
+                 "SQ_VALU_MFMA_BUSY_CYCLES": mb, "SQ_INSTS_VALU": vi, "GRBM_GUI_ACTIVE": gr}
             for c in ("SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F64", "SQ_INSTS_MFMA",
-                      "SQ_INSTS_VALU", "SQ_ACTIVE_INST_LDS"):
+                      "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"):
                 if c in v:
                     r[c] = _median(v[c])
             lines.append(f"{k[:48]:48s} {grid:9d} {us:9.1f} {r['mfma_busy']:10.4f} {r['mfma_busy_clk']:9.4f} "
-                         f"{r['valu_busy']:10.4f} {r['valu_busy_clk']:9.4f} {mb:14.0f} {gr:12.0f}")
+                         f"{r['valu_busy']:10.4f} {r['valu_busy_clk']:9.4f} {r['clock_GHz']:9.3f} {mb:14.0f} "
+                         f"{vi:12.0f} {gr:12.0f}")
             kind = kernel_kind(k)
             if kind and kind != "copy":
                 kernels[kind] = r

@@ -86,7 +86,7 @@ def test_counter_summary(tmp_path, capsys):
     k = '"void mru::(anonymous namespace)::bwd_mfma_kernel<16, 8, false, false>(float const*)"'
     rows = [hdr]
     for disp, (busy, grbm) in enumerate(((1024e6, 8e6), (512e6, 8e6), (768e6, 8e6)), 1):
-        for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", grbm), ("SQ_ACTIVE_INST_VALU", busy / 4)):
+        for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", grbm), ("SQ_INSTS_VALU", busy / 16)):
             rows.append(f'{disp},{disp},"Agent 1",1,1,1,262144,7,{k},64,0,0,256,80,32,"{c}",{v},0,2000000')
     (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
     saved = bench.MFMA_FILE
@@ -97,7 +97,8 @@ def test_counter_summary(tmp_path, capsys):
         r = rec["kernels"]["bwd"]
         # median busy 768e6 over 1e6 cycles per XCD x 1024 SIMDs
         assert r["mfma_busy"] == round(768e6 / (1e6 * 1024), 4)
-        assert r["valu_busy"] == round(192e6 / (1e6 * 1024), 4)
+        assert r["valu_busy"] == round(4 * 48e6 / (1e6 * 1024), 4)
+        assert r["clock_GHz"] == round(1e6 / 2e-3 / 1e9, 3)
         # the 2 ms dispatches at 2.4 GHz
         assert r["mfma_busy_clk"] == round(768e6 / (2e-3 * 2.4e9 * 1024), 4)
         assert rec["source_hash"] == bench.source_hash()
