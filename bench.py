@@ -222,7 +222,9 @@ def summarize(what: str, dirs, workload: str, commands) -> None:
         # the same runs; without one, the factors of the record's last copy
         cal = rec.get("copy_kernel")
         for (k, grid), v in data.items():
-            if kernel_kind(k) == "copy" and "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+            # the 1 GiB copy of copy_reference (other runtime copies are small)
+            if kernel_kind(k) == "copy" and "FETCH_SIZE" in v and "WRITE_SIZE" in v \
+                    and abs(_median(v["WRITE_SIZE"]) - 2 ** 20) < 0.05 * 2 ** 20:
                 f, w = _median(v["FETCH_SIZE"]), _median(v["WRITE_SIZE"])
                 cal = {"name": f"{k} (torch copy_ of 1 GiB)", "bytes_read": 2 ** 30, "bytes_written": 2 ** 30,
                        "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
