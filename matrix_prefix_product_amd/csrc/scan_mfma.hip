@@ -1240,13 +1240,21 @@ __device__ inline void x_operand_direct(typename Mf<N>::aop_t& a, const float* x
 // staged x_t and its e into build_vjp_token, the same routine as the build's
 // gradient kernel, so dx is bit for bit build_inputs_bwd(x, dM); dxl holds gs,
 // the dx staging ds (both row stride n + 4) and 4 floats for the mean.
-template <int N, int PF, bool GRAD, bool FX, bool DX>
+// KR > 0 (a whole chunk of KR tokens, len == KR): the sweep runs expanded at
+// compile time and keeps dL/dP in registers across the two passes: the
+// aggregate pass copies each token's dP_t operand into keep, the pass from
+// the carry takes it from there and reads only M and P.
+template <int N, int PF, bool GRAD, bool FX, bool DX, int KR = 0, int KB>
 __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& G, typename Mf<N>::vec_t& W,
                           const float* __restrict__ M, const float* __restrict__ P,
                           const float* __restrict__ dP, float* __restrict__ dM, double* tr,
-                          float* xs, float* dxl, int64_t base, int64_t t0, int len, int64_t T,
-                          const ScanCarry& cy) {
+                          float* xs, float* dxl, int64_t base, int64_t t0, int len_in, int64_t T,
+                          const ScanCarry& cy,
+                          float (&keep)[KB][4 * (N / 16) * (N / 16)]) {
     static_assert(!DX || (FX && GRAD), "the gradient to x starts from raw token vectors");
+    static_assert(KR == 0 || (!FX && !DX), "the retained sweep starts from M");
+    static_assert(KR <= KB, "the buffer holds the chunk");
+    const int len = KR > 0 ? KR : len_in;
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NT = F::NT;
@@ -1295,15 +1303,17 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
                     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
                 }
         }
+        if constexpr (!(KR > 0 && GRAD)) {  // the retained pass from the carry keeps dP_t
 #pragma unroll
-        for (int I = 0; I < NT; ++I)
+            for (int I = 0; I < NT; ++I)
 #pragma unroll
-            for (int J = 0; J < NT; ++J) {
-                const float4 v = *reinterpret_cast<const float4*>(
-                    Rb + int64_t(pos) * NN + (16 * J + c) * N + 16 * I + trow(l, 0));
-                float* d = &rr[slot][(I * NT + J) * 4];
-                d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-            }
+                for (int J = 0; J < NT; ++J) {
+                    const float4 v = *reinterpret_cast<const float4*>(
+                        Rb + int64_t(pos) * NN + (16 * J + c) * N + 16 * I + trow(l, 0));
+                    float* d = &rr[slot][(I * NT + J) * 4];
+                    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+                }
+        }
         if constexpr (GRAD) {
             const int pp = max(pos, lo_p) - 1;  // clamped: only used when pos >= lo_p
 #pragma unroll
@@ -1426,6 +1436,19 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
     };
 #pragma unroll
     for (int p = 0; p < PF; ++p) fetch(p, min(p, len - 1));
+    if constexpr (KR > 0) {
+        static_for(std::make_integer_sequence<int, KR>{}, [&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int p = i % PF;
+#pragma unroll
+            for (int e = 0; e < NA; ++e) {
+                if constexpr (GRAD) rr[p][e] = keep[i][e];
+                else keep[i][e] = rr[p][e];
+            }
+            step(p, i, i + PF < KR);
+        });
+        return;
+    }
     int i0 = 0;
     for (; i0 + PF <= len; i0 += PF) {
 #pragma unroll
@@ -1445,7 +1468,7 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
 template <int N, bool FX>
 constexpr int bwd_waves() { return (N == 16 && FX) ? 2 : 1; }
 
-template <int N, int PF, bool FX, bool DX>
+template <int N, int PF, bool FX, bool DX, int KRB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bwd_waves<N, FX>(), bwd_waves<N, FX>())))
 void bwd_mfma_kernel(const float* __restrict__ M,
                                                       const float* __restrict__ P,
@@ -1472,10 +1495,12 @@ void bwd_mfma_kernel(const float* __restrict__ M,
 
     vec_t G = vzero<N>();
     vec_t W = videntity<N>(l);
+    float keep[KRB > 0 ? KRB : 1][4 * (N / 16) * (N / 16)];  // KRB: a whole chunk's dL/dP operands
     if (!multi) {
-        bwd_sweep<N, PF, true, FX, DX>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy);
+        bwd_sweep<N, PF, true, FX, DX>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy, keep);
         return;
     }
+    const bool retain = KRB > 0 && ch.len == KRB;
     // Chunks run in reverse token order (position r = 0 is the sequence's last
     // chunk).  Registers hold G = Q^T; a chunk's map is G -> W G + Bl (G form),
     // stored as the rows of W^T and of Bl^T = Q.
@@ -1490,7 +1515,11 @@ void bwd_mfma_kernel(const float* __restrict__ M,
     const bool later = r >= Z;
 
     // 1. affine aggregate
-    bwd_sweep<N, PF, false, FX, false>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy);
+    if (retain)
+        bwd_sweep<N, PF, false, FX, false, KRB>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy,
+                                                keep);
+    else
+        bwd_sweep<N, PF, false, FX, false>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy, keep);
     ws_store_acc_rows<N>(sbl + c * NN, G);
     ws_store_acc_rows<N>(swt + c * NN, W);
     fence_release();
@@ -1538,7 +1567,10 @@ void bwd_mfma_kernel(const float* __restrict__ M,
     }
 
     // 4. re-run from the carry, writing dM
-    bwd_sweep<N, PF, true, FX, DX>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy);
+    if (retain)
+        bwd_sweep<N, PF, true, FX, DX, KRB>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy, keep);
+    else
+        bwd_sweep<N, PF, true, FX, DX>(G, W, M, P, dP, dM, tr, xs, dxl, ch.base, ch.t0, ch.len, T, cy, keep);
 }
 
 template <int N, int PF, int KR, bool FX>
@@ -1553,11 +1585,11 @@ hipError_t run_fwd(const float* M, float* P, int64_t S, int64_t T, int64_t K, in
     return hipGetLastError();
 }
 
-template <int N, int PF, bool FX, bool DX>
+template <int N, int PF, bool FX, bool DX, int KRB = 0>
 hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, int64_t S,
                    int64_t T, int64_t K, int64_t nch, int64_t Z, void* ws, hipStream_t stream,
                    const ScanCarry& cy) {
-    hipLaunchKernelGGL((bwd_mfma_kernel<N, PF, FX, DX>), dim3(unsigned(S * nch)), dim3(64), 0,
+    hipLaunchKernelGGL((bwd_mfma_kernel<N, PF, FX, DX, KRB>), dim3(unsigned(S * nch)), dim3(64), 0,
                        stream, M, P, dP, dM, S, T, K, nch, Z, static_cast<unsigned char*>(ws), cy);
     return hipGetLastError();
 }
@@ -1571,6 +1603,8 @@ constexpr int kRetain16 = 64;
 // build's vector-ALU work of one wave runs while the other's products run on
 // the matrix cores; measured faster than 64-token chunks at one wave)
 constexpr int kRetain16x = 32;
+// the n = 16 backward from M: whole chunks of this length keep dL/dP in registers
+constexpr int kRetainBwd16 = 64;
 constexpr int kPf16 = 16;
 
 int mfma_retain_tokens(int n, bool from_x) { return n == 16 ? (from_x ? kRetain16x : kRetain16) : 0; }
@@ -1607,6 +1641,10 @@ hipError_t launch_bwd_mfma(const float* M, const float* P, const float* dP, floa
     if (n == 16) {
         if (to_dx) return run_bwd<16, 2, true, true>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
         if (from_x) return run_bwd<16, 4, true, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
+        // 64-token chunks keep dL/dP in registers between the passes (a shallower
+        // ring makes room for them)
+        if (nch > 1 && K == kRetainBwd16)
+            return run_bwd<16, 4, false, false, kRetainBwd16>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
         return run_bwd<16, 8, false, false>(M, P, dP, dM, S, T, K, nch, Z, ws, stream, cy);
     }
     if (n == 32) {

@@ -275,6 +275,7 @@ def test_layer_bwd_dx_n16(mpp, n, B, H, T, chunk):
 # auto plan, a ragged forced chunk, exactly 64 tokens), streamed chunks (longer
 # than the register buffer; every n = 32 chunk), a single token
 N16_CASES = [(16, 128, 16, 40, 0), (16, 4, 4, 1000, 0), (16, 2, 3, 203, 5), (16, 2, 2, 130, 64),
+             (16, 2, 3, 1000, 32),
              (16, 1, 2, 300, 100), (16, 3, 1, 1, 0),
              (32, 64, 16, 12, 0), (32, 1, 4, 700, 0), (32, 2, 1, 301, 37), (32, 2, 1, 1, 0)]
 

@@ -95,6 +95,7 @@ FWD_CASES = [
     (8, 8, 8, 256, 0), (8, 2, 3, 203, 5), (8, 1, 2, 203, 1), (8, 33, 1, 64, 64), (8, 2, 2, 500, 16),
     (16, 1, 6, 1000, 0), (16, 2, 3, 1000, 7), (16, 3, 1, 257, 257), (16, 1, 2, 130, 1),
     (16, 2, 3, 1024, 32), (16, 1, 2, 96, 32), (16, 3, 1, 4096, 32),  # chunks dividing T
+    (16, 2, 3, 1000, 64), (16, 1, 2, 128, 64),  # whole 64-token chunks (registers kept) and a ragged one
     (32, 1, 3, 600, 0), (32, 1, 2, 600, 13), (32, 2, 1, 150, 150), (32, 1, 1, 70, 1),
 ]
 
@@ -220,6 +221,7 @@ BWD_CASES = [
     (8, 8, 8, 256, 0), (8, 2, 3, 203, 5), (8, 1, 2, 203, 1), (8, 33, 1, 64, 64), (8, 2, 2, 500, 16),
     (16, 1, 6, 1000, 0), (16, 2, 3, 1000, 7), (16, 3, 1, 257, 257), (16, 1, 2, 130, 1),
     (16, 2, 3, 1024, 32), (16, 1, 2, 96, 32), (16, 3, 1, 4096, 32),  # chunks dividing T
+    (16, 2, 3, 1000, 64), (16, 1, 2, 128, 64),  # whole 64-token chunks (registers kept) and a ragged one
     (32, 1, 3, 600, 0), (32, 1, 2, 600, 13), (32, 2, 1, 150, 150), (32, 1, 1, 70, 1),
 ]
 
