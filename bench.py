@@ -147,10 +147,13 @@ def kernel_kind(short: str):
     if not m:
         return None
     fam, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    # template arguments: fwd_*_kernel<n, ., ., FX, SC>, bwd_valu_kernel<n, R, TB, FX, DX>,
+    # bwd_mfma_kernel<n, PF, FX, DX, KR>
     if fam in ("fwd_valu_kernel", "fwd_mfma_kernel"):
-        return ("fwd_x" if args[-2] == "true" else "fwd") + ("_scaled" if args[-1] == "true" else "")
+        return ("fwd_x" if args[3] == "true" else "fwd") + ("_scaled" if args[4] == "true" else "")
     if fam in ("bwd_valu_kernel", "bwd_mfma_kernel"):
-        return "bwd_dx" if args[-1] == "true" else ("bwd_x" if args[-2] == "true" else "bwd")
+        fx, dx = (args[3], args[4]) if fam == "bwd_valu_kernel" else (args[2], args[3])
+        return "bwd_dx" if dx == "true" else ("bwd_x" if fx == "true" else "bwd")
     if fam in ("build_kernel", "build_mfma_kernel"):
         return "build"
     if fam in ("build_bwd_kernel", "build_bwd_mfma_kernel"):

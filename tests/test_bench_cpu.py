@@ -61,8 +61,10 @@ def test_kernel_kinds():
         "fwd_mfma_kernel<32, 4, 0, false, true>": "fwd_scaled",
         "fwd_valu_kernel<8, 1, 4, false, false>": "fwd",
         "bwd_valu_kernel<8, 1, 4, true, false>": "bwd_x",
-        "bwd_mfma_kernel<16, 2, true, true>": "bwd_dx",
-        "bwd_mfma_kernel<16, 8, false, false>": "bwd",
+        "bwd_mfma_kernel<16, 2, true, true, 0>": "bwd_dx",
+        "bwd_mfma_kernel<16, 4, true, false, 0>": "bwd_x",
+        "bwd_mfma_kernel<16, 4, false, false, 64>": "bwd",
+        "bwd_valu_kernel<8, 1, 4, true, true>": "bwd_dx",
         "build_mfma_kernel<32>": "build",
         "build_kernel<8, 1>": "build",
         "build_bwd_mfma_kernel<16>": "build_bwd",
@@ -83,7 +85,7 @@ def test_counter_summary(tmp_path, capsys):
     hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size",'
            '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
            '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
-    k = '"void mru::(anonymous namespace)::bwd_mfma_kernel<16, 8, false, false>(float const*)"'
+    k = '"void mru::(anonymous namespace)::bwd_mfma_kernel<16, 8, false, false, 0>(float const*)"'
     rows = [hdr]
     for disp, (busy, grbm) in enumerate(((1024e6, 8e6), (512e6, 8e6), (768e6, 8e6)), 1):
         for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("GRBM_GUI_ACTIVE", grbm), ("SQ_INSTS_VALU", busy / 16)):
@@ -105,7 +107,7 @@ def test_counter_summary(tmp_path, capsys):
         assert bench._record(bench.MFMA_FILE, "c5", "bwd")["grid"] == 262144
     finally:
         bench.MFMA_FILE = saved
-    assert "bwd_mfma_kernel<16, 8, false, false>" in capsys.readouterr().out
+    assert "bwd_mfma_kernel<16, 8, false, false, 0>" in capsys.readouterr().out
 
 
 def test_counted_sources_exist():
