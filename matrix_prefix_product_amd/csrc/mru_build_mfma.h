@@ -10,6 +10,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "mru_mfma.h"
+
 namespace mru {
 
 // Sum over each row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -185,7 +187,7 @@ __device__ inline void build_vjp_token(const float* xs, const float* gs, const f
             eg += es[i] * g[I][r];
         }
     if ((l & 15) == 0) part[m] = eg;
-    __syncthreads();
+    wave_lds_sync();
     const float meaneg = (((part[0] + part[1]) + part[2]) + part[3]) * (1.0f / N);
 #pragma unroll
     for (int I = 0; I < NT; ++I)

@@ -234,7 +234,7 @@ template <int N>
 __device__ inline void to_operand(float (&o)[4 * Stage<N>::NV], const float (&v)[4 * Stage<N>::NV],
                                   float* tb) {
     operand_write<N>(v, tb);
-    __syncthreads();
+    wave_lds_sync();
     operand_read<N>(o, tb);
 }
 
@@ -356,9 +356,9 @@ template <int N>
 __device__ inline void to_operand_x(float (&o)[4 * Stage<N>::NV], const float (&v)[4 * Stage<N>::NV],
                                     float* slot) {
     xop_stage<N>(v, slot);
-    __syncthreads();
+    wave_lds_sync();
     xop_factors<N>(slot);
-    __syncthreads();
+    wave_lds_sync();
     xop_read<N>(o, slot);
 }
 
@@ -412,9 +412,9 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
         if (len > 1) {
             float* x1 = xlds + xslot<N, FX>();
             xop_stage<N>(ring[1], x1);
-            __syncthreads();
+            wave_lds_sync();
             xop_factors<N>(x1);
-            __syncthreads();
+            wave_lds_sync();
         }
         load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
         load_token<N>(ring[1], Mb + int64_t(min(PF + 1, len - 1)) * NN);
@@ -436,12 +436,12 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
                 if (k == 2) {
                     if (WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
                     if (t + 2 < len) {
-                        __syncthreads();
+                        wave_lds_sync();
                         xop_factors<N>(x2);
                     }
                 }
                 if (k == 3 && t + 2 < len) {
-                    __syncthreads();
+                    wave_lds_sync();
                     if (refill) load_token<N>(ring[p2], Mb + int64_t(min(t + 2 + PF, len - 1)) * NN);
                 }
             });
@@ -452,7 +452,7 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
             Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
                 if (k == 0 && t + 1 < len) operand_write<N>(ring[pn], tb);
                 if (k == 1 && t + 1 < len) {
-                    __syncthreads();
+                    wave_lds_sync();
                     operand_read<N>(o, tb);
                 }
                 if (k == 2 && WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
@@ -664,22 +664,22 @@ __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N
     if constexpr (FX) {
         static_assert(PF >= 3, "two tokens ahead of the chain");
         xop_stage<N>(ring[0], xlds);
-        __syncthreads();
+        wave_lds_sync();
         xop_factors<N>(xlds);
-        __syncthreads();
+        wave_lds_sync();
         xop_read_f32<N>(o, xlds);
         if (len > 1) {
             float* x1 = xlds + xslot<N, FX>();
             xop_stage<N>(ring[1], x1);
-            __syncthreads();
+            wave_lds_sync();
             xop_factors<N>(x1);
-            __syncthreads();
+            wave_lds_sync();
         }
         load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
         load_token<N>(ring[1], Mb + int64_t(min(PF + 1, len - 1)) * NN);
     } else {
         operand_write<N>(ring[0], tlds);
-        __syncthreads();
+        wave_lds_sync();
         operand_read_f32<N>(o, tlds);
         load_token<N>(ring[0], Mb + int64_t(min(PF, len - 1)) * NN);
     }
@@ -699,12 +699,12 @@ __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N
                 if (k == 2) {
                     if (t > 0) store_prefix_f32<N, SC>(P, pexp, base + t - 1, Y, ex);
                     if (t + 2 < len) {
-                        __syncthreads();
+                        wave_lds_sync();
                         xop_factors<N>(x2);
                     }
                 }
                 if (k == 3 && t + 2 < len) {
-                    __syncthreads();
+                    wave_lds_sync();
                     if (refill) load_token<N>(ring[p2], Mb + int64_t(min(t + 2 + PF, len - 1)) * NN);
                 }
                 if (k == 8 && !SC && (t & 3) == 3) kprev = f32_key<N>(Y);
@@ -715,7 +715,7 @@ __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N
             Yn = chain_step_f32_with<N>(a, Y, [&](int k) {
                 if (k == 0 && t + 1 < len) operand_write<N>(ring[pn], tb);
                 if (k == 1 && t + 1 < len) {
-                    __syncthreads();
+                    wave_lds_sync();
                     operand_read_f32<N>(o, tb);
                 }
                 if (k == 2 && t > 0) store_prefix_f32<N, SC>(P, pexp, base + t - 1, Y, ex);
@@ -835,9 +835,9 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
         if (len > 1) {
             float* x1 = xlds + xslot<N, FX>();
             xop_stage<N>(buf[1], x1);
-            __syncthreads();
+            wave_lds_sync();
             xop_factors<N>(x1);
-            __syncthreads();
+            wave_lds_sync();
         }
     }
     // expanded at compile time (an index sequence, not the loop unroller: with
@@ -871,12 +871,12 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
                         const bool next2 = t + 2 < len;
                         if (k == 1 && next2) xop_stage<N>(buf[t + 2], x2);
                         if (k == 2 && next2) {
-                            __syncthreads();
+                            wave_lds_sync();
                             xop_factors<N>(x2);
                         }
                     }
                     if (k == 3) {
-                        __syncthreads();
+                        wave_lds_sync();
                         if constexpr (t > 0) prefix_read<N>(buf[t - 1], pl);
                     }
                 } else {
@@ -885,7 +885,7 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
                     if constexpr (t + 1 < KR)
                         if (k == 0 && next) operand_write<N>(buf[t + 1], tb);
                     if (k == 1) {
-                        __syncthreads();
+                        wave_lds_sync();
                         if constexpr (t + 1 < KR) {
                             if (next) {
                                 float o[NA];
@@ -907,9 +907,9 @@ __device__ __attribute__((always_inline)) void fwd_pass_retain(typename Mf<N>::v
             if (t + 1 == len) {
                 // the chunk's last prefix: transposed right away
                 float* pn = plds + ((t + 1) & 1) * PB;
-                __syncthreads();
+                wave_lds_sync();
                 prefix_write<N>(X, pn);
-                __syncthreads();
+                wave_lds_sync();
                 prefix_read<N>(buf[t], pn);
             }
         }
@@ -946,7 +946,7 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
     constexpr int NT = Mf<N>::NT;
     constexpr int NN = N * N;
     static_assert(KR % 2 == 0, "tokens in pairs");
-    if constexpr (SC) __syncthreads();  // the prefixes' exponents in exl
+    if constexpr (SC) wave_lds_sync();  // the prefixes' exponents in exl
     // the carry, scaled and rounded once: B entries cb[K][J][b]
     int s = kNoExp;
 #pragma unroll
@@ -1165,7 +1165,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
         } else {
             pre = init_acc<N, SC>(ex, cy, seq);
         }
-        __syncthreads();
+        wave_lds_sync();
         load_a_transposed<N, acc_t>(a, xl);
         X = chain_step<N>(a, pre, vzero<N>());
         if constexpr (SC) {
@@ -1214,11 +1214,11 @@ __device__ inline void x_operand_direct(typename Mf<N>::aop_t& a, const float* x
         const float4 w = reinterpret_cast<const float4*>(xt)[q * 64 + l];
         v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
     }
-    __syncthreads();
+    wave_lds_sync();
     xop_stage<N>(v, xs);
-    __syncthreads();
+    wave_lds_sync();
     xop_factors<N>(xs);
-    __syncthreads();
+    wave_lds_sync();
     xop_read_direct<N>(o, xs);
     operand_from<N>(a, o);
 }
@@ -1344,9 +1344,9 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
             // x_t: stage, factors, and M_t's operand for the next step
             float o[NA];
             xop_stage<N>(rm[p], xsl);
-            __syncthreads();
+            wave_lds_sync();
             xop_factors<N>(xsl);
-            __syncthreads();
+            wave_lds_sync();
             xop_read_direct<N>(o, xsl);
             operand_from<N>(a_next, o);
         } else {
@@ -1383,7 +1383,7 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
             vec_t D;
             if (pos >= lo_p || cy.carry) {
                 // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
-                __syncthreads();
+                wave_lds_sync();
 #pragma unroll
                 for (int I = 0; I < NT; ++I)
 #pragma unroll
@@ -1391,7 +1391,7 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             tr[(16 * I + trow(l, r)) * TS + 16 * J + c] = G.t[I][J][r];
-                __syncthreads();
+                wave_lds_sync();
                 typename F::aop_t ag;
 #pragma unroll
                 for (int I = 0; I < NT; ++I)
@@ -1418,9 +1418,9 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
                         *reinterpret_cast<f4v*>(gs + (16 * J + tcol(l)) * LS + 16 * I + trow(l, 0)) =
                             f4v{float(x[0]), float(x[1]), float(x[2]), float(x[3])};
                     }
-                __syncthreads();
+                wave_lds_sync();
                 build_vjp_token<N>(xsl, gs, xsl + StageX<N>::EF, part, ds);
-                __syncthreads();
+                wave_lds_sync();
                 store_rows_from_lds<N>(out, ds);
             } else {
                 store_acc_rows<N, float>(out, D);
@@ -1554,7 +1554,7 @@ void bwd_mfma_kernel(const float* __restrict__ M,
         store_acc_rows<N, acc_t>(xl, WC);  // rows of WC^T
         wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
         fence_acquire();
-        __syncthreads();
+        wave_lds_sync();
         load_a_transposed<N, acc_t>(a, xl);  // A entries of WC
         G = chain_step<N>(a, ws_load_acc_rows<N>(sinc + (first - 1) * NN), G);
     }
