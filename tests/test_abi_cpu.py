@@ -217,7 +217,7 @@ def _signature(name):
     return [re.sub(r"\s+", " ", p) for p in params]
 
 
-def test_survey_boundary_signatures():
+def test_boundary_signatures():
     """The three scan calls of the boundary take exactly (pointers..., B, H, T,
     n, ws, ws_bytes, stream) and (B, H, T, n, direction): no chunk argument."""
     assert _signature("mru_scan_fwd") == [
@@ -233,7 +233,7 @@ def test_survey_boundary_signatures():
         "void* stream"]
 
 
-def test_survey_boundary_calls(mpp):
+def test_boundary_calls(mpp):
     """Each boundary signature called through ctypes with its own argument list:
     validation answers before any launch, the workspace query matches the plan."""
     lib = mpp.load_library()
