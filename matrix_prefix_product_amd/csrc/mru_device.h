@@ -162,6 +162,16 @@ __device__ inline void wait_range_nonempty(const uint32_t* flags, int64_t lo, in
 }
 
 // frexp exponent: a finite nonzero v with exponent e has 2^(e-1) <= |v| < 2^e.
+// Orders a one-wave workgroup's LDS staging: the scan kernels run one wave per
+// workgroup, and a wave's LDS instructions execute in issue order, so the
+// writes of one staging step are seen by the reads that follow without waiting
+// for them to complete (a workgroup barrier waits: s_waitcnt lgkmcnt(0)).  The
+// wavefront-scope fence keeps the compiler from moving LDS accesses across it.
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // max_exp folds the exponent of a nonzero v into a running maximum that starts
 // at kNoExp (so an all-zero set keeps kNoExp).
 __device__ inline int frexp_exp(float v) { return __builtin_amdgcn_frexp_expf(v); }

@@ -19,19 +19,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include "mru_device.h"
+
 namespace mru {
 
 typedef double d4 __attribute__((ext_vector_type(4)));
 
-// Orders a one-wave workgroup's LDS staging: the kernels using it run one wave
-// per workgroup, and a wave's LDS instructions execute in issue order, so the
-// writes of one staging step are seen by the reads that follow without waiting
-// for them to complete (a workgroup barrier waits: s_waitcnt lgkmcnt(0)).  The
-// wavefront-scope fence keeps the compiler from moving LDS accesses across it.
-__device__ inline void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
 
 // Lane geometry of one 16x16 tile (actual indices).
 __device__ inline int tcol(int l) { return l & 15; }                     // column of X held

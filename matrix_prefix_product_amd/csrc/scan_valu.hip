@@ -433,13 +433,13 @@ __device__ __attribute__((always_inline)) void fwd_sweep(
     // staged loads without waiting for the previous block's stores.
     auto block = [&](int blk, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        __syncthreads();
+        wave_lds_sync();
         stage_store<N, R, TB>(lds, reg);
-        __syncthreads();
+        wave_lds_sync();
         if (FULL || blk + TB < maxlen) stage_load<N, R, TB, false>(reg, M, info, blk + TB, 0, T);
         if constexpr (FX) {
             stage_e<N, R, TB>(lds);
-            __syncthreads();
+            wave_lds_sync();
         }
 #pragma unroll
         for (int tau = 0; tau < TB; ++tau) {
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch / V::G, V::G)
               : int64_t(blockIdx.x) * V::G;
     if (lane < V::G) info[lane] = make_chain(cbase + lane, nchunks, nch, K, T, false);
-    __syncthreads();
+    wave_lds_sync();
     int maxlen = 0;
 #pragma unroll
     for (int i = 0; i < V::G; ++i) maxlen = max(maxlen, info[i].len);
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
     // the wave's own aggregates also go to LDS, for its later chains
-    __syncthreads();
+    wave_lds_sync();
     store_rows<N, R>(lds + g * V::CH_STRIDE + li * R * N, st);
     if (SC && li == 0) aex[g] = a_ex;
 
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
                 }
             }
     }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < V::G - 1; ++j)
         if (j < g) {
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
                 renorm_rows<N, R>(lrow, l_ex);
             }
         }
-    __syncthreads();  // the LDS is the staging buffer again in step 4
+    wave_lds_sync();  // the LDS is the staging buffer again in step 4
 
     // 3. carry = (prefix of the previous super, or the carried-in state) * lrow
     if (later_super || cy.carry) {  // wave-uniform
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(64) void fwd_valu_kernel(const float* __restrict__ 
             wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
             fence_acquire();
         }
-        __syncthreads();
+        wave_lds_sync();
         load_matrix<N>(m, xch + g * V::QX_STRIDE);
         if (later_super) {
             ws_load_rows<N, R>(st, incl + (first - 1) * V::NN + li * R * N);
@@ -766,12 +766,12 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
         store_rows<N, R>(nxg + li * R * N, t);
         if constexpr (FX) {
             // its e on the diagonal, as stage_e does for staged tokens
-            __syncthreads();
+            wave_lds_sync();
             const float mean = ldu_mean<N>(nxg);
             float e[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) e[r] = expf(nxg[(li * R + r) * (N + 1)] - mean);
-            __syncthreads();
+            wave_lds_sync();
 #pragma unroll
             for (int r = 0; r < R; ++r) nxg[(li * R + r) * (N + 1)] = e[r];
         }
@@ -783,7 +783,7 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
     // without waiting for the previous block's dM stores.
     auto block = [&](int blk, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        __syncthreads();
+        wave_lds_sync();
         stage_store<N, R, TB>(lds, rm);
         stage_store<N, R, TB>(lds + V::G * V::CH_STRIDE, rr);
         float cur[NCK][R][N];
@@ -796,11 +796,11 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
                     for (int j = 0; j < N; ++j)
                         cur[u][r][j] = ck_id[u] ? (li * R + r == j ? 1.f : 0.f) : ck[u][r][j];
         }
-        __syncthreads();
+        wave_lds_sync();
         if (FULL || blk + TB < maxlen) load_block(blk + TB);
         if constexpr (FX) {
             stage_e<N, R, TB>(lds);
-            __syncthreads();
+            wave_lds_sync();
         }
         // rp[tau]: the lane's rows of P_{t-1} for the block's token tau, from the
         // block's lowest live token (tau = min(TB-1, hi)) upward
@@ -887,13 +887,13 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
                 }
                 // exchange the rows of Q_t and P_{t-1} within the chain, then
                 // dM rows a = own rows: dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
-                __syncthreads();
+                wave_lds_sync();
                 if (live) {
                     store_rows<N, R>(qxg + li * R * N, q);
                     store_rows<N, R>(pxg + li * R * N, rp[tau]);
                     if constexpr (DX) store_rows<N, R>(lxg + li * R * N, pl);
                 }
-                __syncthreads();
+                wave_lds_sync();
                 if (live) {
                     float d[R][N], u[DX ? R : 1][N];
                     if (DX || FULL || tseq > 0 || cy.carry) {
@@ -1007,7 +1007,7 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch / V::G, V::G)
               : int64_t(blockIdx.x) * V::G;
     if (lane < V::G) info[lane] = make_chain(cbase + lane, nchunks, nch, K, T, true);
-    __syncthreads();
+    wave_lds_sync();
     int maxlen = 0;
 #pragma unroll
     for (int i = 0; i < V::G; ++i) maxlen = max(maxlen, info[i].len);
@@ -1040,7 +1040,7 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
     fence_release();
     if (li == 0) store_flag(&flags[c], kFlagAgg);
     // the wave's own maps also go to LDS (W^T, then Bl), for its later chains
-    __syncthreads();
+    wave_lds_sync();
     store_rows<N, R>(lds + g * V::CH_STRIDE + li * R * N, w);
     store_rows<N, R>(lds + g * V::CH_STRIDE + V::NN + li * R * N, q);
 
@@ -1073,7 +1073,7 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
                     for (int q = 0; q < N; ++q) bc[r][q] += bb[d][r][q];
             }
     }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < V::G - 1; ++j)
         if (j < g) {
@@ -1087,14 +1087,14 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
 #pragma unroll
                 for (int q = 0; q < N; ++q) bc[r][q] += bj[r][q];
         }
-    __syncthreads();  // the LDS is the staging buffer again in step 4
+    wave_lds_sync();  // the LDS is the staging buffer again in step 4
 
     // 3. carry = Y Wc^T + Bc with Y the adjoint published by the previous super
     if (later_super) {
         wait_flag_eq(&flags[first - 1], kFlagPrefix, hdr);
         fence_acquire();
         store_rows<N, R>(qx + g * V::QX_STRIDE + li * R * N, wc);
-        __syncthreads();
+        wave_lds_sync();
         load_matrix<N>(m, qx + g * V::QX_STRIDE);
         ws_load_rows<N, R>(q, sinc + (first - 1) * V::NN + li * R * N);
         rows_times<N, R>(q, m);
@@ -1102,7 +1102,7 @@ void bwd_valu_kernel(const float* __restrict__ M, const float* __restrict__ P,
         for (int a = 0; a < R; ++a)
 #pragma unroll
             for (int b = 0; b < N; ++b) q[a][b] += bc[a][b];
-        __syncthreads();
+        wave_lds_sync();
     } else {
 #pragma unroll
         for (int a = 0; a < R; ++a)
