@@ -388,10 +388,17 @@ __device__ inline void store_prefix(float* __restrict__ P, int32_t* __restrict__
 // the token PF further on, address clamped into the chunk) as soon as its
 // pieces have been turned into operands.  The main loop runs whole blocks of PF
 // tokens so every ring slot stays in fixed registers.
-template <int N, int PF, bool WRITE, bool FX, bool SC>
+// STASH (the aggregate pass from raw token vectors): each token's operand
+// entries, once formed, are also written to the token's own slot of P in the
+// layout the fp32 apply pass reads (stash_operands), which overwrites them.
+template <int N>
+__device__ inline void stash_operands(float* __restrict__ slot, const float (&o)[4 * Stage<N>::NV]);
+
+template <int N, int PF, bool WRITE, bool FX, bool SC, bool STASH = false>
 __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& X, int& ex, const float* __restrict__ M,
                           float* __restrict__ P, int32_t* __restrict__ pexp, int64_t base, int len,
                           float* tlds, float* xlds) {
+    static_assert(!STASH || (FX && !WRITE), "the stash is the aggregate pass's, from raw token vectors");
     using F = Mf<N>;
     using vec_t = typename F::vec_t;
     constexpr int NN = F::NN;
@@ -409,6 +416,7 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
         // The ring then holds tokens t+2 .. t+1+PF at the start of step t.
         static_assert(PF >= 3, "two tokens ahead of the chain");
         to_operand_x<N>(o, ring[0], xlds);
+        if constexpr (STASH) stash_operands<N>(P + base * NN, o);
         if (len > 1) {
             float* x1 = xlds + xslot<N, FX>();
             xop_stage<N>(ring[1], x1);
@@ -431,7 +439,10 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
             float* x1 = xlds + ((t + 1) & 1) * xslot<N, FX>();
             float* x2 = xlds + (t & 1) * xslot<N, FX>();  // token t + 2's slot
             Xn = chain_step_with<N>(a, X, vzero<N>(), [&](int k) {
-                if (k == 0 && t + 1 < len) xop_read<N>(o, x1);
+                if (k == 0 && t + 1 < len) {
+                    xop_read<N>(o, x1);
+                    if constexpr (STASH) stash_operands<N>(P + (base + t + 1) * NN, o);
+                }
                 if (k == 1 && t + 2 < len) xop_stage<N>(ring[p2], x2);
                 if (k == 2) {
                     if (WRITE && t > 0) store_prefix<N, SC>(P, pexp, base + t - 1, X, ex);
@@ -486,11 +497,12 @@ __device__ __attribute__((always_inline)) void fwd_sweep(typename Mf<N>::vec_t& 
 // the step consumes is found (while the step's products run) and, if its
 // exponent has left [-60, 60], the step's result is rescaled by that power of
 // two (exact).  Each P_t is stored as 2^ex Y (IEEE overflow to inf where P_t
-// leaves the fp32 range, as the fp64 pass stores it).  If the state ever holds
-// an inf, a NaN or only subnormal values the pass gives up (returns false) and
-// the caller re-runs the chunk with the fp64 pass, which overwrites every P_t
-// of the chunk.  The scaled scans (SC) renormalise exactly after every step,
-// as the fp64 pass does.
+// leaves the fp32 range, as the fp64 pass stores it).  If a checked state, or
+// the chunk's final one, holds an inf or a NaN (once there, products keep one
+// in the state), or a checked state holds only subnormal values, the pass gives
+// up (returns false) and the caller re-runs the chunk with the fp64 pass, which
+// overwrites every P_t of the chunk.  The scaled scans (SC) renormalise
+// exactly after every step, as the fp64 pass does.
 // Layouts: the fp32 accumulator tile holds the same entries per lane and
 // register as the fp64 one (Y[16I + trow(l, r)][16J + tcol(l)], Y = P^T),
 // with the natural row order instead of pi, so the A-operand entries of M_t^T
@@ -507,6 +519,33 @@ struct Mf32 {
         f4v32 t[NT][NT];
     };
 };
+
+// Stash layout of one token (n*n floats, the token's slot of P): lane l of the
+// fp32 pass reads its 4 * NV operand entries M[16K + trow(l, b)][16I + tcol(l)]
+// as NV 16-byte pieces at float offset 4 * NV * l.  The aggregate pass's lane l
+// holds M[16K + trow(l, b)][16I + tacol(l)] (pi-ordered columns), i.e. the
+// entries of fp32 lane (l & 48) | tacol(l), and writes them there.
+template <int N>
+__device__ inline void stash_operands(float* __restrict__ slot, const float (&o)[4 * Stage<N>::NV]) {
+    constexpr int NA = 4 * Stage<N>::NV;
+    const int l = threadIdx.x & 63;
+    float* q = slot + NA * ((l & 48) | tacol(l));
+#pragma unroll
+    for (int e = 0; e < NA; e += 4)
+        *reinterpret_cast<f4v32*>(q + e) = f4v32{o[e], o[e + 1], o[e + 2], o[e + 3]};
+}
+
+template <int N>
+__device__ inline void load_stash(float (&o)[4 * Stage<N>::NV], const float* __restrict__ slot) {
+    constexpr int NA = 4 * Stage<N>::NV;
+    const int l = threadIdx.x & 63;
+    const float* q = slot + NA * l;
+#pragma unroll
+    for (int e = 0; e < NA; e += 4) {
+        const f4v32 v = *reinterpret_cast<const f4v32*>(q + e);
+        o[e] = v[0]; o[e + 1] = v[1]; o[e + 2] = v[2]; o[e + 3] = v[3];
+    }
+}
 
 template <int N>
 __device__ inline void operand_read_f32(float (&o)[4 * Stage<N>::NV], const float* tb) {
@@ -627,8 +666,10 @@ __device__ inline void store_prefix_f32(float* __restrict__ P, int32_t* __restri
 }
 
 // The apply pass in fp32 from the fp64 carry X (SC: normalised, exponent ex);
-// false if it gave up (see above).
-template <int N, int PF, bool FX, bool SC>
+// false if it gave up (see above).  STASHED (from raw token vectors): the
+// aggregate pass left every token's operand entries in its slot of P
+// (stash_operands), so the pass reads them there instead of forming them again.
+template <int N, int PF, bool FX, bool SC, bool STASHED = false>
 __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N>::vec_t& X, int ex,
                                                              const float* __restrict__ M, float* __restrict__ P,
                                                              int32_t* __restrict__ pexp, int64_t base, int len,
@@ -656,12 +697,21 @@ __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N
             for (int r = 0; r < 4; ++r) Y.t[I][J][r] = float(ldexp(X.t[I][J][r], -e0));
     ex += e0;
     bool ok = true;
+    static_assert(!STASHED || FX, "the stash holds operands formed from raw token vectors");
     const float* Mb = M + base * NN;
+    const float* Sb = P + base * NN;  // STASHED: the operand slots
     float ring[PF][NA];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) load_token<N>(ring[p], Mb + int64_t(min(p, len - 1)) * NN);
+    for (int p = 0; p < PF; ++p) {
+        if constexpr (STASHED) load_stash<N>(ring[p], Sb + int64_t(min(p, len - 1)) * NN);
+        else load_token<N>(ring[p], Mb + int64_t(min(p, len - 1)) * NN);
+    }
     float o[NA];
-    if constexpr (FX) {
+    if constexpr (STASHED) {
+#pragma unroll
+        for (int e = 0; e < NA; ++e) o[e] = ring[0][e];
+        load_stash<N>(ring[0], Sb + int64_t(min(PF, len - 1)) * NN);
+    } else if constexpr (FX) {
         static_assert(PF >= 3, "two tokens ahead of the chain");
         xop_stage<N>(ring[0], xlds);
         wave_lds_sync();
@@ -689,7 +739,21 @@ __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N
         for (int e = 0; e < NA; ++e) a[e] = o[e];
         vec_t Yn;
         uint32_t kprev = 0;  // the consumed state's largest |entry| (checked steps)
-        if constexpr (FX) {
+        if constexpr (STASHED) {
+            // token t+1's entries from the ring, token t+1+PF's loaded into its slot
+            // (never one of the slots already overwritten by a prefix)
+            const int pn = (p + 1) % PF;
+            Yn = chain_step_f32_with<N>(a, Y, [&](int k) {
+                if (k == 0 && t + 1 < len) {
+#pragma unroll
+                    for (int e = 0; e < NA; ++e) o[e] = ring[pn][e];
+                }
+                if (k == 2 && t > 0) store_prefix_f32<N, SC>(P, pexp, base + t - 1, Y, ex);
+                if (k == 3 && t + 1 < len && refill)
+                    load_stash<N>(ring[pn], Sb + int64_t(min(t + 1 + PF, len - 1)) * NN);
+                if (k == 8 && !SC && (t & 3) == 3) kprev = f32_key<N>(Y);
+            });
+        } else if constexpr (FX) {
             const int p2 = (p + 2) % PF;
             float* x1 = xlds + ((t + 1) & 1) * xslot<N, FX>();
             float* x2 = xlds + (t & 1) * xslot<N, FX>();
@@ -749,6 +813,9 @@ __device__ __attribute__((always_inline)) bool fwd_sweep_f32(const typename Mf<N
     for (int p = 0; p < PF; ++p)
         if (t0 + p < len) step(p, t0 + p, false);
     if (!ok) return false;
+    // an inf or NaN that arose after the last checked step is still in the final
+    // state (a product never turns one back into a finite value)
+    if (f32_key<N>(Y) >= 0x7f800000u) return false;
     store_prefix_f32<N, SC>(P, pexp, base + len - 1, Y, ex);
     return true;
 }
@@ -1110,8 +1177,10 @@ void fwd_mfma_kernel(const float* __restrict__ M,
 
     // 1. chunk aggregate (scaled scans: 2^a_ex times the normalised matrix)
     vec_t X = videntity<N>(l);
-    // n = 32: the apply pass runs in fp32 (fwd_sweep_f32)
+    // n = 32: the apply pass runs in fp32 (fwd_sweep_f32); from raw token vectors
+    // it reads the token matrices the aggregate pass formed and left in P's slots
     constexpr bool kF32Apply = N == 32 && KR == 0;
+    constexpr bool kStash = kF32Apply && FX;
     float buf[KR > 0 ? KR : 1][Mf<N>::NT * Mf<N>::NT * 4];
     if constexpr (KR > 0) {
         constexpr int PFR = N == 16 ? kPfRetain16 : PF;
@@ -1120,7 +1189,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
         else
             fwd_pass_retain<N, KR, PFR, FX, SC, false>(X, ex, M, ch.base, ch.len, buf, tlds, xlds, plds, exl);
     } else {
-        fwd_sweep<N, PF, false, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
+        fwd_sweep<N, PF, false, FX, SC, kStash>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
     }
     const int a_ex = ex;
     ws_store_acc_rows<N>(agg + c * NN, X);
@@ -1193,7 +1262,7 @@ void fwd_mfma_kernel(const float* __restrict__ M,
         bool done = false;
         if constexpr (kF32Apply)
             if (ch.len <= kF32ChainMax)
-                done = fwd_sweep_f32<N, PF, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
+                done = fwd_sweep_f32<N, PF, FX, SC, kStash>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
         if (!done)
             fwd_sweep<N, PF, true, FX, SC>(X, ex, M, P, cy.out_exp, ch.base, ch.len, tlds, xlds);
     }

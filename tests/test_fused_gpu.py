@@ -379,3 +379,32 @@ def test_fused_fwd_n16_zero_input_is_identity(mpp, n):
     for chunk in (0, 7, 100):
         P = host(mpp.scan_fwd_x(xd, n, chunk))
         assert np.array_equal(P, np.broadcast_to(np.eye(n, dtype=np.float32), P.shape))
+
+
+@pytest.mark.parametrize("chunk", [8, 5])
+def test_n32_fp32_apply_falls_back_past_the_range(mpp, chunk):
+    """M_t = diag(2^40, 2^-40, 1, ...): within four steps the fp32 apply chain
+    overflows and its chunks are redone by the fp64 pass. Every prefix is an
+    exact power of two (inf / 0 once it leaves fp32; 24 tokens keep the fp64
+    state finite), from M and, bitwise the same as build then scan, from raw
+    token vectors."""
+    n, B, H, T = 32, 2, 1, 24
+    d = np.ones(n)
+    d[0], d[1] = 2.0 ** 40, 2.0 ** -40
+    M = np.broadcast_to(np.diag(d).astype(np.float32), (B, H, T, n, n)).copy()
+    P = host(mpp.scan_fwd(dev(M), chunk))
+    t1 = np.arange(1, T + 1, dtype=np.float64)
+    with np.errstate(over="ignore", under="ignore"):
+        want = np.broadcast_to(np.eye(n, dtype=np.float32), (B, H, T, n, n)).copy()
+        want[..., 0, 0] = (2.0 ** (40 * t1)).astype(np.float32)  # inf from t = 4 on
+        want[..., 1, 1] = (2.0 ** (-40 * t1)).astype(np.float32)  # 0 from t = 4 on
+    assert np.array_equal(P, want)
+    # the same from raw token vectors: X_00 = -X_11 = 40 ln 2, the rest 0
+    x = np.zeros((B, H, T, n, n), dtype=np.float32)
+    x[..., 0, 0], x[..., 1, 1] = 40 * np.log(2.0), -40 * np.log(2.0)
+    xd = dev(x.reshape(B, H, T, n * n))
+    Px = mpp.scan_fwd_x(xd, n, chunk)
+    Pm = mpp.scan_fwd(mpp.build_inputs(xd, n), chunk)
+    assert torch.equal(Px.view(torch.int32), Pm.view(torch.int32))
+    Px = host(Px)
+    assert np.isinf(Px[:, :, 3:, 0, 0]).all() and (Px[:, :, 3:, 1, 1] == 0).all()
