@@ -206,12 +206,12 @@ def test_carry_without_tokens_writes_nothing(mpp):
     assert torch.count_nonzero(dC) == 0
 
 
-def test_c4_scaled_full_length(mpp):
+@pytest.mark.parametrize("h", [0, 7])
+def test_c4_scaled_full_length(mpp, h):
     # n = 32 at full length: 64K tokens reach |P| ~ e^389, far beyond fp32; the
     # scaled scan is graded against the fp64 oracle at every token, including
-    # the 1K / 8K / 64K tracking points
+    # the 1K / 8K / 64K tracking points (the first and the last head)
     w = WORKLOADS["c4"]
-    h = 0
     x = gen_x(w.B, w.H, w.T, w.n, w.sigma_off, w.sigma_diag, w.seed, b_idx=[0], h_idx=[h])
     M32 = build_ref(x, w.n).astype(np.float32)
     Pm, E = mpp.scan_fwd_ex(dev(M32), scaled=True)

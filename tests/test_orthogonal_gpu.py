@@ -80,7 +80,7 @@ def test_orthogonal_scan_full_length(mpp, method):
         assert abs(nrm - np.sqrt(w.n)) <= 1e-3
 
 
-@pytest.mark.parametrize("n", [4, 8, 16])
+@pytest.mark.parametrize("n", [4, 8, 16, 32])
 def test_orthogonal_scan_and_backward_small(mpp, n):
     from gpu_helpers import BWD_TOL
     from oracle import bwd_ref

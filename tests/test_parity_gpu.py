@@ -206,12 +206,20 @@ def test_fwd_edge_shapes(mpp):
 
 
 def test_flatten_is_row_major_view(mpp):
+    from oracle import flatten_ref
     M32 = _M(1, 2, 10, 8, seed=4)
     P = mpp.scan_fwd(dev(M32))
     v = mpp.flatten(P)
     assert v.shape == (1, 2, 10, 64) and v.data_ptr() == P.data_ptr()
-    Ph = host(P)
-    assert np.array_equal(host(v), Ph.reshape(1, 2, 10, 64))
+    Ph, vh = host(P), host(v)
+    # entry (i, j) of P_t is component i*n + j of the vector, by definition
+    for i, j in ((0, 0), (0, 7), (3, 5), (7, 0), (7, 7)):
+        assert np.array_equal(vh[..., i * 8 + j], Ph[..., i, j])
+    # and the vectors are the oracle's flattened prefixes
+    ref = flatten_ref(scan_ref(M32.astype(np.float64)))
+    assert ref.shape == vh.shape
+    err = np.linalg.norm(vh - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert err.max() <= FWD_TOL
 
 
 # ----------------------------------------------------------------------------- backward
