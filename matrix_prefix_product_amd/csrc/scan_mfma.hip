@@ -1406,7 +1406,8 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
         const int pos = len - 1 - i;
         const bool has_next = pos < hi_m;
         typename F::aop_t a;
-        vec_t cr, bv;
+        vec_t cr;
+        float bp[NT][NT][4];  // GRAD: B entries of P_{t-1}, fp32 as read
         float* xsl = xs + (i & 1) * xslot<N, FX>();  // FX: this step's token slot
         if constexpr (FX) {
             a = a_next;
@@ -1426,7 +1427,7 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
         for (int e = 0; e < NA; ++e) cr.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rr[p][e]);
         if constexpr (GRAD) {
 #pragma unroll
-            for (int e = 0; e < NA; ++e) bv.t[e / (4 * NT)][(e / 4) % NT][e % 4] = double(rp[p][e]);
+            for (int e = 0; e < NA; ++e) bp[e / (4 * NT)][(e / 4) % NT][e % 4] = rp[p][e];
         }
         if (refill) fetch(p, i + PF);
         if (has_next) {
@@ -1447,11 +1448,16 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
                     for (int J = 0; J < NT; ++J)
 #pragma unroll
                         for (int b = 0; b < 4; ++b)
-                            bv.t[K][J][b] = double(cs[(16 * K + trow(l, b)) * N + 16 * J + c]);
+                            bp[K][J][b] = cs[(16 * K + trow(l, b)) * N + 16 * J + c];
             }
-            vec_t D;
+            // dM_t^T = G_t P_{t-1} on the fp32 matrix cores, from G_t rounded to
+            // fp32 once: its error stays in dM_t (the recurrence runs on in fp64)
+            f4v32 D[NT][NT];
             if (pos >= lo_p || cy.carry) {
-                // transpose G through LDS: A entries of G are G[16I + acol][16K + trow(l, b)]
+                // transpose G through LDS: A entries of G are G[16I + tcol][16K + trow(l, b)]
+                // (natural row order: the fp32 accumulator keeps rows 4(l/16) .. +3 in lane l)
+                // (row stride n + 4 floats: conflict-free writes, 16-byte reads)
+                float* trf = reinterpret_cast<float*>(tr);
                 wave_lds_sync();
 #pragma unroll
                 for (int I = 0; I < NT; ++I)
@@ -1459,19 +1465,37 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
                     for (int J = 0; J < NT; ++J)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            tr[(16 * I + trow(l, r)) * TS + 16 * J + c] = G.t[I][J][r];
+                            trf[(16 * I + trow(l, r)) * LS + 16 * J + c] = float(G.t[I][J][r]);
                 wave_lds_sync();
-                typename F::aop_t ag;
+                float ag[NT][NT][4];
 #pragma unroll
                 for (int I = 0; I < NT; ++I)
 #pragma unroll
-                    for (int K = 0; K < NT; ++K)
+                    for (int K = 0; K < NT; ++K) {
+                        const f4v32 v = *reinterpret_cast<const f4v32*>(trf + (16 * I + c) * LS + 16 * K + trow(l, 0));
 #pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            ag.v[I][K][b] = tr[(16 * I + ac) * TS + 16 * K + trow(l, b)];
-                D = chain_step<N>(ag, bv, vzero<N>());
+                        for (int b = 0; b < 4; ++b) ag[I][K][b] = v[b];
+                    }
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J) {
+                        f4v32 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int K = 0; K < NT; ++K)
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[I][K][b], bp[K][J][b], acc, 0, 0, 0);
+                        D[I][J] = acc;
+                    }
             } else {
-                D = G;  // t = 0: P_{-1} = I
+                // t = 0: P_{-1} = I
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) D[I][J][r] = float(G.t[I][J][r]);
             }
             if constexpr (DX) {
                 // dM_t (fp32, row-major) into gs, then the build's gradient
@@ -1482,17 +1506,18 @@ __device__ __attribute__((always_inline)) void bwd_sweep(typename Mf<N>::vec_t& 
 #pragma unroll
                 for (int I = 0; I < NT; ++I)
 #pragma unroll
-                    for (int J = 0; J < NT; ++J) {
-                        const d4 x = D.t[I][J];
-                        *reinterpret_cast<f4v*>(gs + (16 * J + tcol(l)) * LS + 16 * I + trow(l, 0)) =
-                            f4v{float(x[0]), float(x[1]), float(x[2]), float(x[3])};
-                    }
+                    for (int J = 0; J < NT; ++J)
+                        *reinterpret_cast<f4v*>(gs + (16 * J + tcol(l)) * LS + 16 * I + trow(l, 0)) = D[I][J];
                 wave_lds_sync();
                 build_vjp_token<N>(xsl, gs, xsl + StageX<N>::EF, part, ds);
                 wave_lds_sync();
                 store_rows_from_lds<N>(out, ds);
             } else {
-                store_acc_rows<N, float>(out, D);
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J)
+                        *reinterpret_cast<f4v32*>(out + (16 * J + tcol(l)) * N + 16 * I + trow(l, 0)) = D[I][J];
             }
             if (pos < lo_p && cy.dcarry) {
                 // dL/dP_{-1} = Q_0 M_0^T, i.e. its transpose is M_0 G_0
@@ -1549,7 +1574,7 @@ void bwd_mfma_kernel(const float* __restrict__ M,
     using acc_t = typename F::acc_t;
     using vec_t = typename F::vec_t;
     constexpr int NN = N * N;
-    __shared__ double tr[N * (N + 1)];
+    __shared__ __align__(16) double tr[N * (N + 1)];  // also the fp32 transpose (row stride n + 4)
     __shared__ double xl[NN];
     __shared__ __align__(16) float xs[FX ? 2 * StageX<N>::SLOT : 4];  // FX: token slots
     __shared__ __align__(16) float dxl[DX ? 2 * N * (N + 4) + 4 : 4];  // DX: gradient staging
