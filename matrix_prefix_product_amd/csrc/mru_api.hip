@@ -69,10 +69,11 @@ int64_t auto_chunk_len(int64_t S, int64_t T, int n, int dir, bool from_x = false
     } else {
         // one wave per chain, one wave per SIMD (1024 SIMDs on MI355X).  Chains
         // wanted (measured, C3-C5 shapes): n = 32 runs best with one round of
-        // waves (its chunks are long enough to hide the look-back), the n = 16
-        // backward with four, the n = 16 forward with two (then capped by the
-        // register buffer below).
-        target = n == 32 ? 1024 : (dir == 1 ? 4096 : 2048);
+        // waves (its chunks are long enough to hide the look-back; the forward
+        // from raw token vectors runs two waves per SIMD, so two chains per
+        // SIMD), the n = 16 backward with four, the n = 16 forward with two
+        // (then capped by the register buffer below).
+        target = n == 32 ? (from_x && dir == MRU_DIR_FWD ? 2048 : 1024) : (dir == 1 ? 4096 : 2048);
         if (S >= target) return T;
     }
     const int64_t nch = (target + S - 1) / S;

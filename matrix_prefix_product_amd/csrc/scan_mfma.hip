@@ -1127,14 +1127,15 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
 
 // One wave per SIMD: the forward keeps a chunk's operands (n = 16) or a deep
 // operand ring (n = 32) in the whole register file.  The 32-token retained
-// chunks run two waves per SIMD: a wave's own vector-ALU instructions do not
-// overlap its matrix-core products (measured: each adds its issue time to the
-// product chain), another wave's do.
-template <int KR>
-constexpr int fwd_waves() { return KR == 32 ? 2 : 1; }
+// chunks and the n = 32 forward from raw token vectors (unscaled) run two waves
+// per SIMD: a wave's own vector-ALU instructions do not overlap its matrix-core
+// products (measured: each adds its issue time to the product chain), another
+// wave's do, and forming each token's matrix on chip is vector-ALU work.
+template <int N, int KR, bool FX, bool SC>
+constexpr int fwd_waves() { return KR == 32 || (N == 32 && FX && !SC) ? 2 : 1; }
 
 template <int N, int PF, int KR, bool FX, bool SC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fwd_waves<KR>(), fwd_waves<KR>())))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fwd_waves<N, KR, FX, SC>(), fwd_waves<N, KR, FX, SC>())))
 void fwd_mfma_kernel(const float* __restrict__ M,
                                                       float* __restrict__ P, int64_t S, int64_t T,
                                                       int64_t K, int64_t nch, int64_t Z,
