@@ -140,9 +140,10 @@ mru_status mru_build_inputs_bwd(const float* x, const float* dM, float* dx, int6
 /*
  * Chunk length (tokens per scan chunk) of the automatic plan for this shape
  * and direction (MRU_DIR_FWD, MRU_DIR_BWD, or MRU_DIR_FWD_X for the forward
- * from raw token vectors, which at n = 16 plans 32-token chunks where the scan
- * from M takes up to 64: it runs two waves per SIMD); a pure function of its
- * arguments.  Returns 0 for an invalid shape.
+ * from raw token vectors, which at n = 16 plans 24-token chunks where the scan
+ * from M takes up to 64, and at n = 32 twice the chunks: it runs three / two
+ * waves per SIMD); a pure function of its arguments.  Returns 0 for an invalid
+ * shape.
  */
 int32_t mru_scan_chunk(int64_t B, int64_t H, int64_t T, int32_t n, int32_t direction);
 

@@ -1126,13 +1126,16 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
 }
 
 // One wave per SIMD: the forward keeps a chunk's operands (n = 16) or a deep
-// operand ring (n = 32) in the whole register file.  The 32-token retained
-// chunks and the n = 32 forward from raw token vectors (unscaled) run two waves
-// per SIMD: a wave's own vector-ALU instructions do not overlap its matrix-core
-// products (measured: each adds its issue time to the product chain), another
-// wave's do, and forming each token's matrix on chip is vector-ALU work.
+// operand ring (n = 32) in the whole register file.  The forwards from raw token
+// vectors run more waves per SIMD: a wave's own vector-ALU instructions do not
+// overlap its matrix-core products (measured: each adds its issue time to the
+// product chain), another wave's do, and forming each token's matrix on chip is
+// vector-ALU work.  n = 16: 24-token retained chunks at three waves (two for
+// the scaled instance, which needs more registers); n = 32 (unscaled): two.
 template <int N, int KR, bool FX, bool SC>
-constexpr int fwd_waves() { return KR == 32 || (N == 32 && FX && !SC) ? 2 : 1; }
+constexpr int fwd_waves() {
+    return KR == 24 ? (SC ? 2 : 3) : ((N == 32 && FX && !SC) ? 2 : 1);
+}
 
 template <int N, int PF, int KR, bool FX, bool SC>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(fwd_waves<N, KR, FX, SC>(), fwd_waves<N, KR, FX, SC>())))
@@ -1694,10 +1697,11 @@ hipError_t run_bwd(const float* M, const float* P, const float* dP, float* dM, i
 // Tokens of one chunk kept in registers by the n = 16 forward kernel, and the
 // operand prefetch depth of its streamed sweeps (tokens in flight).
 constexpr int kRetain16 = 64;
-// from raw token vectors: 32-token chunks at two waves per SIMD (the token
-// build's vector-ALU work of one wave runs while the other's products run on
-// the matrix cores; measured faster than 64-token chunks at one wave)
-constexpr int kRetain16x = 32;
+// from raw token vectors: 24-token chunks at three waves per SIMD (the token
+// build's vector-ALU work of one wave runs while another's products run on the
+// matrix cores; measured faster than 32-token chunks at two waves and 64-token
+// chunks at one)
+constexpr int kRetain16x = 24;
 // the n = 16 backward from M: whole chunks of this length keep dL/dP in registers
 constexpr int kRetainBwd16 = 64;
 constexpr int kPf16 = 16;

@@ -73,12 +73,16 @@ def test_plans_single_and_multi(mpp):
             assert (ws == 0) == (nch == 1)
             assert mpp.workspace_bytes(2, 3, 203, n, mpp.DIR_BWD, chunk) == ws
     assert mpp.scan_chunk(1024, 8, 256, 8) == 256
-    # n = 16 from raw token vectors: 32-token chunks (two waves per SIMD) where the
-    # scan from M takes 64; one workspace size covers both
+    # n = 16 from raw token vectors: 24-token chunks (three waves per SIMD) where
+    # the scan from M takes 64; one workspace size covers both
     assert mpp.scan_chunk(4, 16, 8192, 16) == 64
-    assert mpp.scan_chunk(4, 16, 8192, 16, mpp.DIR_FWD_X) == 32
+    assert mpp.scan_chunk(4, 16, 8192, 16, mpp.DIR_FWD_X) == 24
     Kx, nchx, _, wsx = mpp.scan_plan(4, 16, 8192, 16, mpp.DIR_FWD_X)
-    assert (Kx, nchx) == (32, 256)
+    assert (Kx, nchx) == (24, 342)
+    # n = 32 from raw token vectors: twice the chains of the scan from M (two
+    # waves per SIMD)
+    assert mpp.scan_chunk(1, 8, 65536, 32) == 512
+    assert mpp.scan_chunk(1, 8, 65536, 32, mpp.DIR_FWD_X) == 256
     assert mpp.workspace_bytes(4, 16, 8192, 16) == wsx > mpp.scan_plan(4, 16, 8192, 16)[3]
     assert mpp.workspace_bytes(4, 16, 8192, 16, mpp.DIR_FWD_X) == wsx
     # the same explicit chunk gives the same plan either way
