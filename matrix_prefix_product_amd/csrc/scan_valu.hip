@@ -40,11 +40,18 @@ struct Valu {
     static constexpr int F4_BLK = TB * F4_TOK;    // float4 per chain per staged block
     static constexpr int LD = (G * F4_BLK) / 64;  // float4 loads per lane per staged array
     static constexpr int CH_STRIDE = TB * NN + 4; // floats per chain in LDS (16 B skew)
-    // floats per chain in the LDS buffers through which a chain's lanes swap
-    // rows; every lane then reads its chain's whole matrix, and the 16 B skew
-    // puts the chains in different banks (an unskewed n*n-float stride sends
-    // all chains of a wave to the same banks)
-    static constexpr int QX_STRIDE = NN + 4;
+    // LDS buffers through which a chain's lanes swap rows: every lane writes its
+    // rows (16-byte stores), then reads its chain's whole matrix (16-byte
+    // broadcasts within the chain) and single columns (4-byte reads).  XR floats
+    // per row, QX_STRIDE per chain.  n = 8: rows of 12 floats, so that the 8
+    // lanes of a chain (one 8-lane group of a 16-byte access) store to distinct
+    // banks (with 8-float rows lanes li and li+4 share banks), and chains 8 banks
+    // apart, so that the 4 chains of a 32-lane half read a column from distinct
+    // banks.  n = 4: rows of 4 floats with a 16 B skew per chain (an unskewed
+    // n*n-float stride sends all chains of a wave to the same banks).
+    static constexpr int XR = N == 8 ? 12 : N;
+    static constexpr int QX_STRIDE = N == 8 ? 104 : NN + 4;
+    static_assert(XR * N <= QX_STRIDE, "a chain's exchanged matrix fits its stride");
     // floats per chain of the backward's kept input matrix (16 B skew, as above)
     static constexpr int NX_STRIDE = NN + 4;
     static_assert((G * F4_BLK) % 64 == 0, "staging must tile the wave");
@@ -179,6 +186,31 @@ __device__ inline void add_rows(float (&st)[R][N], const float* src) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < N; ++j) st[r][j] += t[r][j];
+}
+
+// The same with rows XR floats apart (the row-exchange buffers).
+template <int N, int R, int XR>
+__device__ inline void store_rows_x(float* dst, const float (&st)[R][N]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q)
+            reinterpret_cast<float4*>(dst + r * XR)[q] =
+                make_float4(st[r][4 * q], st[r][4 * q + 1], st[r][4 * q + 2], st[r][4 * q + 3]);
+}
+
+template <int N, int XR>
+__device__ inline void load_matrix_x(float (&m)[N * N], const float* src) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            const float4 v = reinterpret_cast<const float4*>(src + i * XR)[q];
+            m[i * N + 4 * q + 0] = v.x;
+            m[i * N + 4 * q + 1] = v.y;
+            m[i * N + 4 * q + 2] = v.z;
+            m[i * N + 4 * q + 3] = v.w;
+        }
 }
 
 // Workspace (look-back) accessors, element by element through ws_store /
@@ -889,26 +921,26 @@ __device__ __attribute__((always_inline)) void bwd_sweep(
                 // dM rows a = own rows: dM[a][:] = sum_i P_{t-1}[i][a] Q_t[i][:]
                 wave_lds_sync();
                 if (live) {
-                    store_rows<N, R>(qxg + li * R * N, q);
-                    store_rows<N, R>(pxg + li * R * N, rp[tau]);
-                    if constexpr (DX) store_rows<N, R>(lxg + li * R * N, pl);
+                    store_rows_x<N, R, V::XR>(qxg + li * R * V::XR, q);
+                    store_rows_x<N, R, V::XR>(pxg + li * R * V::XR, rp[tau]);
+                    if constexpr (DX) store_rows_x<N, R, V::XR>(lxg + li * R * V::XR, pl);
                 }
                 wave_lds_sync();
                 if (live) {
                     float d[R][N], u[DX ? R : 1][N];
                     if (DX || FULL || tseq > 0 || cy.carry) {
                         float qa[V::NN];
-                        load_matrix<N>(qa, qxg);
+                        load_matrix_x<N, V::XR>(qa, qxg);
                         set_zero_rows<N, R>(d);
                         if constexpr (DX) set_zero_rows<N, R>(u);
 #pragma unroll
                         for (int ii = 0; ii < N; ++ii) {
                             float pc[R], lc[R];
 #pragma unroll
-                            for (int r = 0; r < R; ++r) pc[r] = pxg[ii * N + li * R + r];
+                            for (int r = 0; r < R; ++r) pc[r] = pxg[ii * V::XR + li * R + r];
                             if constexpr (DX)
 #pragma unroll
-                                for (int r = 0; r < R; ++r) lc[r] = lxg[ii * N + li * R + r];
+                                for (int r = 0; r < R; ++r) lc[r] = lxg[ii * V::XR + li * R + r];
 #pragma unroll
                             for (int r = 0; r < R; ++r)
 #pragma unroll
