@@ -85,8 +85,14 @@ def test_plans_single_and_multi(mpp):
     assert mpp.scan_chunk(1, 8, 65536, 32, mpp.DIR_FWD_X) == 256
     assert mpp.workspace_bytes(4, 16, 8192, 16) == wsx > mpp.scan_plan(4, 16, 8192, 16)[3]
     assert mpp.workspace_bytes(4, 16, 8192, 16, mpp.DIR_FWD_X) == wsx
-    # the same explicit chunk gives the same plan either way
-    assert mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD_X, 5) == mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD, 5)
+    # the same explicit chunk gives the same chunks and workspace either way; the
+    # forward from M at n = 16 groups them into smaller supers (a quarter of
+    # sqrt(chunks), at least 3, against a half)
+    fx, fm = mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD_X, 5), mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD, 5)
+    assert (fx[0], fx[1], fx[3]) == (fm[0], fm[1], fm[3])
+    assert (fx[2], fm[2]) == (round(0.5 * math.sqrt(41)), 3)
+    assert mpp.scan_plan(4, 16, 8192, 16)[2] == 3 and mpp.scan_plan(4, 16, 8192, 16, mpp.DIR_BWD)[2] == 4
+    assert mpp.scan_plan(8, 8, 4096, 16)[2] == 3 and mpp.scan_plan(4, 16, 65536, 16)[2] == 8
 
 
 def test_plan_rejects_bad_arguments(mpp):
