@@ -1157,6 +1157,21 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+    // Retained n = 16 chunks all take the same time, so the waves of a launch
+    // would go through their load pass, look-back and store pass in step, with
+    // HBM idle during the look-backs.  Every other wave of the first round
+    // (1024 = one per SIMD) starts kStagger clocks late and takes its ticket
+    // then, which keeps the two halves out of phase for the whole launch
+    // (interleaved on one box: C3 250.5 -> 246.5-247 us, C5 141 -> 136 us; two
+    // groups 8k clocks apart timed the same).  The wait is bounded and the wave
+    // holds no ticket meanwhile, so nothing waits on it.
+    if constexpr (KR == 64) {
+        constexpr uint64_t kStagger = 16000;
+        if (multi && blockIdx.x < 1024 && (blockIdx.x & 1)) {
+            const uint64_t t0 = __builtin_amdgcn_s_memtime();
+            while (__builtin_amdgcn_s_memtime() - t0 < kStagger) __builtin_amdgcn_s_sleep(8);
+        }
+    }
     const int64_t cidx =
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
