@@ -1125,6 +1125,22 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
     });
 }
 
+// Start delay of the one-wave-per-SIMD multi-chunk scans.  Their chunks all
+// take the same time, so the waves of a launch would go through their load
+// pass, look-back and store pass in step, with HBM idle during the look-backs.
+// Every other wave of the first round (1024 = one per SIMD) starts `clocks`
+// late and only then takes its ticket, which keeps the two halves out of phase
+// for the whole launch (figures at the call sites, interleaved runs on one
+// box).  Launches of fewer chunks than SIMDs have no such contention and start
+// at once.  The wait is bounded and the wave holds no ticket meanwhile, so
+// nothing waits on it.
+__device__ inline void stagger_start(int64_t nchunks, uint64_t clocks) {
+    if (nchunks >= 1024 && blockIdx.x < 1024 && (blockIdx.x & 1)) {
+        const uint64_t t0 = __builtin_amdgcn_s_memtime();
+        while (__builtin_amdgcn_s_memtime() - t0 < clocks) __builtin_amdgcn_s_sleep(8);
+    }
+}
+
 // One wave per SIMD: the forward keeps a chunk's operands (n = 16) or a deep
 // operand ring (n = 32) in the whole register file.  The forwards from raw token
 // vectors run more waves per SIMD: a wave's own vector-ALU instructions do not
@@ -1157,21 +1173,12 @@ void fwd_mfma_kernel(const float* __restrict__ M,
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    // Retained n = 16 chunks all take the same time, so the waves of a launch
-    // would go through their load pass, look-back and store pass in step, with
-    // HBM idle during the look-backs.  Every other wave of the first round
-    // (1024 = one per SIMD) starts kStagger clocks late and takes its ticket
-    // then, which keeps the two halves out of phase for the whole launch
-    // (interleaved on one box: C3 250.5 -> 246.5-247 us, C5 141 -> 136 us; two
-    // groups 8k clocks apart timed the same).  The wait is bounded and the wave
-    // holds no ticket meanwhile, so nothing waits on it.
-    if constexpr (KR == 64) {
-        constexpr uint64_t kStagger = 16000;
-        if (multi && blockIdx.x < 1024 && (blockIdx.x & 1)) {
-            const uint64_t t0 = __builtin_amdgcn_s_memtime();
-            while (__builtin_amdgcn_s_memtime() - t0 < kStagger) __builtin_amdgcn_s_sleep(8);
-        }
-    }
+    // retained n = 16 chunks: 16k clocks (C3 250.5 -> 246.5-247 us, C5 141 ->
+    // 136 us; four groups 8k clocks apart timed the same); n = 32 (one round of
+    // 512-token chunks): 50k clocks (1462 -> 1448 us; 150k: 1488 us); the
+    // forwards from raw token vectors, three and two waves per SIMD: no gain
+    if constexpr (KR == 64) stagger_start(multi ? nchunks : 0, 16000);
+    if constexpr (N == 32 && KR == 0 && !FX) stagger_start(multi ? nchunks : 0, 50000);
     const int64_t cidx =
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
@@ -1601,6 +1608,8 @@ void bwd_mfma_kernel(const float* __restrict__ M,
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+    // the retained backward from M (one wave per SIMD): C5 299 -> 290 us
+    if constexpr (KRB == 64) stagger_start(multi ? nchunks : 0, 16000);
     const int64_t cidx =
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
