@@ -110,14 +110,15 @@ Plan make_plan(int64_t S, int64_t T, int n, int dir, int64_t chunk, bool from_x 
         // supers of about sqrt(chunks) chunks balance the walk over a super's
         // aggregates against the chain of super prefixes; at n = 16 half that
         // measured faster (C5 backward 323-329 -> 313-317 us, C3 forward from raw
-        // token vectors 466-469 -> 451-453 us), a quarter (at least 3) for the
+        // token vectors 466-469 -> 451-453 us), a quarter (at least 5) for the
         // forward from M, whose retained chunks leave the look-back on the
-        // critical path (C3 265-267 -> 259-261 us; C5 149 us at 3 or 4, 158 at 2;
-        // interleaved runs on one box), at n = 32 neither
+        // critical path (with its staggered start, interleaved runs on one box:
+        // C3 Z = 2, 3, 4, 5, 6 -> 259, 247-248, 249-250, 247-248, 249-252 us, C5
+        // 148, 136, 136-137, 133, 136 us), at n = 32 neither
         const bool fwd16 = n == 16 && dir == 0 && !from_x;
         const double zf = n == 16 ? (fwd16 ? 0.25 : 0.5) : 1.0;
         int64_t z = llround(zf * sqrt(double(p.nch)));
-        if (fwd16 && z < 3) z = 3;
+        if (fwd16 && z < 5) z = 5;
         p.Z = z < 1 ? 1 : (z > 64 ? 64 : z);
     }
     p.nchunks = S * p.nch;

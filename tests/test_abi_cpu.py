@@ -87,12 +87,12 @@ def test_plans_single_and_multi(mpp):
     assert mpp.workspace_bytes(4, 16, 8192, 16, mpp.DIR_FWD_X) == wsx
     # the same explicit chunk gives the same chunks and workspace either way; the
     # forward from M at n = 16 groups them into smaller supers (a quarter of
-    # sqrt(chunks), at least 3, against a half)
+    # sqrt(chunks), at least 5, against a half)
     fx, fm = mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD_X, 5), mpp.scan_plan(2, 3, 203, 16, mpp.DIR_FWD, 5)
     assert (fx[0], fx[1], fx[3]) == (fm[0], fm[1], fm[3])
-    assert (fx[2], fm[2]) == (round(0.5 * math.sqrt(41)), 3)
-    assert mpp.scan_plan(4, 16, 8192, 16)[2] == 3 and mpp.scan_plan(4, 16, 8192, 16, mpp.DIR_BWD)[2] == 4
-    assert mpp.scan_plan(8, 8, 4096, 16)[2] == 3 and mpp.scan_plan(4, 16, 65536, 16)[2] == 8
+    assert (fx[2], fm[2]) == (round(0.5 * math.sqrt(41)), 5)
+    assert mpp.scan_plan(4, 16, 8192, 16)[2] == 5 and mpp.scan_plan(4, 16, 8192, 16, mpp.DIR_BWD)[2] == 4
+    assert mpp.scan_plan(8, 8, 4096, 16)[2] == 5 and mpp.scan_plan(4, 16, 65536, 16)[2] == 8
 
 
 def test_plan_rejects_bad_arguments(mpp):
