@@ -1047,23 +1047,34 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
             }
     };
     if constexpr (!SC) {
-        if (len == KR && s >= -64 && s <= 64) {
-            // a whole chunk whose carry is well inside the fp32 range: the carry
-            // rounded to fp32 as it is (scaling by 2^-s and back by 2^s changes no
-            // bit of a result unless an intermediate leaves the normal range), and
-            // each product stored straight from the matrix-core accumulators,
-            // branch-free, token t+1's products issued before token t is stored
+        if (len == KR) {
+            // a whole chunk: branch-free, token t+1's products issued before token
+            // t is stored.  A carry well inside the fp32 range is rounded as it is
+            // and every product stored straight from the matrix-core accumulators
+            // (scaling by 2^-s and back by 2^s changes no bit of a result unless
+            // an intermediate leaves the normal range); any other takes the scaling
+            // above and each result is multiplied back by 2^s (v_ldexp: exact, inf
+            // past the fp32 range) before its store, the same bits as the paired
+            // path below
+            const int se = (s >= -64 && s <= 64) ? 0 : s;
+            if (se == 0)
 #pragma unroll
-            for (int K = 0; K < NT; ++K)
+                for (int K = 0; K < NT; ++K)
 #pragma unroll
-                for (int J = 0; J < NT; ++J)
+                    for (int J = 0; J < NT; ++J)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) cb[K][J][b] = float(X.t[K][J][b]);
+                        for (int b = 0; b < 4; ++b) cb[K][J][b] = float(X.t[K][J][b]);
             f4v32 D[2][NT][NT];
             product(D[0], buf[0]);
             static_for(std::make_integer_sequence<int, KR>{}, [&](auto tc) {
                 constexpr int t = decltype(tc)::value;
                 if constexpr (t + 1 < KR) product(D[(t + 1) & 1], buf[t + 1]);
+#pragma unroll
+                for (int I = 0; I < NT; ++I)
+#pragma unroll
+                    for (int J = 0; J < NT; ++J)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) D[t & 1][I][J][r] = ldexpf(D[t & 1][I][J][r], se);
                 store_f4_rows<N>(P + (base + t) * NN, D[t & 1]);
             });
             return;
