@@ -1139,14 +1139,15 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
 // Start delay of the one-wave-per-SIMD multi-chunk scans.  Their chunks all
 // take the same time, so the waves of a launch would go through their load
 // pass, look-back and store pass in step, with HBM idle during the look-backs.
-// Every other wave of the first round (1024 = one per SIMD) starts `clocks`
-// late and only then takes its ticket, which keeps the two halves out of phase
-// for the whole launch (figures at the call sites, interleaved runs on one
-// box).  Launches of fewer chunks than SIMDs have no such contention and start
-// at once.  The wait is bounded and the wave holds no ticket meanwhile, so
-// nothing waits on it.
+// Every other wave of the first round (1024 per wave a SIMD holds) starts
+// `clocks` late and only then takes its ticket, which keeps the two halves out
+// of phase for the whole launch (figures at the call sites, interleaved runs on
+// one box).  Launches of fewer chunks than that have no such contention and
+// start at once.  The wait is bounded and the wave holds no ticket meanwhile,
+// so nothing waits on it.
+template <int WAVES = 1>
 __device__ inline void stagger_start(int64_t nchunks, uint64_t clocks) {
-    if (nchunks >= 1024 && blockIdx.x < 1024 && (blockIdx.x & 1)) {
+    if (nchunks >= 1024 * WAVES && blockIdx.x < 1024u * WAVES && (blockIdx.x & 1)) {
         const uint64_t t0 = __builtin_amdgcn_s_memtime();
         while (__builtin_amdgcn_s_memtime() - t0 < clocks) __builtin_amdgcn_s_sleep(8);
     }
@@ -1619,8 +1620,11 @@ void bwd_mfma_kernel(const float* __restrict__ M,
     const int64_t nchunks = S * nch;
     const bool multi = nch > 1;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-    // the retained backward from M (one wave per SIMD): C5 299 -> 290 us
+    // the retained backward from M (one wave per SIMD): C5 299 -> 290 us; the
+    // n = 16 backwards from raw token vectors (two waves per SIMD): C5 to dM
+    // 455 -> 447 us, to dx 567 -> 559 us
     if constexpr (KRB == 64) stagger_start(multi ? nchunks : 0, 16000);
+    if constexpr (N == 16 && FX) stagger_start<bwd_waves<N, FX>()>(multi ? nchunks : 0, 16000);
     const int64_t cidx =
         multi ? ticket_to_chunk(int64_t(wave_ticket(&hdr->ticket)), S, nch, 1) : int64_t(blockIdx.x);
     if (cidx >= nchunks) return;
