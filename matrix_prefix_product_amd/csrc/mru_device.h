@@ -161,17 +161,22 @@ __device__ inline void wait_range_nonempty(const uint32_t* flags, int64_t lo, in
     }
 }
 
-// frexp exponent: a finite nonzero v with exponent e has 2^(e-1) <= |v| < 2^e.
 // Orders a one-wave workgroup's LDS staging: the scan kernels run one wave per
-// workgroup, and a wave's LDS instructions execute in issue order, so the
-// writes of one staging step are seen by the reads that follow without waiting
-// for them to complete (a workgroup barrier waits: s_waitcnt lgkmcnt(0)).  The
-// wavefront-scope fence keeps the compiler from moving LDS accesses across it.
+// workgroup, so no workgroup barrier is needed, but the wave waits until its
+// own LDS operations have completed (s_waitcnt lgkmcnt(0)) before the accesses
+// that follow.  Without that wait (the fence alone, relying on a wave's LDS
+// instructions taking effect in issue order) the n = 16 layer backward to dx
+// read stale staged data at every other token in some builds of identical
+// machine code placed differently in the library, while the wait makes every
+// build correct.  The wavefront-scope fence keeps the compiler from moving LDS
+// accesses across it.
 __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
 }
 
+// frexp exponent: a finite nonzero v with exponent e has 2^(e-1) <= |v| < 2^e.
 // max_exp folds the exponent of a nonzero v into a running maximum that starts
 // at kNoExp (so an all-zero set keeps kNoExp).
 __device__ inline int frexp_exp(float v) { return __builtin_amdgcn_frexp_expf(v); }

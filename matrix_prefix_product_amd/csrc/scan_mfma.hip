@@ -1148,8 +1148,9 @@ __device__ __attribute__((always_inline)) void fwd_apply_retain(const typename M
 template <int WAVES = 1>
 __device__ inline void stagger_start(int64_t nchunks, uint64_t clocks) {
     if (nchunks >= 1024 * WAVES && blockIdx.x < 1024u * WAVES && (blockIdx.x & 1)) {
+        // at most 256 sleeps of 512 clocks, whatever the clock counter reads
         const uint64_t t0 = __builtin_amdgcn_s_memtime();
-        while (__builtin_amdgcn_s_memtime() - t0 < clocks) __builtin_amdgcn_s_sleep(8);
+        for (int i = 0; i < 256 && __builtin_amdgcn_s_memtime() - t0 < clocks; ++i) __builtin_amdgcn_s_sleep(8);
     }
 }
 
