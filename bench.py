@@ -68,6 +68,10 @@ WARMUP_EXTRA = 30
 # the library sources it was taken on (every .hip and .h of the package's csrc):
 # a figure taken on other sources is not reported.
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
+# (grid, wave x token steps per dispatch) of the bench step's kernels
+# (--summarize counters): C2L runs 8192 chains of 256 tokens, 8 chains per
+# wave, 1024 waves of 64 lanes
+COUNTER_STEPS = {"c2l": (1024 * 64, 1024 * 256)}
 CSRC = os.path.join(ROOT, "matrix_prefix_product_amd", "csrc")
 SIMDS = 1024          # 256 CUs x 4 SIMDs
 XCDS = 8
@@ -222,6 +226,24 @@ def summarize(what: str, dirs, workload: str, commands) -> None:
                       f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}")
         return
     data = read_counters(dirs)
+    if what == "counters":
+        # every counter of the runs, median per dispatch, and per wave and token
+        # step (the dispatch's wave count x the workload's tokens per chain)
+        sgrid, steps = COUNTER_STEPS.get(workload, (None, None))
+        names = sorted({c for v in data.values() for c in v if c != "dur_ns"})
+        head += [f"# median per dispatch; '/step' rows (kernels of grid {sgrid}) divide by waves x tokens "
+                 f"per chain = {steps} (the {workload} step kernels, one chunk per chain)" if steps else
+                 "# median per dispatch"]
+        print("\n".join(head))
+        print(f"{'kernel':48s} {'grid':>9s} {'us':>9s} " + " ".join(f"{c:>22s}" for c in names))
+        for (k, grid), v in sorted(data.items(), key=lambda kv: -_median(kv[1]["dur_ns"])):
+            if not all(c in v for c in names):
+                continue
+            vals = " ".join(f"{_median(v[c]):22.0f}" for c in names)
+            print(f"{k[:48]:48s} {grid:9d} {_median(v['dur_ns']) / 1e3:9.1f} {vals}")
+            if steps and grid == sgrid:
+                print(f"{'  /step':48s} {'':9s} {'':9s} " + " ".join(f"{_median(v[c]) / steps:22.2f}" for c in names))
+        return
     path = TRAFFIC_FILE if what == "traffic" else MFMA_FILE
     try:
         rec = json.load(open(path))
@@ -754,7 +776,7 @@ def main():
                     help="only the n=16 / n=32 and next-row figures (for profiling those kernels)")
     ap.add_argument("--only", choices=("c3", "c4", "c5"),
                     help="with --extra-only: just this workload's figures (one workload per profile)")
-    ap.add_argument("--summarize", choices=("trace", "traffic", "mfma"),
+    ap.add_argument("--summarize", choices=("trace", "traffic", "mfma", "counters"),
                     help="print the summary of the rocprofv3 CSVs under DIR... (no GPU work)")
     ap.add_argument("--profile-workload", help="with --summarize: the workload the runs covered")
     ap.add_argument("--command", action="append", default=[],

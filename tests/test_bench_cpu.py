@@ -110,6 +110,28 @@ def test_counter_summary(tmp_path, capsys):
     assert "bwd_mfma_kernel<16, 8, false, false, 0>" in capsys.readouterr().out
 
 
+def test_counters_summary_per_step(tmp_path, capsys):
+    """--summarize counters: medians per dispatch, and per wave-token step for the
+    step kernels' grid."""
+    import bench
+    d = tmp_path / "run"
+    d.mkdir()
+    hdr = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size",'
+           '"Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+           '"Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
+    k = '"void mru::(anonymous namespace)::bwd_valu_kernel<8, 1, 4, true, false>(float const*)"'
+    steps = 1024 * 256
+    rows = [hdr]
+    for disp, lds in enumerate((60.0, 62.5, 70.0), 1):
+        rows.append(f'{disp},{disp},"Agent 1",1,1,1,65536,7,{k},64,0,0,238,0,32,"SQ_INSTS_LDS",{lds * steps},0,350000')
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize("counters", [str(d)], "c2l", ["cmd"])
+    out = capsys.readouterr().out.splitlines()
+    i = next(j for j, ln in enumerate(out) if ln.startswith("bwd_valu_kernel<8, 1, 4, true, false>"))
+    assert out[i].split()[-1] == str(int(62.5 * steps))
+    assert out[i + 1].split()[-1] == "62.50"
+
+
 def test_counted_sources_exist():
     import bench
     assert any(f.endswith(".hip") for f in os.listdir(bench.CSRC))
